@@ -1,0 +1,186 @@
+/*
+ * moe_mxfp4.h -- C ABI of a sparse Mixture-of-Experts FFN layer with MXFP4
+ * routed experts and bf16 shared experts, for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (per token x, one MoE layer):
+ *   Deltafin explainer (bhfrc.com), section 5.1, and Deltafin README
+ *   ("An experiment in running Kimi K3 ..."), "How it works": the router picks
+ *   the top-k (K3: 16) of E (K3: 896) routed experts, the selected experts'
+ *   MXFP4 weights are applied with the dequantisation fused into the product
+ *   (README, "Techniques / Compute"), and the outputs of the always-on shared
+ *   experts (K3: 2) are added.  Readings used where the pages are silent:
+ *     s_e   = sigmoid(x . Wr[e] + bias[e])        (bias optional)
+ *     ids   = k largest s_e, ties to the lower expert index, ordered by
+ *             (s descending, index ascending)
+ *     w_j   = s_{ids_j} / sum_j s_{ids_j}
+ *     E(x)  = Wd (SiLU(Wg x) * (Wu x))            SwiGLU, MXFP4 weights
+ *     S(x)  = same form, bf16 weights              shared experts, weight 1
+ *     y     = residual + sum_j w_j E_{ids_j}(x) + sum_s S_s(x)
+ *   rounded once to bf16 (round to nearest even) at the output; everything
+ *   before is accumulated in fp32.
+ *
+ * MXFP4 (kimi-k3-in-c note (curvesoft.net), byte accounting): 4-bit E2M1
+ * elements with one E8M0 exponent per 32 consecutive elements along the
+ * input dimension, 0.53125 bytes per weight, 17,547,264 bytes per K3 expert.
+ *
+ * Expert record (README, "Techniques / I/O and streaming": an expert's six
+ * tensors are one contiguous span).  Record of expert e starts at
+ * experts + e * expert_stride and holds, in order:
+ *     gate codes  uint8 [I][H/2]    gate scales uint8 [I][H/32]
+ *     up   codes  uint8 [I][H/2]    up   scales uint8 [I][H/32]
+ *     down codes  uint8 [H][I/2]    down scales uint8 [H][I/32]
+ *   rows are output features, the contraction dimension is contiguous;
+ *   element k of a row is in byte k/2, even k in the low nibble; scale byte j
+ *   of a row covers elements 32j..32j+31 and means 2^(byte-127) (255 = NaN).
+ *   moe_record_bytes() gives the size (17,547,264 at H=7168, I=1536).
+ *
+ * Conventions for every call:
+ *   - pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t
+ *     bit patterns; every device pointer must be 16-byte aligned.
+ *   - the caller owns every buffer.  The library allocates nothing, keeps no
+ *     mutable global state, never synchronises the host, and enqueues all
+ *     work on the given stream (NULL = the default stream).
+ *   - arguments are validated on the host before anything is launched; on
+ *     error nothing is launched and a negative MOE_E* code is returned.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - x, y and residual must not overlap, except y == residual (in place).
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION ((1u << 16) | 0u)
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL -1      /* null pointer, negative or zero size */
+#define MOE_EALIGN -2      /* a device pointer or stride is not 16-byte aligned */
+#define MOE_ESHAPE -3      /* unsupported shape (see moe_layer_desc) */
+#define MOE_EWORKSPACE -4  /* workspace smaller than moe_workspace_bytes() */
+#define MOE_EDEVICE -5     /* current device is not gfx950 */
+#define MOE_ELAUNCH -6     /* a kernel launch failed; see moe_last_hip_error() */
+#define MOE_EUNSUPPORTED -7 /* valid request this build does not implement */
+
+/* moe_forward path selection */
+#define MOE_PATH_AUTO 0  /* GEMV path for small T, MXFP8 MFMA path for large T */
+#define MOE_PATH_GEMV 1  /* bf16 activations, dequant-fused GEMV (decode) */
+#define MOE_PATH_MFMA 2  /* MXFP8 activations, scaled FP4 MFMA (prefill) */
+
+/*
+ * One MoE layer.  Host struct; the pointers in it are device pointers.
+ *   hidden (H) and inter (I): multiples of 32, H <= 8192, I <= 8192.
+ *   n_experts (E) <= 1024; 1 <= top_k <= min(E, 32); 0 <= n_shared <= 4.
+ *   router_w:    bf16 [E][H]
+ *   router_bias: fp32 [E] added to the logits before the sigmoid, or NULL
+ *   experts:     E records, expert_stride bytes apart (stride >= record
+ *                bytes, multiple of 16)
+ *   shared_gate, shared_up: bf16 [S][I][H];  shared_down: bf16 [S][H][I]
+ *                (may be NULL when n_shared == 0)
+ */
+typedef struct moe_layer_desc {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_shared;
+  int32_t reserved0; /* must be 0 */
+  const uint16_t* router_w;
+  const float* router_bias;
+  const uint8_t* experts;
+  uint64_t expert_stride;
+  const uint16_t* shared_gate;
+  const uint16_t* shared_up;
+  const uint16_t* shared_down;
+} moe_layer_desc;
+
+/* major << 16 | minor of the library; bindings refuse a different major. */
+uint32_t moe_abi_version(void);
+
+/* Static description of a status code (host; never NULL). */
+const char* moe_status_string(int status);
+
+/* hipError_t of the last failed launch on the calling host thread. */
+int moe_last_hip_error(void);
+
+/* Bytes of one expert record for (hidden, inter); MOE_ESHAPE if not
+ * multiples of 32. */
+int moe_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes);
+
+/* Workspace needed by moe_route / moe_forward / moe_layer for n_tokens
+ * tokens of this layer.  The caller allocates it (any device memory, e.g. a
+ * torch uint8 tensor); its contents need no initialisation and are
+ * overwritten by every call.  Calls that share a workspace must be ordered
+ * (same stream). */
+int moe_workspace_bytes(const moe_layer_desc* layer, int64_t n_tokens, uint64_t* out_bytes);
+
+/*
+ * Router: topk_ids int32 [T][k] and topk_w fp32 [T][k] (see the formulas at
+ * the top).  Logits accumulate in fp32 from exact bf16 products.
+ *   x: bf16 [T][H].
+ */
+int moe_route(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+              int32_t* topk_ids, float* topk_w, void* workspace, uint64_t workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * Experts and combine for a given routing:
+ *   y = residual + sum_j topk_w[t][j] * E_{topk_ids[t][j]}(x_t) + sum_s S_s(x_t)
+ *   x, residual (or NULL), y: bf16 [T][H];  topk_ids int32 [T][k] with
+ *   distinct ids per token in [0, E);  topk_w fp32 [T][k].
+ *   path: MOE_PATH_GEMV keeps x and h exact (bf16 x, fp32 h);
+ *         MOE_PATH_MFMA rounds x and h to MXFP8 (E4M3 with one E8M0
+ *         exponent per 32 along the contraction) for the routed experts, the
+ *         reading of the MXFP8 activations in the Deltafin explainer,
+ *         section 2.1;
+ *         MOE_PATH_AUTO picks MFMA when n_tokens >= moe_mfma_min_tokens().
+ * Routing ids out of range are clamped on the device (never read out of
+ * bounds); they are the caller's error.
+ */
+int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                const int32_t* topk_ids, const float* topk_w, const uint16_t* residual,
+                uint16_t* y, int32_t path, void* workspace, uint64_t workspace_bytes,
+                hipStream_t stream);
+
+/* moe_route followed by moe_forward, scheduled together (the shared experts
+ * overlap the router).  topk_ids / topk_w receive the routing. */
+int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+              const uint16_t* residual, uint16_t* y, int32_t* topk_ids, float* topk_w,
+              int32_t path, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/* Smallest n_tokens for which MOE_PATH_AUTO takes the MFMA path. */
+int64_t moe_mfma_min_tokens(void);
+
+/*
+ * RMSNorm for stacked layers: out = bf16(x * (mean(x^2) + eps)^-1/2 * gamma),
+ * fp32 inside.  x, out: bf16 [T][H] (may be equal); gamma: bf16 [H].
+ */
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_tokens,
+                int32_t hidden, uint16_t* out, hipStream_t stream);
+
+/*
+ * Test export: the fp32 weights of one matrix of one expert, dequantised by
+ * the same device code the GEMV uses.  matrix: 0 gate [I][H], 1 up [I][H],
+ * 2 down [H][I]; out: fp32 of that shape.
+ */
+int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matrix, float* out,
+                       hipStream_t stream);
+
+/*
+ * Test export: MXFP8 quantisation of bf16 rows as used by the MFMA path.
+ *   x: bf16 [T][K] (K multiple of 32); codes: uint8 [T][K] E4M3;
+ *   scales: uint8 [T][K/32] E8M0.
+ */
+int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* codes,
+                       uint8_t* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H */

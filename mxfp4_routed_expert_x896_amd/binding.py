@@ -1,0 +1,201 @@
+"""ctypes binding of libmoe_mxfp4.so (argument marshalling only).
+
+Every call forwards device pointers of torch tensors and torch's current HIP
+stream to the C ABI in include/moe_mxfp4.h; all arithmetic runs in the
+library's gfx950 kernels.  torch is used for device memory and streams only.
+Loading fails loudly when the library has not been built: there is no
+fallback path.
+"""
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library links against)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
+
+ABI_MAJOR = 1
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE",
+                -4: "MOE_EWORKSPACE", -5: "MOE_EDEVICE", -6: "MOE_ELAUNCH",
+                -7: "MOE_EUNSUPPORTED"}
+
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+GATE, UP, DOWN = 0, 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib().moe_status_string(status).decode()
+        extra = ""
+        if status == -6:
+            extra = f" (hipError {_lib().moe_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}{extra}")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("n_shared", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("router_w", ctypes.c_void_p),
+        ("router_bias", ctypes.c_void_p),
+        ("experts", ctypes.c_void_p),
+        ("expert_stride", ctypes.c_uint64),
+        ("shared_gate", ctypes.c_void_p),
+        ("shared_up", ctypes.c_void_p),
+        ("shared_down", ctypes.c_void_p),
+    ]
+
+
+_LIB = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_U64 = ctypes.c_uint64
+_DESC = ctypes.POINTER(LayerDesc)
+
+_SIGNATURES = {
+    "moe_abi_version": (ctypes.c_uint32, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_last_hip_error": (ctypes.c_int, []),
+    "moe_record_bytes": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_U64)]),
+    "moe_workspace_bytes": (ctypes.c_int, [_DESC, _I64, ctypes.POINTER(_U64)]),
+    "moe_route": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _U64, _P]),
+    "moe_forward": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P, _U64, _P]),
+    "moe_layer": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P, _U64, _P]),
+    "moe_mfma_min_tokens": (ctypes.c_int64, []),
+    "moe_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _I64, _I32, _P, _P]),
+    "moe_dequant_export": (ctypes.c_int, [_DESC, _I32, _I32, _P, _P]),
+    "moe_mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+}
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mxfp4_routed_expert_x896_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        ver = lib.moe_abi_version()
+        if ver >> 16 != ABI_MAJOR:
+            raise ImportError(f"library ABI {ver >> 16}.{ver & 0xFFFF}, binding expects {ABI_MAJOR}.x")
+        _LIB = lib
+    return _LIB
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError when not built)."""
+    return _lib()
+
+
+def _check(status, where):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def record_bytes(hidden, inter):
+    out = _U64()
+    _check(_lib().moe_record_bytes(hidden, inter, ctypes.byref(out)), "moe_record_bytes")
+    return out.value
+
+
+def mfma_min_tokens():
+    return _lib().moe_mfma_min_tokens()
+
+
+class Layer:
+    """Device tensors of one MoE layer plus the C descriptor that points at them.
+
+    router_w: bf16/uint16-viewable [E, H]; experts: uint8 [E, stride] (or flat);
+    shared_*: bf16 [S, I, H] / [S, H, I] or None; router_bias: fp32 [E] or None.
+    """
+
+    def __init__(self, hidden, inter, n_experts, top_k, router_w, experts,
+                 shared_gate=None, shared_up=None, shared_down=None, router_bias=None,
+                 expert_stride=None):
+        self.hidden, self.inter = int(hidden), int(inter)
+        self.n_experts, self.top_k = int(n_experts), int(top_k)
+        self.router_w = router_w
+        self.experts = experts
+        self.shared_gate, self.shared_up, self.shared_down = shared_gate, shared_up, shared_down
+        self.router_bias = router_bias
+        self.n_shared = 0 if shared_gate is None else int(shared_gate.shape[0])
+        stride = expert_stride if expert_stride is not None else record_bytes(hidden, inter)
+        self.expert_stride = int(stride)
+        self._desc = LayerDesc(
+            self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, 0,
+            router_w.data_ptr(),
+            None if router_bias is None else router_bias.data_ptr(),
+            experts.data_ptr(), self.expert_stride,
+            None if shared_gate is None else shared_gate.data_ptr(),
+            None if shared_up is None else shared_up.data_ptr(),
+            None if shared_down is None else shared_down.data_ptr())
+
+    @property
+    def desc(self):
+        return ctypes.byref(self._desc)
+
+    def workspace_bytes(self, n_tokens):
+        out = _U64()
+        _check(_lib().moe_workspace_bytes(self.desc, n_tokens, ctypes.byref(out)),
+               "moe_workspace_bytes")
+        return out.value
+
+    def workspace(self, n_tokens, device=None):
+        dev = device if device is not None else self.router_w.device
+        return torch.empty(self.workspace_bytes(n_tokens), dtype=torch.uint8, device=dev)
+
+
+def route(layer, x, topk_ids, topk_w, ws, stream=None):
+    _check(_lib().moe_route(layer.desc, _ptr(x), x.shape[0], _ptr(topk_ids), _ptr(topk_w),
+                            _ptr(ws), ws.numel(), _stream(stream)), "moe_route")
+
+
+def forward(layer, x, topk_ids, topk_w, y, ws, residual=None, path=PATH_AUTO, stream=None):
+    _check(_lib().moe_forward(layer.desc, _ptr(x), x.shape[0], _ptr(topk_ids), _ptr(topk_w),
+                              _ptr(residual), _ptr(y), path, _ptr(ws), ws.numel(),
+                              _stream(stream)), "moe_forward")
+
+
+def moe_layer(layer, x, y, topk_ids, topk_w, ws, residual=None, path=PATH_AUTO, stream=None):
+    _check(_lib().moe_layer(layer.desc, _ptr(x), x.shape[0], _ptr(residual), _ptr(y),
+                            _ptr(topk_ids), _ptr(topk_w), path, _ptr(ws), ws.numel(),
+                            _stream(stream)), "moe_layer")
+
+
+def rmsnorm(x, gamma, eps, out, stream=None):
+    _check(_lib().moe_rmsnorm(_ptr(x), _ptr(gamma), ctypes.c_float(eps), x.shape[0],
+                              x.shape[1], _ptr(out), _stream(stream)), "moe_rmsnorm")
+
+
+def dequant_export(layer, expert, matrix, out, stream=None):
+    _check(_lib().moe_dequant_export(layer.desc, expert, matrix, _ptr(out), _stream(stream)),
+           "moe_dequant_export")
+
+
+def mxfp8_quantize(x, codes, scales, stream=None):
+    _check(_lib().moe_mxfp8_quantize(_ptr(x), x.shape[0], x.shape[1], _ptr(codes),
+                                     _ptr(scales), _stream(stream)), "moe_mxfp8_quantize")

@@ -1,0 +1,293 @@
+// C ABI of the MoE layer library: host-side validation, workspace carving
+// and launch sequencing on the caller's stream.  See include/moe_mxfp4.h.
+#include <atomic>
+#include <climits>
+#include <cstring>
+
+#include "../../include/moe_mxfp4.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_EDEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MOE_OK : MOE_EDEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = int(e);
+    return MOE_ELAUNCH;
+  }
+  return MOE_OK;
+}
+
+uint64_t record_bytes(int H, int I) {
+  return 3ull * (uint64_t(H) * I / 2 + uint64_t(H) * I / 32);
+}
+
+int check_layer(const moe_layer_desc* L) {
+  if (L == nullptr) return MOE_EINVAL;
+  if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0 || L->n_shared < 0)
+    return MOE_EINVAL;
+  if (L->reserved0 != 0) return MOE_EINVAL;
+  if (L->hidden % 32 || L->inter % 32 || L->hidden > 8192 || L->inter > 8192) return MOE_ESHAPE;
+  if (L->n_experts > 1024 || L->top_k > 32 || L->top_k > L->n_experts || L->n_shared > 4)
+    return MOE_ESHAPE;
+  if (L->router_w == nullptr || L->experts == nullptr) return MOE_EINVAL;
+  if (L->n_shared > 0 &&
+      (L->shared_gate == nullptr || L->shared_up == nullptr || L->shared_down == nullptr))
+    return MOE_EINVAL;
+  if (!aligned16(L->router_w) || !aligned16(L->experts) || (L->expert_stride & 15u))
+    return MOE_EALIGN;
+  if (L->router_bias != nullptr && !aligned16(L->router_bias)) return MOE_EALIGN;
+  if (L->n_shared > 0 &&
+      (!aligned16(L->shared_gate) || !aligned16(L->shared_up) || !aligned16(L->shared_down)))
+    return MOE_EALIGN;
+  if (L->expert_stride < record_bytes(L->hidden, L->inter)) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
+constexpr int64_t kMaxTokens = 1 << 16;
+
+uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// Workspace layout for T tokens.
+struct Carve {
+  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, total;
+};
+
+Carve carve(const moe_layer_desc* L, int64_t T) {
+  const uint64_t E = L->n_experts, k = L->top_k, H = L->hidden, I = L->inter, S = L->n_shared;
+  const uint64_t t = uint64_t(T);
+  Carve c;
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  c.logits = take(t * E * 4);
+  c.n_active = take(4);
+  c.active = take(E * 4);
+  c.act_off = take((E + 1) * 4);
+  c.pairs = take(t * k * 4);
+  c.h = take(t * k * I * 4);
+  c.hs = take(S * t * I * 4);
+  c.part = take(t * k * H * 4);
+  c.ysh = take(t * H * 4);
+  c.total = off;
+  return c;
+}
+
+template <typename T>
+T* at(void* ws, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
+}
+
+int check_tokens(int64_t T) {
+  if (T <= 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
+int check_ws(const moe_layer_desc* L, int64_t T, void* ws, uint64_t ws_bytes) {
+  if (ws == nullptr) return MOE_EINVAL;
+  if (!aligned16(ws)) return MOE_EALIGN;
+  if (ws_bytes < carve(L, T).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+int do_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, int32_t* ids, float* w,
+             void* ws, hipStream_t stream) {
+  const Carve c = carve(L, T);
+  float* logits = at<float>(ws, c.logits);
+  int st = launched(moe::launch_router_logits(x, L->router_w, L->router_bias, logits, int(T),
+                                              L->hidden, L->n_experts, stream));
+  if (st) return st;
+  return launched(moe::launch_router_topk(logits, int(T), L->n_experts, L->top_k, ids, w, stream));
+}
+
+int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
+                    const float* w, const uint16_t* residual, uint16_t* y, void* ws,
+                    hipStream_t stream) {
+  const Carve c = carve(L, T);
+  moe::GemvLayer G;
+  G.T = int(T);
+  G.H = L->hidden;
+  G.I = L->inter;
+  G.E = L->n_experts;
+  G.k = L->top_k;
+  G.S = L->n_shared;
+  G.x = x;
+  G.experts = L->experts;
+  G.stride = L->expert_stride;
+  G.sgate = L->shared_gate;
+  G.sup = L->shared_up;
+  G.sdown = L->shared_down;
+  G.plan.n_active = at<int32_t>(ws, c.n_active);
+  G.plan.active = at<int32_t>(ws, c.active);
+  G.plan.act_off = at<int32_t>(ws, c.act_off);
+  G.plan.pairs = at<int32_t>(ws, c.pairs);
+  const int64_t pairs = T * L->top_k;
+  G.max_active = int(pairs < L->n_experts ? pairs : L->n_experts);
+  G.h = at<float>(ws, c.h);
+  G.hs = at<float>(ws, c.hs);
+  G.part = at<float>(ws, c.part);
+  G.ysh = at<float>(ws, c.ysh);
+  int st = launched(moe::launch_plan(ids, int(pairs), L->n_experts, G.plan, stream));
+  if (st) return st;
+  if ((st = launched(moe::launch_gateup(G, stream)))) return st;
+  if ((st = launched(moe::launch_down(G, stream)))) return st;
+  return launched(moe::launch_combine(G, w, residual, y, stream));
+}
+
+int resolve_path(int32_t path, int64_t T) {
+  if (path == MOE_PATH_AUTO) return T >= moe_mfma_min_tokens() ? MOE_PATH_MFMA : MOE_PATH_GEMV;
+  return path;
+}
+
+}  // namespace
+
+MOE_API uint32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer or non-positive size)";
+    case MOE_EALIGN: return "device pointer or stride not 16-byte aligned";
+    case MOE_ESHAPE: return "unsupported shape";
+    case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_EDEVICE: return "current device is not gfx950";
+    case MOE_ELAUNCH: return "kernel launch failed (see moe_last_hip_error)";
+    case MOE_EUNSUPPORTED: return "request not implemented by this build";
+    default: return "unknown status";
+  }
+}
+
+MOE_API int moe_last_hip_error(void) { return g_last_hip_error; }
+
+MOE_API int moe_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes) {
+  if (out_bytes == nullptr || hidden <= 0 || inter <= 0) return MOE_EINVAL;
+  if (hidden % 32 || inter % 32) return MOE_ESHAPE;
+  *out_bytes = record_bytes(hidden, inter);
+  return MOE_OK;
+}
+
+MOE_API int moe_workspace_bytes(const moe_layer_desc* layer, int64_t n_tokens,
+                                uint64_t* out_bytes) {
+  if (out_bytes == nullptr) return MOE_EINVAL;
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  *out_bytes = carve(layer, n_tokens).total;
+  return MOE_OK;
+}
+
+MOE_API int64_t moe_mfma_min_tokens(void) { return INT64_MAX; }
+
+MOE_API int moe_route(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                      int32_t* topk_ids, float* topk_w, void* workspace,
+                      uint64_t workspace_bytes, hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_EALIGN;
+  if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
+  if ((st = check_device())) return st;
+  return do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream);
+}
+
+MOE_API int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                        const int32_t* topk_ids, const float* topk_w, const uint16_t* residual,
+                        uint16_t* y, int32_t path, void* workspace, uint64_t workspace_bytes,
+                        hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_EALIGN;
+  if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
+  if ((st = check_device())) return st;
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
+  return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+}
+
+MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                      const uint16_t* residual, uint16_t* y, int32_t* topk_ids, float* topk_w,
+                      int32_t path, void* workspace, uint64_t workspace_bytes,
+                      hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_EALIGN;
+  if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
+  if ((st = check_device())) return st;
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
+  if ((st = do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream))) return st;
+  return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+}
+
+MOE_API int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_tokens,
+                        int32_t hidden, uint16_t* out, hipStream_t stream) {
+  if (x == nullptr || gamma == nullptr || out == nullptr || n_tokens <= 0 || hidden <= 0)
+    return MOE_EINVAL;
+  if (hidden % 32 || hidden > 8192 || n_tokens > INT_MAX) return MOE_ESHAPE;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(out)) return MOE_EALIGN;
+  if (!(eps >= 0.0f)) return MOE_EINVAL;
+  int st = check_device();
+  if (st) return st;
+  return launched(moe::launch_rmsnorm(x, gamma, eps, int(n_tokens), hidden, out, stream));
+}
+
+MOE_API int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matrix,
+                               float* out, hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if (out == nullptr || expert < 0 || expert >= layer->n_experts || matrix < 0 || matrix > 2)
+    return MOE_EINVAL;
+  if (!aligned16(out)) return MOE_EALIGN;
+  if ((st = check_device())) return st;
+  const uint8_t* rec = layer->experts + uint64_t(expert) * layer->expert_stride;
+  return launched(
+      moe::launch_dequant_export(rec, layer->hidden, layer->inter, matrix, out, stream));
+}
+
+MOE_API int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr || n_rows <= 0 || k <= 0)
+    return MOE_EINVAL;
+  if (k % 32) return MOE_ESHAPE;
+  if (!aligned16(x) || !aligned16(codes)) return MOE_EALIGN;
+  if (uint64_t(n_rows) * uint64_t(k / 32) > (uint64_t(UINT_MAX) - 255)) return MOE_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  return launched(moe::launch_mxfp8_quantize(x, n_rows, k, codes, scales, stream));
+}

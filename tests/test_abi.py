@@ -1,0 +1,128 @@
+"""C-ABI library: loads, exports exactly the header's functions, and rejects
+invalid arguments on the host before launching anything (CPU only: every
+call here fails validation, so no device pointer is ever dereferenced).
+"""
+
+import ctypes
+import os
+
+import pytest
+import torch
+
+from mxfp4_routed_expert_x896_amd import build as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        B.build()
+    from mxfp4_routed_expert_x896_amd import binding
+    return binding
+
+
+def test_exports_match_header(lib):
+    lib.lib()
+    want = B.header_functions()
+    assert "moe_route" in want and "moe_forward" in want and "moe_layer" in want
+    assert B.exported_functions() == want
+
+
+def test_library_is_gfx950_only():
+    import re
+    blob = open(B.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-[-a-z]*gfx[0-9a-z]+", blob))
+    assert targets == {b"amdgcn-amd-amdhsa--gfx950"}
+
+
+def test_abi_version_and_record_bytes(lib):
+    assert lib.lib().moe_abi_version() >> 16 == lib.ABI_MAJOR
+    assert lib.record_bytes(7168, 1536) == 17_547_264
+    assert lib.record_bytes(256, 64) == 26_112
+    out = ctypes.c_uint64()
+    assert lib.lib().moe_record_bytes(100, 64, ctypes.byref(out)) == -3
+    assert lib.lib().moe_record_bytes(256, 64, None) == -1
+
+
+def _desc(lib, **kw):
+    d = dict(hidden=256, inter=64, n_experts=32, top_k=4, n_shared=1, reserved0=0,
+             router_w=0x10000, router_bias=None, experts=0x20000, expert_stride=26_112,
+             shared_gate=0x30000, shared_up=0x40000, shared_down=0x50000)
+    d.update(kw)
+    return lib.LayerDesc(**d)
+
+
+def _ws(lib, desc, t):
+    out = ctypes.c_uint64()
+    st = lib.lib().moe_workspace_bytes(ctypes.byref(desc), t, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(hidden=250), -3),
+    (dict(inter=48), -3),
+    (dict(hidden=8224), -3),
+    (dict(n_experts=1025), -3),
+    (dict(top_k=33, n_experts=64), -3),
+    (dict(top_k=40), -3),
+    (dict(n_shared=5), -3),
+    (dict(router_w=None), -1),
+    (dict(experts=None), -1),
+    (dict(shared_down=None), -1),
+    (dict(n_shared=0, shared_gate=None, shared_up=None, shared_down=None), 0),
+    (dict(router_w=0x10008), -2),
+    (dict(expert_stride=26_120), -2),
+    (dict(expert_stride=26_096), -3),
+    (dict(reserved0=1), -1),
+])
+def test_descriptor_validation(lib, kw, status):
+    st, nbytes = _ws(lib, _desc(lib, **kw), 4)
+    assert st == status
+    if status == 0:
+        assert nbytes > 0
+
+
+def test_workspace_grows_with_tokens_and_token_limits(lib):
+    d = _desc(lib)
+    s1, b1 = _ws(lib, d, 1)
+    s2, b2 = _ws(lib, d, 64)
+    assert s1 == 0 and s2 == 0 and b2 > b1
+    assert _ws(lib, d, 0)[0] == -1
+    assert _ws(lib, d, 1 << 17)[0] == -3
+
+
+def test_calls_reject_bad_arguments_before_launch(lib):
+    L = lib.lib()
+    d = _desc(lib)
+    _, need = _ws(lib, d, 2)
+    P = ctypes.c_void_p
+    x, ids, w, y, ws = P(0x100000), P(0x200000), P(0x300000), P(0x400000), P(0x500000)
+    dp = ctypes.byref(d)
+    assert L.moe_route(dp, None, 2, ids, w, ws, need, None) == -1
+    assert L.moe_route(dp, x, 0, ids, w, ws, need, None) == -1
+    assert L.moe_route(dp, P(0x100004), 2, ids, w, ws, need, None) == -2
+    assert L.moe_route(dp, x, 2, ids, w, ws, need - 1, None) == -4
+    assert L.moe_forward(dp, x, 2, ids, w, None, None, 1, ws, need, None) == -1
+    assert L.moe_forward(dp, x, 2, ids, w, None, y, 7, ws, need, None) == -1
+    assert L.moe_forward(dp, x, 2, ids, w, P(0x600002), y, 1, ws, need, None) == -2
+    assert L.moe_forward(dp, x, 2, ids, w, None, y, 1, ws, 16, None) == -4
+    assert L.moe_layer(dp, x, 2, None, y, ids, None, 1, ws, need, None) == -1
+    assert L.moe_rmsnorm(x, None, 1e-6, 2, 256, y, None) == -1
+    assert L.moe_rmsnorm(x, x, 1e-6, 2, 100, y, None) == -3
+    assert L.moe_rmsnorm(x, x, -1.0, 2, 256, y, None) == -1
+    assert L.moe_dequant_export(dp, 32, 0, y, None) == -1
+    assert L.moe_dequant_export(dp, 0, 3, y, None) == -1
+    assert L.moe_mxfp8_quantize(x, 2, 48, y, w, None) == -3
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
+        assert L.moe_status_string(code)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU refusal")
+def test_valid_call_without_gfx950_refuses(lib):
+    L = lib.lib()
+    d = _desc(lib)
+    _, need = _ws(lib, d, 2)
+    P = ctypes.c_void_p
+    st = L.moe_route(ctypes.byref(d), P(0x100000), 2, P(0x200000), P(0x300000), P(0x500000),
+                     need, None)
+    assert st == -5

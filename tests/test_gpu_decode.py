@@ -1,0 +1,247 @@
+"""GPU parity of the decode path (router, dequant-fused GEMV, shared experts,
+combine) against the float64 oracle, through the C ABI.
+
+Bars: bit-exact dequantised weights; routing equal up to near-ties within
+1e-6 of the k-th score; layer output max over tokens of relative L2 error
+<= 2e-3 (bf16 output vs float64 oracle).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import synth.device as SD
+from oracle import formats as F
+from oracle import moe as M
+from oracle import record as R
+from tests._gpu import REL_TOL, Built, check_routing, oracle_weights, rel_l2_per_token, to_np_u16
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = dict(hidden=288, inter=96, n_experts=40, top_k=5, n_shared=2)
+WIDE = dict(hidden=8192, inter=64, n_experts=24, top_k=3, n_shared=1)
+MANY = dict(hidden=128, inter=32, n_experts=1024, top_k=32, n_shared=0)
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mxfp4_routed_expert_x896_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return Built(synth.TINY, seed=0)
+
+
+def _run_layer(b, built, x_dev, residual=None, path=1):
+    T = x_dev.shape[0]
+    k, H = built.cfg["top_k"], built.cfg["hidden"]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ws = built.lib.workspace(T)
+    b.moe_layer(built.lib, x_dev, y, ids, w, ws, residual=residual, path=path)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
+
+
+def _forward(b, built, x_dev, ids_np, w_np, residual=None):
+    T = x_dev.shape[0]
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    w = torch.from_numpy(np.ascontiguousarray(w_np, dtype=np.float32)).cuda()
+    y = torch.empty((T, built.cfg["hidden"]), dtype=torch.int16, device="cuda")
+    ws = built.lib.workspace(T)
+    b.forward(built.lib, x_dev, ids, w, y, ws, residual=residual, path=b.PATH_GEMV)
+    torch.cuda.synchronize()
+    return to_np_u16(y)
+
+
+# ------------------------------------------------------------ dequant ----
+
+def _export(b, built, e, m):
+    H, I = built.cfg["hidden"], built.cfg["inter"]
+    shape = (H, I) if m == R.DOWN else (I, H)
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    b.dequant_export(built.lib, e, m, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _bits_equal(gpu_f32, ref_f64):
+    ref = ref_f64.astype(np.float32)
+    g = gpu_f32.view(np.uint32)
+    r = ref.view(np.uint32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(gpu_f32), nan)
+    np.testing.assert_array_equal(g[~nan], r[~nan])
+
+
+def test_dequant_export_bit_exact_tiny(b, tiny):
+    for e in range(tiny.cfg["n_experts"]):
+        rec = tiny.oracle.expert_record(e)
+        for m in (R.GATE, R.UP, R.DOWN):
+            _bits_equal(_export(b, tiny, e, m), R.dequant_matrix(rec, 256, 64, m))
+
+
+def test_dequant_export_extreme_scales_and_every_code(b):
+    H, I = 64, 32
+    rb = R.record_bytes(H, I)
+    recs = np.zeros((2, rb), dtype=np.uint8)
+    for j in range(2):
+        views = R.split(recs[j], H, I)
+        for m in range(3):
+            codes, scales = views[2 * m], views[2 * m + 1]
+            codes[...] = np.arange(codes.size, dtype=np.int64).reshape(codes.shape) % 256
+            pattern = np.array([0, 1, 2, 126, 127, 128, 253, 254, 255] if j == 0 else [118, 126])
+            scales[...] = pattern[np.arange(scales.size) % len(pattern)].reshape(scales.shape)
+    experts = torch.from_numpy(recs).cuda()
+    wr = torch.zeros((2, H), dtype=torch.int16, device="cuda")
+    layer = b.Layer(H, I, 2, 1, wr, experts)
+    for j in range(2):
+        for m in range(3):
+            shape = (H, I) if m == 2 else (I, H)
+            out = torch.empty(shape, dtype=torch.float32, device="cuda")
+            b.dequant_export(layer, j, m, out)
+            torch.cuda.synchronize()
+            _bits_equal(out.cpu().numpy(), R.dequant_matrix(recs[j], H, I, m))
+
+
+# ------------------------------------------------------------- router ----
+
+def test_route_tiny_matches_oracle(b, tiny):
+    xh, xd = SD.upload_tokens(1000, 64, 256)
+    ids, w, _ = _run_layer(b, tiny, xd)
+    _, _, s = M.route(xh, tiny.oracle)
+    check_routing(ids, w, s, 4)
+    np.testing.assert_allclose(w, oracle_weights(s, ids), rtol=0, atol=2e-6)
+
+
+def test_route_exact_ties_lower_index(b):
+    cfg = dict(hidden=256, inter=64, n_experts=32, top_k=4, n_shared=0)
+    built = Built(cfg, seed=3)
+    wr = built.dev["router_w"]
+    wr[:] = wr[5]            # every row equal: all logits tie exactly
+    xh, xd = SD.upload_tokens(1001, 3, 256)
+    ids, w, _ = _run_layer(b, built, xd)
+    assert ids.tolist() == [[0, 1, 2, 3]] * 3
+    np.testing.assert_allclose(w, 0.25, atol=1e-7)
+
+
+# ------------------------------------------------------------- layer -----
+
+@pytest.mark.parametrize("T", [1, 3, 16])
+def test_forward_tiny_given_oracle_routing(b, tiny, T):
+    xh, xd = SD.upload_tokens(1002 + T, T, 256)
+    ids, w, _ = M.route(xh, tiny.oracle)
+    w32 = w.astype(np.float32)
+    y = _forward(b, tiny, xd, ids, w32)
+    ref = M.moe_forward(xh, tiny.oracle, ids, w32.astype(np.float64))
+    err = rel_l2_per_token(y, ref)
+    assert err.max() <= REL_TOL, err
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY], ids=["tiny", "ragged", "wide", "many"])
+@pytest.mark.parametrize("T", [1, 7])
+def test_layer_matches_oracle(b, cfg, T):
+    built = Built(cfg, seed=11)
+    xh, xd = SD.upload_tokens(1100 + T, T, cfg["hidden"])
+    ids, w, y = _run_layer(b, built, xd)
+    _, _, s = M.route(xh, built.oracle)
+    check_routing(ids, w, s, cfg["top_k"])
+    ref = M.moe_forward(xh, built.oracle, ids, oracle_weights(s, ids))
+    err = rel_l2_per_token(y, ref)
+    assert err.max() <= REL_TOL, err
+
+
+def test_residual_added(b, tiny):
+    xh, xd = SD.upload_tokens(1200, 5, 256)
+    rh, rd = SD.upload_tokens(1201, 5, 256)
+    ids, w, _ = M.route(xh, tiny.oracle)
+    y = _forward(b, tiny, xd, ids, w, residual=rd)
+    ref = M.moe_forward(xh, tiny.oracle, ids, w.astype(np.float32).astype(np.float64),
+                        residual_bits=rh)
+    assert rel_l2_per_token(y, ref).max() <= REL_TOL
+
+
+def test_one_more_scale_exponent_doubles_output_bitwise(b):
+    """All up scales +1 doubles every routed partial exactly in fp32; with no
+    shared experts the bf16 output doubles bit for bit."""
+    cfg = dict(hidden=256, inter=64, n_experts=8, top_k=2, n_shared=0)
+    built = Built(cfg, seed=4)
+    xh, xd = SD.upload_tokens(1300, 4, 256)
+    _, _, y1 = _run_layer(b, built, xd)
+    ex = built.dev["experts"].cpu().numpy()
+    for e in range(8):
+        R.split(ex[e], 256, 64)[3][...] += 1
+    built.dev["experts"].copy_(torch.from_numpy(ex))
+    _, _, y2 = _run_layer(b, built, xd)
+    np.testing.assert_array_equal(F.bf16_decode(y2), 2.0 * F.bf16_decode(y1))
+
+
+def test_zero_routed_experts_leave_shared_only(b):
+    cfg = dict(hidden=256, inter=64, n_experts=8, top_k=3, n_shared=2)
+    built = Built(cfg, seed=5)
+    built.dev["experts"].zero_()
+    xh, xd = SD.upload_tokens(1400, 4, 256)
+    _, _, y = _run_layer(b, built, xd)
+    ref = M.shared_sum(xh, built.oracle)
+    assert rel_l2_per_token(y, ref).max() <= REL_TOL
+
+
+def test_all_experts_equal_is_routing_independent(b):
+    cfg = dict(hidden=256, inter=64, n_experts=16, top_k=4, n_shared=1)
+    built = Built(cfg, seed=6)
+    built.dev["experts"][:] = built.dev["experts"][7]
+    xh, xd = SD.upload_tokens(1500, 6, 256)
+    ids1, _, y1 = _run_layer(b, built, xd)
+    built.dev["router_w"].copy_(torch.flip(built.dev["router_w"], dims=[0]))
+    ids2, _, y2 = _run_layer(b, built, xd)
+    assert not np.array_equal(ids1, ids2)
+    rec = synth.expert_record(6, 0, 7, 256, 64)
+    xv = F.bf16_decode(xh)
+    dense = M.expert_ffn(xv, *R.dequant_expert(rec, 256, 64)) + M.shared_sum(xh, built.oracle)
+    assert rel_l2_per_token(y1, dense).max() <= REL_TOL
+    assert rel_l2_per_token(y2, dense).max() <= REL_TOL
+
+
+def test_deterministic(b, tiny):
+    xh, xd = SD.upload_tokens(1600, 9, 256)
+    a = _run_layer(b, tiny, xd)
+    c = _run_layer(b, tiny, xd)
+    for u, v in zip(a, c):
+        np.testing.assert_array_equal(u, v)
+
+
+# --------------------------------------------------------------- misc ----
+
+def test_rmsnorm_within_one_bf16_ulp(b):
+    H = 7168
+    xh, xd = SD.upload_tokens(1700, 8, H)
+    gh, gd = SD.upload_gamma(0, 0, H)
+    out = torch.empty_like(xd)
+    b.rmsnorm(xd, gd, 1e-6, out)
+    torch.cuda.synchronize()
+    got = to_np_u16(out).astype(np.int32)
+    ref = M.rmsnorm(xh, gh, 1e-6).astype(np.int32)
+    d = np.abs(got - ref)
+    assert d.max() <= 1
+    assert (d > 0).mean() < 1e-3
+
+
+def test_mxfp8_quantize_bit_exact(b):
+    g = np.random.default_rng(0)
+    v = g.standard_normal((16, 7168)).astype(np.float32) * np.exp(g.uniform(-30, 30, (16, 1)))
+    v[0, :32] = 0.0
+    v[1, 32:64] = -0.0
+    v[2, 64] = 3e38
+    xh = synth.to_bf16_bits(v)
+    xd = torch.from_numpy(xh.view(np.int16)).cuda()
+    codes = torch.empty((16, 7168), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((16, 224), dtype=torch.uint8, device="cuda")
+    b.mxfp8_quantize(xd, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = F.mxfp8_quantize(F.bf16_decode(xh))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)

@@ -1,0 +1,92 @@
+"""GPU parity at the full K3 layer shape (hidden 7168, 896 experts of
+intermediate 1536, top-16, 2 shared experts): batch 1, batched decode of 64
+tokens, and 8 tokens with a residual, in the launch configuration the
+benchmark times.  The oracle checks sampled tokens one by one; routing is
+checked for every token.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import synth.device as SD
+from oracle import moe as M
+from oracle import record as R
+from tests._gpu import REL_TOL, Built, check_routing, oracle_weights, rel_l2_per_token, to_np_u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mxfp4_routed_expert_x896_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def k3():
+    print("building K3 layer (15.7 GB of expert records)", flush=True)
+    return Built(synth.K3, seed=0)
+
+
+def _run(b, built, xd, residual=None):
+    T = xd.shape[0]
+    ids = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 16), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, 7168), dtype=torch.int16, device="cuda")
+    ws = built.lib.workspace(T)
+    b.moe_layer(built.lib, xd, y, ids, w, ws, residual=residual, path=b.PATH_GEMV)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
+
+
+def test_k3_dequant_sampled_experts_bit_exact(b, k3):
+    for e in (0, 517, 895):
+        rec = k3.oracle.expert_record(e)
+        for m in (R.GATE, R.UP, R.DOWN):
+            shape = (7168, 1536) if m == R.DOWN else (1536, 7168)
+            out = torch.empty(shape, dtype=torch.float32, device="cuda")
+            b.dequant_export(k3.lib, e, m, out)
+            torch.cuda.synchronize()
+            ref = R.dequant_matrix(rec, 7168, 1536, m).astype(np.float32)
+            np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", [1000, 1001, 1002])
+def test_k3_decode_batch1(b, k3, seed):
+    xh, xd = SD.upload_tokens(seed, 1, 7168)
+    ids, w, y = _run(b, k3, xd)
+    _, _, s = M.route(xh, k3.oracle)
+    check_routing(ids, w, s, 16)
+    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids))
+    err = rel_l2_per_token(y, ref)
+    print(f"K3 b=1 seed {seed}: rel L2 {err.max():.3e}")
+    assert err.max() <= REL_TOL
+
+
+def test_k3_batched_decode_64(b, k3):
+    xh, xd = SD.upload_tokens(2000, 64, 7168)
+    ids, w, y = _run(b, k3, xd)
+    _, _, s = M.route(xh, k3.oracle)
+    check_routing(ids, w, s, 16)
+    distinct = len(np.unique(ids))
+    print(f"K3 b=64: {distinct} distinct experts")
+    assert 500 < distinct < 700
+    sample = [0, 21, 42, 63]
+    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids), tokens=sample)
+    err = rel_l2_per_token(y[sample], ref)
+    print(f"K3 b=64 sampled rel L2 {err.max():.3e}")
+    assert err.max() <= REL_TOL
+
+
+def test_k3_eight_tokens_with_residual(b, k3):
+    xh, xd = SD.upload_tokens(3000, 8, 7168)
+    rh, rd = SD.upload_tokens(3001, 8, 7168)
+    ids, w, y = _run(b, k3, xd, residual=rd)
+    _, _, s = M.route(xh, k3.oracle)
+    check_routing(ids, w, s, 16)
+    sample = [1, 6]
+    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids), residual_bits=rh,
+                        tokens=sample)
+    assert rel_l2_per_token(y[sample], ref).max() <= REL_TOL
