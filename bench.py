@@ -1,0 +1,288 @@
+"""Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b8|b64|stack12]
+
+A step is one full pass of the layer (router GEMV + top-k, token->expert
+plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
+combine) over one batch of synthetic tokens already resident in HBM.  Each
+step takes fresh tokens (seed 1000 + i), so the routing and the set of
+experts streamed change from step to step.  For batch 1 the layer is held in
+several replicas at different addresses, used round-robin, so that no step
+finds the previous step's weights in the 256 MB Infinity Cache (in a model
+the other layers run in between).
+
+Printed: one JSON line with tokens/s (value), ms per step, the expert-weight
+HBM rate, the dominant kernel's roofline (HIP events around each kernel of
+the library's own launches) and the float64 oracle timed on the host cores
+on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MAT_BYTES = 7168 * 1536 // 2 + 7168 * 1536 // 32   # one MXFP4 matrix: 5,849,088 B
+REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
+SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
+# kernels of one moe_layer call, in launch order (see moe_profile_events)
+KERNELS_DECODE = ["router_logits", "select_plan", "gateup", "down"]
+KERNELS_LARGE = ["router_logits", "router_topk", "plan", "gateup", "down"]
+
+CONFIGS = {
+    "b1": dict(tokens=1, layers=1, replicas=8,
+               desc="K3 MoE layer decode, batch 1 (H 7168, 896 experts x I 1536 MXFP4, top-16, 2 bf16 shared)"),
+    "b8": dict(tokens=8, layers=1, replicas=8,
+               desc="K3 MoE layer decode, batch 8"),
+    "b64": dict(tokens=64, layers=1, replicas=1,
+                desc="K3 MoE layer batched decode, 64 tokens"),
+    "stack12": dict(tokens=8, layers=12, replicas=1,
+                    desc="12 stacked K3 MoE layers (RMSNorm -> MoE -> residual), batch 8"),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default="b1", choices=sorted(CONFIGS))
+    p.add_argument("--replicas", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=1)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp4_routed_expert_x896_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
+    """Algorithmic HBM bytes of one launch: weights read once, activations in
+    and out; intermediates passed between kernels counted once."""
+    x = T * H * 2
+    if name == "router_logits":
+        return E * H * 2 + x + T * E * 4
+    if name == "router_topk":
+        return T * E * 4 + T * k * 8
+    if name == "plan":
+        return T * k * 4 * 2 + E * 8
+    if name == "select_plan":
+        return T * E * 4 + T * k * 8 + T * k * 4 * 2 + E * 8
+    if name == "gateup":
+        return D * 2 * MAT_BYTES + S * 2 * SHARED_MAT_BYTES + x + (T * k + S * T) * I * 4
+    if name == "down":  # includes the combine: bf16 output written once
+        return D * MAT_BYTES + S * SHARED_MAT_BYTES + (T * k + S * T) * I * 4 + T * k * 4 + x
+    raise KeyError(name)
+
+
+def cpu_baseline(cfg_name, n_tokens):
+    """The float64 oracle on the host cores, on a bounded sample."""
+    import synth
+    from oracle import moe as M
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    c = synth.K3
+    H, I = c["hidden"], c["inter"]
+    layer = M.Layer(H, I, c["n_experts"], c["top_k"], synth.router_weight(0, 0, c["n_experts"], H),
+                    expert_record=lambda e: synth.expert_record(0, 0, e, H, I),
+                    shared=[synth.shared_expert(0, 0, s, H, I) for s in range(c["n_shared"])])
+    n_layers = CONFIGS[cfg_name]["layers"]
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(n_tokens):
+        # one token of the workload's input through one layer (route + experts)
+        M.moe_layer(synth.activations(1000 + i, 1, H), layer)
+        done += 1
+        if time.perf_counter() - t0 > 30:
+            break
+    dt = time.perf_counter() - t0
+    # a token of the stacked workload passes n_layers layers
+    return {"value": round(done / dt / n_layers, 6), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} single-token layer call(s) of {cfg_name} through the float64 numpy "
+                      f"oracle (router + 16 experts dequantised and applied + 2 shared"
+                      f"{', scaled by 1/%d layers' % n_layers if n_layers > 1 else ''}), "
+                      f"{dt:.1f} s; BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note, not a measured path)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import synth.device as SD
+    from mxfp4_routed_expert_x896_amd import binding as b
+
+    cfgd = CONFIGS[args.config]
+    T, n_layers = cfgd["tokens"], cfgd["layers"]
+    replicas = args.replicas or cfgd["replicas"]
+    c = synth.K3
+    H, I, E, k, S = c["hidden"], c["inter"], c["n_experts"], c["top_k"], c["n_shared"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- layers resident in HBM
+    t_setup = time.time()
+    layers, keep = [], []
+    n_distinct = n_layers
+    for l in range(n_distinct):
+        d = SD.upload_layer(c, seed=0, layer=l)
+        L = b.Layer.from_canonical(H, I, E, k, d["router_w"], d["experts"], d["shared_gate"],
+                                   d["shared_up"], d["shared_down"])
+        del d  # canonical copies are not needed once packed
+        keep.append(L)
+        layers.append(L)
+        print(f"[bench] layer {l} resident ({time.time() - t_setup:.0f} s)", file=sys.stderr,
+              flush=True)
+    if n_layers == 1:
+        for r in range(1, replicas):
+            L0 = layers[0]
+            t = {n: (getattr(L0, n).clone() if getattr(L0, n) is not None else None)
+                 for n in ("router_w", "experts", "shared_gate", "shared_up", "shared_down")}
+            layers.append(b.Layer(H, I, E, k, t["router_w"], t["experts"], t["shared_gate"],
+                                  t["shared_up"], t["shared_down"]))
+    torch.cuda.synchronize()
+    gammas = [SD.upload_gamma(0, l, H)[1] for l in range(n_layers)]
+    n_steps = args.warmup + args.steps
+    xs = torch.stack([SD.upload_tokens(1000 + i, T, H)[1] for i in range(n_steps)])
+    ids = torch.empty((n_steps, n_layers, T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((n_steps, n_layers, T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((n_layers + 1, T, H), dtype=torch.int16, device=dev)
+    normed = torch.empty((T, H), dtype=torch.int16, device=dev)
+    ws = layers[0].workspace(T)
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.time() - t_setup:.0f} s; {len(layers)} resident layer copies",
+          file=sys.stderr, flush=True)
+
+    def step(i):
+        if n_layers == 1:
+            L = layers[i % len(layers)]
+            b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=b.PATH_GEMV)
+        else:
+            cur = xs[i]
+            for l in range(n_layers):
+                b.rmsnorm(cur, gammas[l], 1e-6, normed)
+                b.moe_layer(layers[l], normed, y[l + 1], ids[i, l], wts[i, l], ws,
+                            residual=cur, path=b.PATH_GEMV)
+                cur = y[l + 1]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step", file=sys.stderr,
+          flush=True)
+
+    # distinct experts per (step, layer)
+    id_np = ids[args.warmup:].cpu().numpy()
+    D = np.array([[len(np.unique(id_np[s, l])) for l in range(n_layers)]
+                  for s in range(args.steps)])
+    exp_bytes = (D * REC_BYTES + S * 3 * SHARED_MAT_BYTES).sum(axis=1).mean()
+    exp_gbs = exp_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- per-kernel durations: the library records an event after each kernel
+    n_ev = 8
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    import ctypes
+    arr = (ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs])
+    b.profile_events(arr, n_ev)
+    KERNELS = KERNELS_DECODE if T <= 64 else KERNELS_LARGE
+    per_kernel = {name: [] for name in KERNELS}
+    span = []
+    prof_steps = min(args.steps, 100)
+    for i in range(args.warmup, args.warmup + prof_steps):
+        L = layers[i % len(layers)]
+        b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=b.PATH_GEMV)
+        cnt = b.profile_count()
+        torch.cuda.synchronize()
+        for j, name in enumerate(KERNELS[:cnt - 1]):
+            per_kernel[name].append(evs[j].elapsed_time(evs[j + 1]) * 1e3)
+        span.append(evs[0].elapsed_time(evs[cnt - 1]) * 1e3)
+    b.profile_events(None, 0)
+    kern_us = {n: float(np.mean(v)) for n, v in per_kernel.items() if v}
+    dom = max(kern_us, key=kern_us.get)
+    D0 = D[:prof_steps, 0]
+    dom_bytes = float(np.mean([kernel_bytes(dom, T, k, d, S) for d in D0]))
+    achieved = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
+
+    traffic = None
+    pmc_path = os.path.join(ROOT, "profiles", f"pmc_{dom}_{args.config}.json")
+    if os.path.exists(pmc_path):
+        pmc = json.load(open(pmc_path))
+        if pmc.get("source_hash") == source_hash():
+            traffic = pmc.get("bytes_per_launch")
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    out = {
+        "metric": "tokens/s & expert-weight HBM GB/s, K3-shape MXFP4 MoE layer (b=1/64/4096)",
+        "value": round(T / (ms_per_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4*bf16->f32",
+        "data": "synthetic (seeded; codes uniform, E8M0 118..126, N(0,0.02) bf16 router/shared, N(0,1) tokens)",
+        "config": {"workload": cfgd["desc"], "tokens_per_step": T, "layers": n_layers,
+                   "resident_copies": len(layers), "path": "gemv"},
+        "expert_weight_gbs": round(float(exp_gbs), 1),
+        "expert_weight_hbm_frac": round(float(exp_gbs) / HBM_PEAK_GBS, 4),
+        "distinct_experts_mean": round(float(D.mean()), 2),
+        "kernel_us": {n: round(v, 2) for n, v in kern_us.items()},
+        "layer_span_us_events": round(float(np.mean(span)), 2),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": round(dom_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,9 +23,8 @@
  * elements with one E8M0 exponent per 32 consecutive elements along the
  * input dimension, 0.53125 bytes per weight, 17,547,264 bytes per K3 expert.
  *
- * Expert record (README, "Techniques / I/O and streaming": an expert's six
- * tensors are one contiguous span).  Record of expert e starts at
- * experts + e * expert_stride and holds, in order:
+ * Canonical expert record (README, "Techniques / I/O and streaming": an
+ * expert's six tensors are one contiguous span), the interchange format:
  *     gate codes  uint8 [I][H/2]    gate scales uint8 [I][H/32]
  *     up   codes  uint8 [I][H/2]    up   scales uint8 [I][H/32]
  *     down codes  uint8 [H][I/2]    down scales uint8 [H][I/32]
@@ -33,6 +32,17 @@
  *   element k of a row is in byte k/2, even k in the low nibble; scale byte j
  *   of a row covers elements 32j..32j+31 and means 2^(byte-127) (255 = NaN).
  *   moe_record_bytes() gives the size (17,547,264 at H=7168, I=1536).
+ *
+ * Packed layout (what the layer kernels read; moe_pack_experts writes it).
+ * Each MXFP4 matrix of R rows x K columns becomes tiles of 16 rows x 128
+ * columns, 1088 bytes each, ordered (row group, column group): bytes
+ * 16 l .. 16 l + 15 hold the codes of block 4 kb + l / 16 of row
+ * 16 rg + l % 16 and byte 1024 + l its scale (blocks past K/32 are zero
+ * codes, scale 127).  A wave64 reads one tile as 1 KiB of contiguous codes
+ * in which lane l holds exactly its MFMA operand.  Same bytes as the
+ * canonical record when K is a multiple of 128 (17,547,264 at K3 shape).
+ * bf16 shared matrices are packed the same way into 1 KiB tiles of 16 rows
+ * x 32 columns (lane l: row 16 rg + l % 16, columns 8 (l / 16) .. +7).
  *
  * Conventions for every call:
  *   - pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t
@@ -78,10 +88,11 @@ extern "C" {
  *   n_experts (E) <= 1024; 1 <= top_k <= min(E, 32); 0 <= n_shared <= 4.
  *   router_w:    bf16 [E][H]
  *   router_bias: fp32 [E] added to the logits before the sigmoid, or NULL
- *   experts:     E records, expert_stride bytes apart (stride >= record
- *                bytes, multiple of 16)
- *   shared_gate, shared_up: bf16 [S][I][H];  shared_down: bf16 [S][H][I]
- *                (may be NULL when n_shared == 0)
+ *   experts:     E PACKED records (moe_pack_experts), expert_stride bytes
+ *                apart (stride >= moe_packed_record_bytes, multiple of 16)
+ *   shared_gate, shared_up: S packed bf16 [I][H] matrices, back to back;
+ *   shared_down: S packed bf16 [H][I] matrices (moe_pack_bf16); NULL when
+ *                n_shared == 0
  */
 typedef struct moe_layer_desc {
   int32_t hidden;
@@ -111,6 +122,26 @@ int moe_last_hip_error(void);
 /* Bytes of one expert record for (hidden, inter); MOE_ESHAPE if not
  * multiples of 32. */
 int moe_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes);
+
+/* Bytes of one packed expert record (see "Packed layout" above). */
+int moe_packed_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes);
+
+/*
+ * Repack n_experts canonical records (src, src_stride bytes apart) into the
+ * packed layout at dst (dst_stride bytes apart; dst_stride >=
+ * moe_packed_record_bytes, multiple of 16).  One-time weight preparation;
+ * src and dst must not overlap.  Weight loading, not part of the hot path.
+ */
+int moe_pack_experts(const uint8_t* src, uint64_t src_stride, uint8_t* dst, uint64_t dst_stride,
+                     int32_t n_experts, int32_t hidden, int32_t inter, hipStream_t stream);
+
+/*
+ * Repack count row-major bf16 matrices of rows x cols (back to back at src)
+ * into packed tiles (back to back at dst, same total size); rows a multiple
+ * of 16, cols a multiple of 32.  Used for the shared experts.
+ */
+int moe_pack_bf16(const uint16_t* src, uint16_t* dst, int32_t count, int32_t rows, int32_t cols,
+                  hipStream_t stream);
 
 /* Workspace needed by moe_route / moe_forward / moe_layer for n_tokens
  * tokens of this layer.  The caller allocates it (any device memory, e.g. a
@@ -164,9 +195,26 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
                 int32_t hidden, uint16_t* out, hipStream_t stream);
 
 /*
- * Test export: the fp32 weights of one matrix of one expert, dequantised by
- * the same device code the GEMV uses.  matrix: 0 gate [I][H], 1 up [I][H],
- * 2 down [H][I]; out: fp32 of that shape.
+ * Optional per-kernel timing for benchmarks.  While an event array is set
+ * (per host thread), every call that launches kernels records events[0] on
+ * its stream before its first kernel and events[i] right after its i-th
+ * kernel (i < n_events); moe_profile_count() returns how many the last such
+ * call recorded.  Kernel order: moe_route: router logits, top-k;
+ * moe_forward (GEMV path): plan, gate/up, down (with the combine);
+ * moe_layer (GEMV path, n_tokens <= 64): router logits, top-k with plan,
+ * gate/up, down; above 64 tokens: router logits, top-k, plan, gate/up,
+ * down.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
+ * to stop.  Timing
+ * records only add event markers; no kernel is skipped or changed.
+ */
+int moe_profile_events(hipEvent_t* events, int32_t n_events);
+int moe_profile_count(void);
+
+/*
+ * Test export: the fp32 weights of one matrix of one (packed) expert,
+ * decoded by the same device conversion the expert kernels use and written
+ * in canonical order.  matrix: 0 gate [I][H], 1 up [I][H], 2 down [H][I];
+ * out: fp32 of that shape.
  */
 int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matrix, float* out,
                        hipStream_t stream);

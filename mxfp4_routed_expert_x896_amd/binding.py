@@ -75,6 +75,11 @@ _SIGNATURES = {
     "moe_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _I64, _I32, _P, _P]),
     "moe_dequant_export": (ctypes.c_int, [_DESC, _I32, _I32, _P, _P]),
     "moe_mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "moe_packed_record_bytes": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_U64)]),
+    "moe_pack_experts": (ctypes.c_int, [_P, _U64, _P, _U64, _I32, _I32, _I32, _P]),
+    "moe_pack_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
+    "moe_profile_events": (ctypes.c_int, [_P, _I32]),
+    "moe_profile_count": (ctypes.c_int, []),
 }
 
 
@@ -122,6 +127,33 @@ def record_bytes(hidden, inter):
     return out.value
 
 
+def packed_record_bytes(hidden, inter):
+    out = _U64()
+    _check(_lib().moe_packed_record_bytes(hidden, inter, ctypes.byref(out)),
+           "moe_packed_record_bytes")
+    return out.value
+
+
+def pack_experts(src, n_experts, hidden, inter, dst=None, stream=None):
+    """Canonical uint8 records [E, record_bytes] -> packed uint8 [E, packed_bytes]."""
+    pb = packed_record_bytes(hidden, inter)
+    if dst is None:
+        dst = torch.empty((n_experts, pb), dtype=torch.uint8, device=src.device)
+    src_stride = src.numel() // n_experts
+    _check(_lib().moe_pack_experts(_ptr(src), src_stride, _ptr(dst), dst.numel() // n_experts,
+                                   n_experts, hidden, inter, _stream(stream)), "moe_pack_experts")
+    return dst
+
+
+def pack_bf16(src, stream=None):
+    """Row-major bf16 matrices [count, rows, cols] (int16/bf16) -> packed, same shape."""
+    count, rows, cols = src.shape
+    dst = torch.empty_like(src)
+    _check(_lib().moe_pack_bf16(_ptr(src), _ptr(dst), count, rows, cols, _stream(stream)),
+           "moe_pack_bf16")
+    return dst
+
+
 def mfma_min_tokens():
     return _lib().moe_mfma_min_tokens()
 
@@ -129,8 +161,9 @@ def mfma_min_tokens():
 class Layer:
     """Device tensors of one MoE layer plus the C descriptor that points at them.
 
-    router_w: bf16/uint16-viewable [E, H]; experts: uint8 [E, stride] (or flat);
-    shared_*: bf16 [S, I, H] / [S, H, I] or None; router_bias: fp32 [E] or None.
+    router_w: bf16/uint16-viewable [E, H]; experts: PACKED uint8 records
+    [E, stride] (pack_experts); shared_*: PACKED bf16 [S, I, H] / [S, H, I]
+    (pack_bf16) or None; router_bias: fp32 [E] or None.
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, router_w, experts,
@@ -143,7 +176,7 @@ class Layer:
         self.shared_gate, self.shared_up, self.shared_down = shared_gate, shared_up, shared_down
         self.router_bias = router_bias
         self.n_shared = 0 if shared_gate is None else int(shared_gate.shape[0])
-        stride = expert_stride if expert_stride is not None else record_bytes(hidden, inter)
+        stride = expert_stride if expert_stride is not None else packed_record_bytes(hidden, inter)
         self.expert_stride = int(stride)
         self._desc = LayerDesc(
             self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, 0,
@@ -163,6 +196,16 @@ class Layer:
         _check(_lib().moe_workspace_bytes(self.desc, n_tokens, ctypes.byref(out)),
                "moe_workspace_bytes")
         return out.value
+
+    @classmethod
+    def from_canonical(cls, hidden, inter, n_experts, top_k, router_w, experts,
+                       shared_gate=None, shared_up=None, shared_down=None, router_bias=None):
+        """Packs canonical expert records and row-major shared matrices first."""
+        packed = pack_experts(experts, n_experts, hidden, inter)
+        sg = None if shared_gate is None else pack_bf16(shared_gate)
+        su = None if shared_up is None else pack_bf16(shared_up)
+        sd = None if shared_down is None else pack_bf16(shared_down)
+        return cls(hidden, inter, n_experts, top_k, router_w, packed, sg, su, sd, router_bias)
 
     def workspace(self, n_tokens, device=None):
         dev = device if device is not None else self.router_w.device
@@ -194,6 +237,17 @@ def rmsnorm(x, gamma, eps, out, stream=None):
 def dequant_export(layer, expert, matrix, out, stream=None):
     _check(_lib().moe_dequant_export(layer.desc, expert, matrix, _ptr(out), _stream(stream)),
            "moe_dequant_export")
+
+
+def profile_events(event_array, n):
+    """Register an array of n hipEvent_t handles (ctypes array) for per-kernel
+    timing on this host thread; pass None to stop."""
+    _check(_lib().moe_profile_events(event_array, n if event_array is not None else 0),
+           "moe_profile_events")
+
+
+def profile_count():
+    return _lib().moe_profile_count()
 
 
 def mxfp8_quantize(x, codes, scales, stream=None):

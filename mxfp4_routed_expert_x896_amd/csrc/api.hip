@@ -14,6 +14,27 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// Benchmark timing hook (see moe_profile_events in the header).
+struct ProfileHook {
+  hipEvent_t* events = nullptr;
+  int n = 0;
+  int used = 0;
+};
+thread_local ProfileHook g_prof;
+
+void prof_begin(hipStream_t stream) {
+  g_prof.used = 0;
+  if (g_prof.events != nullptr && g_prof.n > 0) {
+    (void)hipEventRecord(g_prof.events[0], stream);
+    g_prof.used = 1;
+  }
+}
+
+void prof_mark(hipStream_t stream) {
+  if (g_prof.events != nullptr && g_prof.used > 0 && g_prof.used < g_prof.n)
+    (void)hipEventRecord(g_prof.events[g_prof.used++], stream);
+}
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -33,11 +54,12 @@ int check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int launched(hipError_t e) {
+int launched(hipError_t e, hipStream_t stream) {
   if (e != hipSuccess) {
     g_last_hip_error = int(e);
     return MOE_ELAUNCH;
   }
+  prof_mark(stream);
   return MOE_OK;
 }
 
@@ -63,7 +85,7 @@ int check_layer(const moe_layer_desc* L) {
   if (L->n_shared > 0 &&
       (!aligned16(L->shared_gate) || !aligned16(L->shared_up) || !aligned16(L->shared_down)))
     return MOE_EALIGN;
-  if (L->expert_stride < record_bytes(L->hidden, L->inter)) return MOE_ESHAPE;
+  if (L->expert_stride < moe::packed_record_bytes(L->hidden, L->inter)) return MOE_ESHAPE;
   return MOE_OK;
 }
 
@@ -73,7 +95,7 @@ uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, total;
+  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, total;
 };
 
 Carve carve(const moe_layer_desc* L, int64_t T) {
@@ -94,7 +116,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
   c.h = take(t * k * I * 4);
   c.hs = take(S * t * I * 4);
   c.part = take(t * k * H * 4);
-  c.ysh = take(t * H * 4);
+  c.ysh = take(S * t * H * 4);
+  c.tile_cnt = take(((H + 63) / 64) * 4);
   c.total = off;
   return c;
 }
@@ -122,14 +145,13 @@ int do_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, int32_t* ids
   const Carve c = carve(L, T);
   float* logits = at<float>(ws, c.logits);
   int st = launched(moe::launch_router_logits(x, L->router_w, L->router_bias, logits, int(T),
-                                              L->hidden, L->n_experts, stream));
+                                              L->hidden, L->n_experts, stream), stream);
   if (st) return st;
-  return launched(moe::launch_router_topk(logits, int(T), L->n_experts, L->top_k, ids, w, stream));
+  return launched(moe::launch_router_topk(logits, int(T), L->n_experts, L->top_k, ids, w, stream), stream);
 }
 
-int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
-                    const float* w, const uint16_t* residual, uint16_t* y, void* ws,
-                    hipStream_t stream) {
+moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                          const float* w, const uint16_t* residual, uint16_t* y, void* ws) {
   const Carve c = carve(L, T);
   moe::GemvLayer G;
   G.T = int(T);
@@ -150,15 +172,55 @@ int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const
   G.plan.pairs = at<int32_t>(ws, c.pairs);
   const int64_t pairs = T * L->top_k;
   G.max_active = int(pairs < L->n_experts ? pairs : L->n_experts);
-  G.h = at<float>(ws, c.h);
-  G.hs = at<float>(ws, c.hs);
+  G.h = at<uint16_t>(ws, c.h);
+  G.hs = at<uint16_t>(ws, c.hs);
   G.part = at<float>(ws, c.part);
   G.ysh = at<float>(ws, c.ysh);
-  int st = launched(moe::launch_plan(ids, int(pairs), L->n_experts, G.plan, stream));
+  G.tile_cnt = at<int>(ws, c.tile_cnt);
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  return G;
+}
+
+int n_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
+
+// Expert kernels once the plan exists.
+int run_experts(const moe::GemvLayer& G, hipStream_t stream) {
+  int st = launched(moe::launch_gateup(G, stream), stream);
   if (st) return st;
-  if ((st = launched(moe::launch_gateup(G, stream)))) return st;
-  if ((st = launched(moe::launch_down(G, stream)))) return st;
-  return launched(moe::launch_combine(G, w, residual, y, stream));
+  return launched(moe::launch_down(G, stream), stream);
+}
+
+int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
+                    const float* w, const uint16_t* residual, uint16_t* y, void* ws,
+                    hipStream_t stream) {
+  const moe::GemvLayer G = gemv_layer(L, x, T, w, residual, y, ws);
+  int st = launched(moe::launch_plan(ids, int(T * L->top_k), L->n_experts, G.plan, G.tile_cnt,
+                                     n_tiles(L), stream), stream);
+  if (st) return st;
+  return run_experts(G, stream);
+}
+
+// Router, then the experts.  Decode batches select and plan in one launch.
+int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                  const uint16_t* residual, uint16_t* y, int32_t* ids, float* w, void* ws,
+                  hipStream_t stream) {
+  if (T > moe::kSelectPlanMaxTokens) {
+    int st = do_route(L, x, T, ids, w, ws, stream);
+    if (st) return st;
+    return do_forward_gemv(L, x, T, ids, w, residual, y, ws, stream);
+  }
+  const Carve c = carve(L, T);
+  float* logits = at<float>(ws, c.logits);
+  int st = launched(moe::launch_router_logits(x, L->router_w, L->router_bias, logits, int(T),
+                                              L->hidden, L->n_experts, stream), stream);
+  if (st) return st;
+  const moe::GemvLayer G = gemv_layer(L, x, T, w, residual, y, ws);
+  st = launched(moe::launch_router_select_plan(logits, int(T), L->n_experts, L->top_k, ids, w,
+                                               G.plan, G.tile_cnt, n_tiles(L), stream), stream);
+  if (st) return st;
+  return run_experts(G, stream);
 }
 
 int resolve_path(int32_t path, int64_t T) {
@@ -186,10 +248,68 @@ MOE_API const char* moe_status_string(int status) {
 
 MOE_API int moe_last_hip_error(void) { return g_last_hip_error; }
 
+MOE_API int moe_profile_events(hipEvent_t* events, int32_t n_events) {
+  if (events == nullptr || n_events <= 0) {
+    g_prof = ProfileHook();
+    return MOE_OK;
+  }
+  g_prof.events = events;
+  g_prof.n = n_events;
+  g_prof.used = 0;
+  return MOE_OK;
+}
+
+MOE_API int moe_profile_count(void) { return g_prof.used; }
+
 MOE_API int moe_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes) {
   if (out_bytes == nullptr || hidden <= 0 || inter <= 0) return MOE_EINVAL;
   if (hidden % 32 || inter % 32) return MOE_ESHAPE;
   *out_bytes = record_bytes(hidden, inter);
+  return MOE_OK;
+}
+
+MOE_API int moe_packed_record_bytes(int32_t hidden, int32_t inter, uint64_t* out_bytes) {
+  if (out_bytes == nullptr || hidden <= 0 || inter <= 0) return MOE_EINVAL;
+  if (hidden % 32 || inter % 32) return MOE_ESHAPE;
+  *out_bytes = moe::packed_record_bytes(hidden, inter);
+  return MOE_OK;
+}
+
+MOE_API int moe_pack_experts(const uint8_t* src, uint64_t src_stride, uint8_t* dst,
+                             uint64_t dst_stride, int32_t n_experts, int32_t hidden,
+                             int32_t inter, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || n_experts <= 0 || hidden <= 0 || inter <= 0)
+    return MOE_EINVAL;
+  if (hidden % 32 || inter % 32 || hidden > 8192 || inter > 8192) return MOE_ESHAPE;
+  if (src_stride < record_bytes(hidden, inter)) return MOE_ESHAPE;
+  if (dst_stride < moe::packed_record_bytes(hidden, inter)) return MOE_ESHAPE;
+  if (!aligned16(src) || !aligned16(dst) || (src_stride & 15u) || (dst_stride & 15u))
+    return MOE_EALIGN;
+  int st = check_device();
+  if (st) return st;
+  prof_begin(stream);
+  for (int32_t e = 0; e < n_experts; ++e) {
+    st = launched(moe::launch_pack_record(src + uint64_t(e) * src_stride, hidden, inter,
+                                          dst + uint64_t(e) * dst_stride, stream),
+                  stream);
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
+MOE_API int moe_pack_bf16(const uint16_t* src, uint16_t* dst, int32_t count, int32_t rows,
+                          int32_t cols, hipStream_t stream) {
+  if (src == nullptr || dst == nullptr || count <= 0 || rows <= 0 || cols <= 0) return MOE_EINVAL;
+  if (rows % 16 || cols % 32) return MOE_ESHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_EALIGN;
+  int st = check_device();
+  if (st) return st;
+  prof_begin(stream);
+  const uint64_t n = uint64_t(rows) * cols;
+  for (int32_t i = 0; i < count; ++i) {
+    st = launched(moe::launch_pack_bf16(src + i * n, rows, cols, dst + i * n, stream), stream);
+    if (st) return st;
+  }
   return MOE_OK;
 }
 
@@ -215,6 +335,7 @@ MOE_API int moe_route(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_EALIGN;
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
+  prof_begin(stream);
   return do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream);
 }
 
@@ -233,6 +354,7 @@ MOE_API int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t 
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
   if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
+  prof_begin(stream);
   return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
 }
 
@@ -251,8 +373,8 @@ MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
   if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
-  if ((st = do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream))) return st;
-  return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+  prof_begin(stream);
+  return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
 }
 
 MOE_API int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_tokens,
@@ -264,7 +386,8 @@ MOE_API int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int
   if (!(eps >= 0.0f)) return MOE_EINVAL;
   int st = check_device();
   if (st) return st;
-  return launched(moe::launch_rmsnorm(x, gamma, eps, int(n_tokens), hidden, out, stream));
+  prof_begin(stream);
+  return launched(moe::launch_rmsnorm(x, gamma, eps, int(n_tokens), hidden, out, stream), stream);
 }
 
 MOE_API int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matrix,
@@ -276,8 +399,9 @@ MOE_API int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int3
   if (!aligned16(out)) return MOE_EALIGN;
   if ((st = check_device())) return st;
   const uint8_t* rec = layer->experts + uint64_t(expert) * layer->expert_stride;
+  prof_begin(stream);
   return launched(
-      moe::launch_dequant_export(rec, layer->hidden, layer->inter, matrix, out, stream));
+      moe::launch_dequant_export(rec, layer->hidden, layer->inter, matrix, out, stream), stream);
 }
 
 MOE_API int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* codes,
@@ -289,5 +413,6 @@ MOE_API int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uin
   if (uint64_t(n_rows) * uint64_t(k / 32) > (uint64_t(UINT_MAX) - 255)) return MOE_ESHAPE;
   int st = check_device();
   if (st) return st;
-  return launched(moe::launch_mxfp8_quantize(x, n_rows, k, codes, scales, stream));
+  prof_begin(stream);
+  return launched(moe::launch_mxfp8_quantize(x, n_rows, k, codes, scales, stream), stream);
 }

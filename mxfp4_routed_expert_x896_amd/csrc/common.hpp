@@ -54,13 +54,81 @@ __device__ __forceinline__ f32x2_t fp4x2_to_f32x2(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
 }
 
-// ------------------------------------------------------------ reductions --
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Eight E2M1 codes (one dword, low nibble first) times the fp32 scale sc,
+// as eight bf16 (v_cvt_scalef32_pk_bf16_fp4).  For sc = 2^e this is exact:
+// every E2M1 value times a power of two is a bf16 (subnormals included) up
+// to overflow; a NaN scale gives NaN.
+__device__ __forceinline__ u32x4 fp4x8_scaled(uint32_t w, float sc) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  return r;
 }
+
+// ------------------------------------------------------------ reductions --
+// Wave-wide reductions with DPP row operations (a few cycles per step, no
+// LDS round trip): quad swaps, half-row and row mirrors, then the row
+// broadcasts; the total ends in lane 63 and is broadcast with readlane.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_sum_step(float v) {
+  return v + __uint_as_float(dpp_or_zero<CTRL, ROW_MASK>(__float_as_uint(v)));
+}
+
+// Sum over all 64 lanes (every lane must be active); result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_sum_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_sum_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_sum_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_sum_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_sum_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_sum_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(v)), 63)));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint64_t o = (uint64_t(dpp_or_zero<CTRL, ROW_MASK>(uint32_t(v >> 32))) << 32) |
+                     dpp_or_zero<CTRL, ROW_MASK>(uint32_t(v));
+  return o > v ? o : v;
+}
+
+// Maximum of an unsigned 64-bit key over all 64 lanes; result in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);
+  v = dpp_max_step<0x4E, 0xF>(v);
+  v = dpp_max_step<0x141, 0xF>(v);
+  v = dpp_max_step<0x140, 0xF>(v);
+  v = dpp_max_step<0x142, 0xA>(v);
+  v = dpp_max_step<0x143, 0xC>(v);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// ------------------------------------------------------------- layout -----
+// MFMA-tiled MXFP4 matrix (written by the pack kernels, see pack.hip): code
+// tiles of 16 rows x 128 columns (1 KiB, lane order), then the scales, lane
+// by lane, nkb4 bytes each.
+struct PackedMx {
+  int nb, nkb, nkb4;   // blocks per row, 128-column tiles per row group, nkb rounded to 4
+  size_t code_bytes;   // offset of the scales
+  size_t bytes;        // whole matrix
+  __host__ __device__ PackedMx(int R, int K) {
+    nb = K / 32;
+    nkb = (nb + 3) / 4;
+    nkb4 = (nkb + 3) / 4 * 4;
+    code_bytes = size_t(R / 16) * nkb * 1024;
+    bytes = code_bytes + size_t(R / 16) * 64 * nkb4;
+  }
+};
 
 // --------------------------------------------------------------- plan -----
 // Token -> expert grouping written by the plan kernel and read by the expert

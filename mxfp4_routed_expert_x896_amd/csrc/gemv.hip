@@ -1,21 +1,33 @@
-// Decode-path expert kernels: dequant-fused MXFP4 GEMV for the routed
-// experts, bf16 GEMV for the shared experts, and the weighted combine.
+// Decode-path expert kernels on the matrix cores: dequant-fused MXFP4
+// gate/up and down projections for the routed experts, the bf16 shared
+// experts, and the weighted combine.
 //
 // Deltafin README ("An experiment in running Kimi K3 ..."), "Techniques /
-// Compute": the MXFP4 weights are decoded inside the product rather than
-// dequantised to a temporary first; the Deltafin explainer (bhfrc.com),
-// section 6.2, gives the reason: a separate dequantisation pass costs
-// memory and another trip through memory bandwidth.  Here a weight never
-// exists in dequantised form outside registers: each 16-byte chunk of codes
-// (one 32-element scale block) is converted to bf16 pairs with
-// v_cvt_scalef32_pk_bf16_fp4 and multiplied into the token with
-// v_dot2_f32_bf16; the block's E8M0 exponent scales the block's fp32 partial.
+// Compute": the MXFP4 weights are decoded inside the product instead of
+// being dequantised to a temporary first; the Deltafin explainer
+// (bhfrc.com), section 6.2, gives the reason (a separate pass costs memory
+// and another trip through memory bandwidth).  Here a weight never exists in
+// dequantised form outside registers.  Each lane loads 16 bytes of codes --
+// one whole 32-element block of one row, so one E8M0 exponent -- converts
+// them with v_cvt_scalef32_pk_bf16_fp4 (the block exponent applied in the
+// convert; exact, since an E2M1 value times a power of two is a bf16,
+// subnormals included) and feeds them as the A operand of
+// v_mfma_f32_16x16x32_bf16.  The tokens routed to the expert are the B
+// columns (up to 16 per pass), accumulation is fp32.  At batch 1 only one B
+// column is live: the matrix core is used to take the multiply-accumulate
+// off the vector ALU (one convert per code byte remains), which is what
+// lets the weight stream run near the HBM roof; batched decode then reuses
+// every converted weight for all tokens of the expert at no extra cost.
 //
-// Mapping (gfx950, wave64): one wave owns one weight row at a time; lane l
-// reads chunks c = l, l + 64, ... so every load instruction covers 1 KiB of
-// contiguous codes; the activations for those chunks stay in registers
-// across all rows of the workgroup.  Gate and up rows with the same index are
-// processed together so SiLU(g) * u is formed before anything is written.
+// Operand mapping (wave64, lane l: g = l / 16, c = l % 16): weights are
+// read in the MFMA-tiled layout written by pack.hip, so for super-step kb a
+// wave loads one 1088-byte tile: lane l gets block bi = 4 kb + g of row
+// r0 + c (16 contiguous bytes of a 1 KiB contiguous read) and its scale
+// byte.  MFMA step s (0..3) takes elements 8 s .. 8 s + 7 of that block,
+// i.e. contraction index K = 32 bi + 8 s + j; the B lane (g, c) supplies the
+// same K indices of token c.  The 16 x 16 fp32 result leaves rows 4 g + i
+// (i = 0..3) of token c in lane (g, c).  bf16 (shared) matrices use 1 KiB
+// tiles of 16 rows x 32 columns, lane l holding columns 8 g .. 8 g + 7.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,11 +37,12 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRowsGU = 16;   // routed gate/up rows per workgroup
-constexpr int kRowsGUS = 4;   // shared gate/up rows per workgroup
-constexpr int kRowsD = 32;    // routed down rows per workgroup
-constexpr int kRowsDS = 16;   // shared down rows per workgroup
-constexpr int kSharedTokens = 2;  // tokens per LDS pass in the shared gate/up
+constexpr int kRowsD = 64;        // down rows per workgroup (16 per wave)
+constexpr int kCols = 16;         // B columns of one MFMA: at most 16 tokens per pass
+constexpr int kLdsBudget = 32768;  // bytes of staged activations per workgroup
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -39,457 +52,466 @@ __device__ __forceinline__ u32x4 ld_nt(const void* p) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// 32 E2M1 codes (one scale block) against 32 bf16 activations.
-__device__ __forceinline__ float block_dot_bf16(const u32x4& codes, const uint32_t* xv, float acc) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t w = codes[d];
-    acc = dot2_bf16(fp4x2_to_bf16x2<0>(w), xv[4 * d + 0], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<1>(w), xv[4 * d + 1], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<2>(w), xv[4 * d + 2], acc);
-    acc = dot2_bf16(fp4x2_to_bf16x2<3>(w), xv[4 * d + 3], acc);
+__device__ __forceinline__ f32x4_t mfma(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 hi + bf16 lo with hi + lo = v to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+// Partials cross workgroups (and XCDs, whose L2s are private): they are
+// stored and re-read with device-scope atomic accesses, which the compiler
+// emits as write-through stores and L2-bypassing loads, instead of fencing
+// (a device-scope fence writes back and invalidates the whole L2).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Stage the bf16 rows of mt tokens into LDS rows of `stride` elements:
+// dst[j][0..K) = src(j)[0..K); sources via the callback src(j).
+template <typename Src>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, int stride, int mt, int K, Src src) {
+  const int nch = K / 8;
+  for (int i = threadIdx.x; i < mt * nch; i += kThreads) {
+    const int j = i / nch, q = i % nch;
+    *reinterpret_cast<u32x4*>(dst + j * stride + q * 8) = ld16(src(j) + q * 8);
   }
-  return acc;
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // ------------------------------------------------------------------------
-// Routed gate/up: workgroup = (active expert a, tile of kRowsGU rows).
-// CPL = code chunks per lane per row; MT = tokens held in registers at once.
-template <int CPL, int MT>
-__device__ void routed_gateup(const GemvLayer& L, int a, int tile) {
+// Gate/up.  Workgroup = (contributor, 32 rows): wave w takes row group
+// w / 2 of the tile and half w % 2 of the contraction; the halves meet in
+// LDS.  The tokens' x rows are staged in LDS (B operand), mtp at a time.
+// Weight tiles are double-buffered: the loads of super-step kq + 1 are in
+// flight while super-step kq is converted and multiplied.
+
+struct GuTiles {
+  u32x4 g[4], u[4];
+  uint32_t sg, su;
+};
+
+__device__ __forceinline__ void load_gu(GuTiles& t, const uint8_t* gcodes, const uint8_t* ucodes,
+                                        const uint8_t* gscl, const uint8_t* uscl, int kq, int nkb,
+                                        int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kb = 4 * kq + j;
+    t.g[j] = kb < nkb ? ld_nt(gcodes + size_t(kb) * 1024 + 16 * lane) : u32x4{0, 0, 0, 0};
+    t.u[j] = kb < nkb ? ld_nt(ucodes + size_t(kb) * 1024 + 16 * lane) : u32x4{0, 0, 0, 0};
+  }
+  t.sg = *reinterpret_cast<const uint32_t*>(gscl + 4 * kq);
+  t.su = *reinterpret_cast<const uint32_t*>(uscl + 4 * kq);
+}
+
+__device__ __forceinline__ void mma_gu(const GuTiles& t, const uint16_t* xrow, int kq, int nb,
+                                       int g, f32x4_t& ag, f32x4_t& au) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bi = 16 * kq + 4 * j + g;
+    const float sg = e8m0_to_f32((t.sg >> (8 * j)) & 0xFFu);
+    const float su = e8m0_to_f32((t.su >> (8 * j)) & 0xFFu);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bx = bi < nb ? lds16(xrow + bi * 32 + 8 * s) : u32x4{0, 0, 0, 0};
+      ag = mfma(fp4x8_scaled(t.g[j][s], sg), bx, ag);
+      au = mfma(fp4x8_scaled(t.u[j][s], su), bx, au);
+    }
+  }
+}
+
+// Adds the partner half's tiles (wave w ^ 1) into waves with even index.
+__device__ __forceinline__ void join_halves(f32x4_t& a, f32x4_t& b, float* red) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  __syncthreads();
+  if (wave & 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[(wave * kWave + lane) * 8 + i] = a[i];
+      red[(wave * kWave + lane) * 8 + 4 + i] = b[i];
+    }
+  }
+  __syncthreads();
+  if (!(wave & 1)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] += red[((wave + 1) * kWave + lane) * 8 + i];
+      b[i] += red[((wave + 1) * kWave + lane) * 8 + 4 + i];
+    }
+  }
+}
+
+__device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
   if (a >= L.plan.n_active[0]) return;
   const int e = L.plan.active[a];
   const int p0 = L.plan.act_off[a];
   const int p1 = L.plan.act_off[a + 1];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
   const int H = L.H, I = L.I;
-  const int nch = H / 32;
-  const size_t code_bytes = size_t(I) * H / 2;
-  const size_t scale_bytes = size_t(I) * H / 32;
-  const uint8_t* gc = L.experts + size_t(e) * L.stride;
-  const uint8_t* gs = gc + code_bytes;
-  const uint8_t* uc = gs + scale_bytes;
-  const uint8_t* us = uc + code_bytes;
+  const PackedMx pm(I, H);
+  const int nkq = pm.nkb4 / 4;
+  const int kqh = (nkq + 1) / 2;
+  const int kq0 = (wave & 1) * kqh, kq1 = min(kq0 + kqh, nkq);
+  const int rg = tile * 2 + wave / 2;
+  const uint8_t* gbase = L.experts + size_t(e) * L.stride;
+  const uint8_t* ubase = gbase + pm.bytes;
+  const uint8_t* gcodes = gbase + size_t(rg) * pm.nkb * 1024;
+  const uint8_t* ucodes = ubase + size_t(rg) * pm.nkb * 1024;
+  const uint8_t* gscl = gbase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  const uint8_t* uscl = ubase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  const int xstride = H + 8;
+  uint16_t* hhi = L.h;
+  uint16_t* hlo = L.h + size_t(L.T) * L.k * I;
 
-  for (int g0 = p0; g0 < p1; g0 += MT) {
-    uint32_t xr[MT][CPL][16];
-    int pr[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const bool valid = g0 + t < p1;
-      pr[t] = valid ? L.plan.pairs[g0 + t] : -1;
-      const int tok = valid ? min(pr[t] / L.k, L.T - 1) : 0;
-      const uint16_t* xrow = L.x + size_t(tok) * H;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + kWave * i;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u32x4 q = (valid && c < nch) ? ld16(xrow + c * 32 + v * 8) : u32x4{0, 0, 0, 0};
-          xr[t][i][4 * v + 0] = q[0];
-          xr[t][i][4 * v + 1] = q[1];
-          xr[t][i][4 * v + 2] = q[2];
-          xr[t][i][4 * v + 3] = q[3];
-        }
-      }
+  for (int t0 = p0; t0 < p1; t0 += L.mtp_gu) {
+    const int mt = min(L.mtp_gu, p1 - t0);
+    GuTiles cur, nxt;
+    if (kq0 < kq1) load_gu(cur, gcodes, ucodes, gscl, uscl, kq0, pm.nkb, lane);
+    __syncthreads();
+    stage_rows(xs, xstride, mt, H, [&](int j) {
+      return L.x + size_t(min(L.plan.pairs[t0 + j] / L.k, L.T - 1)) * H;
+    });
+    __syncthreads();
+    const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kq = kq0; kq < kq1; ++kq) {
+      if (kq + 1 < kq1) load_gu(nxt, gcodes, ucodes, gscl, uscl, kq + 1, pm.nkb, lane);
+      mma_gu(cur, xrow, kq, pm.nb, g, ag, au);
+      cur = nxt;
     }
-#pragma unroll 2
-    for (int q = 0; q < kRowsGU / kWaves; ++q) {
-      const int r = tile * kRowsGU + wave + kWaves * q;
-      const uint8_t* grow = gc + size_t(r) * (H / 2);
-      const uint8_t* urow = uc + size_t(r) * (H / 2);
-      u32x4 gw[CPL], uw[CPL];
-      uint32_t gsb[CPL], usb[CPL];
+    join_halves(ag, au, red);
+    if (!(wave & 1) && c < mt) {
+      const int pair = L.plan.pairs[t0 + c];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) {
-          gw[i] = ld_nt(grow + c * 16);
-          uw[i] = ld_nt(urow + c * 16);
-          gsb[i] = gs[size_t(r) * nch + c];
-          usb[i] = us[size_t(r) * nch + c];
-        } else {
-          gw[i] = uw[i] = u32x4{0, 0, 0, 0};
-          gsb[i] = usb[i] = 127;
-        }
-      }
-      float ag[MT], au[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const float sg = e8m0_to_f32(gsb[i]);
-        const float su = e8m0_to_f32(usb[i]);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          ag[t] = fmaf(block_dot_bf16(gw[i], xr[t][i], 0.0f), sg, ag[t]);
-          au[t] = fmaf(block_dot_bf16(uw[i], xr[t][i], 0.0f), su, au[t]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float g = wave_sum(ag[t]);
-        const float u = wave_sum(au[t]);
-        if (lane == 0 && pr[t] >= 0) L.h[size_t(pr[t]) * I + r] = silu(g) * u;
+      for (int i = 0; i < 4; ++i) {
+        uint16_t hi, lo;
+        split_bf16(silu(ag[i]) * au[i], hi, lo);
+        const size_t o = size_t(pair) * I + rg * 16 + 4 * g + i;
+        hhi[o] = hi;
+        hlo[o] = lo;
       }
     }
   }
 }
 
-// Shared gate/up (bf16 weights): workgroup = (shared expert s, tile of
-// kRowsGUS rows, one per wave); all T tokens, MT at a time, staged in LDS.
-// CPLS = 16-byte chunks (8 bf16) per lane per row, consumed 4 at a time.
-template <int CPLS, int MT>
-__device__ void shared_gateup(const GemvLayer& L, int s, int tile, u32x4* xs) {
+// Shared gate/up (bf16): 1 KiB tiles of 16 rows x 32 columns are the A
+// operand as loaded; four tiles per super-step, double-buffered.
+__device__ void shared_gateup(const GemvLayer& L, int sx, int tile, uint16_t* xs, float* red) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
   const int H = L.H, I = L.I;
-  const int nch = H / 8;
-  const uint16_t* G = L.sgate + size_t(s) * I * H;
-  const uint16_t* U = L.sup + size_t(s) * I * H;
-  const int r = tile * kRowsGUS + wave;
-  const uint16_t* grow = G + size_t(r) * H;
-  const uint16_t* urow = U + size_t(r) * H;
-  for (int t0 = 0; t0 < L.T; t0 += MT) {
-    const int nt = min(MT, L.T - t0);
+  const int nu = H / 32;
+  const int nq = (nu + 3) / 4;
+  const int qh = (nq + 1) / 2;
+  const int q0 = (wave & 1) * qh, q1 = min(q0 + qh, nq);
+  const int rg = tile * 2 + wave / 2;
+  const uint16_t* gt = L.sgate + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
+  const uint16_t* ut = L.sup + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
+  const int xstride = H + 8;
+  const size_t plane = size_t(L.S) * L.T * I;
+  auto load = [&](u32x4 (&wg)[4], u32x4 (&wu)[4], int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = 4 * q + j;
+      wg[j] = u < nu ? ld_nt(gt + size_t(u) * 512 + 8 * lane) : u32x4{0, 0, 0, 0};
+      wu[j] = u < nu ? ld_nt(ut + size_t(u) * 512 + 8 * lane) : u32x4{0, 0, 0, 0};
+    }
+  };
+  for (int t0 = 0; t0 < L.T; t0 += L.mtp_gu) {
+    const int mt = min(L.mtp_gu, L.T - t0);
+    u32x4 cg[4], cu[4], ng[4], nu4[4];
+    if (q0 < q1) load(cg, cu, q0);
     __syncthreads();
-    const u32x4* src = reinterpret_cast<const u32x4*>(L.x + size_t(t0) * H);
-    for (int i = threadIdx.x; i < nt * nch; i += kThreads) xs[i] = src[i];
+    stage_rows(xs, xstride, mt, H, [&](int j) { return L.x + size_t(t0 + j) * H; });
     __syncthreads();
-    float ag[MT], au[MT];
+    const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = q0; q < q1; ++q) {
+      if (q + 1 < q1) load(ng, nu4, q + 1);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.0f;
-#pragma unroll
-    for (int i0 = 0; i0 < CPLS; i0 += 4) {
-      u32x4 gw[4], uw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = lane + kWave * (i0 + i);
-        gw[i] = c < nch ? ld_nt(grow + c * 8) : u32x4{0, 0, 0, 0};
-        uw[i] = c < nch ? ld_nt(urow + c * 8) : u32x4{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) {
+        const int u = 4 * q + j;
+        const u32x4 bx = u < nu ? lds16(xrow + u * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+        ag = mfma(cg[j], bx, ag);
+        au = mfma(cu[j], bx, au);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = lane + kWave * (i0 + i);
-        if (c < nch) {
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            if (t < nt) {
-              const u32x4 xv = xs[t * nch + c];
-#pragma unroll
-              for (int d = 0; d < 4; ++d) {
-                ag[t] = dot2_bf16(gw[i][d], xv[d], ag[t]);
-                au[t] = dot2_bf16(uw[i][d], xv[d], au[t]);
-              }
-            }
-          }
-        }
+      for (int j = 0; j < 4; ++j) {
+        cg[j] = ng[j];
+        cu[j] = nu4[j];
       }
     }
+    join_halves(ag, au, red);
+    if (!(wave & 1) && c < mt) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float g = wave_sum(ag[t]);
-      const float u = wave_sum(au[t]);
-      if (lane == 0 && t < nt) L.hs[(size_t(s) * L.T + t0 + t) * I + r] = silu(g) * u;
+      for (int i = 0; i < 4; ++i) {
+        uint16_t hi, lo;
+        split_bf16(silu(ag[i]) * au[i], hi, lo);
+        const size_t o = (size_t(sx) * L.T + t0 + c) * I + rg * 16 + 4 * g + i;
+        L.hs[o] = hi;
+        L.hs[plane + o] = lo;
+      }
     }
   }
 }
 
-// Grid: [shared tiles (S * I / kRowsGUS)] then [max_active * I / kRowsGU].
-template <int CPL, int MT>
+// Grid: [S * I / 32 shared tiles] then [max_active * I / 32 routed tiles].
 __global__ __launch_bounds__(kThreads) void gateup_kernel(GemvLayer L) {
-  __shared__ u32x4 xs[kSharedTokens * 1024];  // kSharedTokens rows of H <= 8192 bf16
-  const int shared_wgs = L.S * (L.I / kRowsGUS);
+  extern __shared__ u32x4 lds_raw[];
+  __shared__ float red[kWaves * kWave * 8];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds_raw);
+  const int tiles = L.I / 32;
+  const int shared_wgs = L.S * tiles;
   const int b = blockIdx.x;
-  if (b < shared_wgs) {
-    const int tiles = L.I / kRowsGUS;
-    shared_gateup<4 * CPL, kSharedTokens>(L, b / tiles, b % tiles, xs);
-  } else {
-    const int tiles = L.I / kRowsGU;
-    const int r = b - shared_wgs;
-    routed_gateup<CPL, MT>(L, r / tiles, r % tiles);
-  }
+  if (b < shared_wgs)
+    shared_gateup(L, b / tiles, b % tiles, xs, red);
+  else
+    routed_gateup(L, (b - shared_wgs) / tiles, (b - shared_wgs) % tiles, xs, red);
 }
 
 // ------------------------------------------------------------------------
-// Routed down: workgroup = (active expert a, tile of kRowsD output rows).
-// part[pair][n] = sum_k Wd[n][k] h[pair][k]  (unweighted).
-template <int CPL, int MT>
-__device__ void routed_down(const GemvLayer& L, int a, int tile) {
-  if (a >= L.plan.n_active[0]) return;
+// Down projections and the combine.  Workgroups are (contributor, tile of
+// kRowsD output rows, 16 per wave); contributors are the active experts
+// (MXFP4) and the shared experts (bf16).  h enters as bf16 hi + lo, staged
+// in LDS, two MFMAs per step.  Each contributor writes fp32 partials for
+// its rows and tokens; the last workgroup to finish a tile (device-scope
+// counter, zeroed by the plan kernel of the same call) sums the tile's
+// partials in a fixed order -- routed slots j = 0..k-1 weighted by w, then
+// shared experts, then the residual -- and writes the bf16 output.  The sum
+// order does not depend on which workgroup arrives last, so the output is
+// deterministic.
+
+struct DnTiles {
+  u32x4 w[4];
+  uint32_t sc;
+};
+
+__device__ void routed_down(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int rg = tile * (kRowsD / 16) + wave;
+  const bool live = rg < L.H / 16;  // ragged last tile
   const int e = L.plan.active[a];
   const int p0 = L.plan.act_off[a];
   const int p1 = L.plan.act_off[a + 1];
+  const int H = L.H, I = L.I;
+  const PackedMx pgu(I, H), pd(H, I);
+  const int nkq = pd.nkb4 / 4;
+  const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
+  const uint8_t* codes = base + size_t(live ? rg : 0) * pd.nkb * 1024;
+  const uint8_t* scl = base + pd.code_bytes + (size_t(live ? rg : 0) * 64 + lane) * pd.nkb4;
+  const int hstride = I + 8;
+  uint16_t* hs_hi = hsm;
+  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
+  const uint16_t* hhi = L.h;
+  const uint16_t* hlo = L.h + size_t(L.T) * L.k * I;
+  auto load = [&](DnTiles& t, int kq) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = 4 * kq + j;
+      t.w[j] = kb < pd.nkb ? ld_nt(codes + size_t(kb) * 1024 + 16 * lane) : u32x4{0, 0, 0, 0};
+    }
+    t.sc = *reinterpret_cast<const uint32_t*>(scl + 4 * kq);
+  };
+
+  for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
+    const int mt = min(L.mtp_d, p1 - t0);
+    DnTiles cur, nxt;
+    if (live) load(cur, 0);
+    __syncthreads();
+    stage_rows(hs_hi, hstride, mt, I,
+               [&](int j) { return hhi + size_t(L.plan.pairs[t0 + j]) * I; });
+    stage_rows(hs_lo, hstride, mt, I,
+               [&](int j) { return hlo + size_t(L.plan.pairs[t0 + j]) * I; });
+    __syncthreads();
+    if (!live) continue;
+    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
+    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kq = 0; kq < nkq; ++kq) {
+      if (kq + 1 < nkq) load(nxt, kq + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bi = 16 * kq + 4 * j + g;
+        const float sd = e8m0_to_f32((cur.sc >> (8 * j)) & 0xFFu);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 aw = fp4x8_scaled(cur.w[j][s], sd);
+          const u32x4 vh = bi < pd.nb ? lds16(bh + bi * 32 + 8 * s) : u32x4{0, 0, 0, 0};
+          const u32x4 vl = bi < pd.nb ? lds16(bl + bi * 32 + 8 * s) : u32x4{0, 0, 0, 0};
+          acc = mfma(aw, vh, acc);
+          acc = mfma(aw, vl, acc);
+        }
+      }
+      cur = nxt;
+    }
+    if (c < mt) {
+      const int pair = L.plan.pairs[t0 + c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_coherent(&L.part[size_t(pair) * H + rg * 16 + 4 * g + i], acc[i]);
+    }
+  }
+}
+
+__device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm) {
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int rg = tile * (kRowsD / 16) + wave;
+  const bool live = rg < L.H / 16;
   const int H = L.H, I = L.I;
-  const int nch = I / 32;
-  const size_t gu_bytes = 2 * (size_t(I) * H / 2 + size_t(I) * H / 32);
-  const uint8_t* dc = L.experts + size_t(e) * L.stride + gu_bytes;
-  const uint8_t* ds = dc + size_t(H) * I / 2;
-
-  for (int g0 = p0; g0 < p1; g0 += MT) {
-    float hr[MT][CPL][32];
-    int pr[MT];
+  const int nu = I / 32;
+  const int nq = (nu + 3) / 4;
+  const uint16_t* dt = L.sdown + sx * (size_t(H) * I) + size_t(live ? rg : 0) * nu * 512;
+  const int hstride = I + 8;
+  uint16_t* hs_hi = hsm;
+  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
+  const size_t plane = size_t(L.S) * L.T * I;
+  auto load = [&](u32x4 (&w)[4], int q) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const bool valid = g0 + t < p1;
-      pr[t] = valid ? L.plan.pairs[g0 + t] : -1;
-      const float* hrow = L.h + size_t(valid ? pr[t] : 0) * I;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + kWave * i;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const u32x4 q = (valid && c < nch) ? ld16(hrow + c * 32 + v * 4) : u32x4{0, 0, 0, 0};
-          hr[t][i][4 * v + 0] = __uint_as_float(q[0]);
-          hr[t][i][4 * v + 1] = __uint_as_float(q[1]);
-          hr[t][i][4 * v + 2] = __uint_as_float(q[2]);
-          hr[t][i][4 * v + 3] = __uint_as_float(q[3]);
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int u = 4 * q + j;
+      w[j] = u < nu ? ld_nt(dt + size_t(u) * 512 + 8 * lane) : u32x4{0, 0, 0, 0};
     }
-#pragma unroll 2
-    for (int q = 0; q < kRowsD / kWaves; ++q) {
-      const int n = tile * kRowsD + wave + kWaves * q;
-      const uint8_t* row = dc + size_t(n) * (I / 2);
-      u32x4 w[CPL];
-      uint32_t sb[CPL];
+  };
+  for (int t0 = 0; t0 < L.T; t0 += L.mtp_d) {
+    const int mt = min(L.mtp_d, L.T - t0);
+    u32x4 cw[4], nw[4];
+    if (live) load(cw, 0);
+    __syncthreads();
+    stage_rows(hs_hi, hstride, mt, I,
+               [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
+    stage_rows(hs_lo, hstride, mt, I,
+               [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
+    __syncthreads();
+    if (!live) continue;
+    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
+    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < nq; ++q) {
+      if (q + 1 < nq) load(nw, q + 1);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = lane + kWave * i;
-        if (c < nch) {
-          w[i] = ld_nt(row + c * 16);
-          sb[i] = ds[size_t(n) * nch + c];
-        } else {
-          w[i] = u32x4{0, 0, 0, 0};
-          sb[i] = 127;
-        }
-      }
-      float acc[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const float sc = e8m0_to_f32(sb[i]);
-        float blk[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) blk[t] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t cw = w[i][d];
-          const f32x2_t v0 = fp4x2_to_f32x2<0>(cw);
-          const f32x2_t v1 = fp4x2_to_f32x2<1>(cw);
-          const f32x2_t v2 = fp4x2_to_f32x2<2>(cw);
-          const f32x2_t v3 = fp4x2_to_f32x2<3>(cw);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const float* hv = &hr[t][i][8 * d];
-            float b = blk[t];
-            b = fmaf(v0[0], hv[0], b);
-            b = fmaf(v0[1], hv[1], b);
-            b = fmaf(v1[0], hv[2], b);
-            b = fmaf(v1[1], hv[3], b);
-            b = fmaf(v2[0], hv[4], b);
-            b = fmaf(v2[1], hv[5], b);
-            b = fmaf(v3[0], hv[6], b);
-            b = fmaf(v3[1], hv[7], b);
-            blk[t] = b;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = fmaf(blk[t], sc, acc[t]);
+      for (int j = 0; j < 4; ++j) {
+        const int u = 4 * q + j;
+        const u32x4 vh = u < nu ? lds16(bh + u * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+        const u32x4 vl = u < nu ? lds16(bl + u * 32 + 8 * g) : u32x4{0, 0, 0, 0};
+        acc = mfma(cw[j], vh, acc);
+        acc = mfma(cw[j], vl, acc);
       }
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float y = wave_sum(acc[t]);
-        if (lane == 0 && pr[t] >= 0) L.part[size_t(pr[t]) * H + n] = y;
-      }
+      for (int j = 0; j < 4; ++j) cw[j] = nw[j];
+    }
+    if (c < mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_coherent(&L.ysh[(size_t(sx) * L.T + t0 + c) * H + rg * 16 + 4 * g + i], acc[i]);
     }
   }
 }
 
-// Shared down (bf16): workgroup = tile of kRowsDS output rows, all shared
-// experts and all tokens; ysh[t][n] = sum_s sum_k Wd_s[n][k] hs[s][t][k].
-template <int CPLS, int MT>
-__device__ void shared_down(const GemvLayer& L, int tile) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int H = L.H, I = L.I;
-  const int nch = I / 8;
-  constexpr int NQ = kRowsDS / kWaves;
-  for (int t0 = 0; t0 < L.T; t0 += MT) {
-    float acc[NQ][MT];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) acc[q][t] = 0.0f;
-    for (int s = 0; s < L.S; ++s) {
-      float hr[MT][CPLS][8];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const bool valid = t0 + t < L.T;
-        const float* hrow = L.hs + (size_t(s) * L.T + (valid ? t0 + t : 0)) * I;
-#pragma unroll
-        for (int i = 0; i < CPLS; ++i) {
-          const int c = lane + kWave * i;
-#pragma unroll
-          for (int v = 0; v < 2; ++v) {
-            const u32x4 q = (valid && c < nch) ? ld16(hrow + c * 8 + v * 4) : u32x4{0, 0, 0, 0};
-            hr[t][i][4 * v + 0] = __uint_as_float(q[0]);
-            hr[t][i][4 * v + 1] = __uint_as_float(q[1]);
-            hr[t][i][4 * v + 2] = __uint_as_float(q[2]);
-            hr[t][i][4 * v + 3] = __uint_as_float(q[3]);
-          }
-        }
-      }
-      const uint16_t* D = L.sdown + size_t(s) * H * I;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int n = tile * kRowsDS + wave + kWaves * q;
-        u32x4 w[CPLS];
-#pragma unroll
-        for (int i = 0; i < CPLS; ++i) {
-          const int c = lane + kWave * i;
-          w[i] = c < nch ? ld_nt(D + size_t(n) * I + c * 8) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < CPLS; ++i)
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            float b = acc[q][t];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              b = fmaf(bf16_lo(w[i][d]), hr[t][i][2 * d], b);
-              b = fmaf(bf16_hi(w[i][d]), hr[t][i][2 * d + 1], b);
-            }
-            acc[q][t] = b;
-          }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int n = tile * kRowsDS + wave + kWaves * q;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const float y = wave_sum(acc[q][t]);
-        if (lane == 0 && t0 + t < L.T) L.ysh[size_t(t0 + t) * H + n] = y;
-      }
-    }
-  }
-}
-
-// Grid: [shared tiles (H / kRowsDS, when S > 0)] then [max_active * H / kRowsD].
-template <int CPL, int MT>
-__global__ __launch_bounds__(kThreads) void down_kernel(GemvLayer L) {
-  const int shared_wgs = L.S > 0 ? L.H / kRowsDS : 0;
-  const int b = blockIdx.x;
-  if (b < shared_wgs) {
-    shared_down<4 * CPL, MT>(L, b);
-  } else {
-    const int tiles = L.H / kRowsD;
-    const int r = b - shared_wgs;
-    routed_down<CPL, MT>(L, r / tiles, r % tiles);
-  }
-}
-
-// ------------------------------------------------------------------------
-// y[t][n] = bf16( sum_j w[t][j] part[t*k+j][n] + ysh[t][n] + residual[t][n] ),
-// eight outputs per thread, summed in that order.
-__global__ __launch_bounds__(256) void combine_kernel(GemvLayer L, const float* __restrict__ w,
-                                                      const uint16_t* __restrict__ residual,
-                                                      uint16_t* __restrict__ y) {
+// The last contributor of a tile sums its partials into the bf16 output.
+// All of a token's partial loads are issued before the first add, so the
+// tail costs one memory round trip, not k of them.
+__device__ void combine_tile(const GemvLayer& L, int tile) {
   const int H = L.H;
-  const int nch = H / 8;
-  const size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= size_t(L.T) * nch) return;
-  const int t = int(idx / nch);
-  const int c = int(idx % nch);
-  float acc[8];
+  const int n_out = L.T * kRowsD;
+  for (int idx = threadIdx.x; idx < n_out; idx += kThreads) {
+    const int t = idx / kRowsD;
+    const int n = tile * kRowsD + idx % kRowsD;
+    if (n >= H) continue;
+    float pv[32], wv[32], sv[4];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) acc[v] = 0.0f;
-  for (int j = 0; j < L.k; ++j) {
-    const size_t p = size_t(t) * L.k + j;
-    const float wj = w[p];
-    const float* src = L.part + p * H + c * 8;
-    const u32x4 a = ld16(src);
-    const u32x4 b = ld16(src + 4);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      acc[v] = fmaf(wj, __uint_as_float(a[v]), acc[v]);
-      acc[4 + v] = fmaf(wj, __uint_as_float(b[v]), acc[4 + v]);
+    for (int j = 0; j < 32; ++j) {
+      const size_t p = size_t(t) * L.k + j;
+      pv[j] = j < L.k ? load_coherent(&L.part[p * H + n]) : 0.0f;
+      wv[j] = j < L.k ? L.w[p] : 0.0f;
     }
-  }
-  if (L.S > 0) {
-    const float* src = L.ysh + size_t(t) * H + c * 8;
-    const u32x4 a = ld16(src);
-    const u32x4 b = ld16(src + 4);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      acc[v] += __uint_as_float(a[v]);
-      acc[4 + v] += __uint_as_float(b[v]);
-    }
-  }
-  if (residual != nullptr) {
-    const u32x4 r = ld16(residual + size_t(t) * H + c * 8);
+    for (int s = 0; s < 4; ++s)
+      sv[s] = s < L.S ? load_coherent(&L.ysh[(size_t(s) * L.T + t) * H + n]) : 0.0f;
+    const float r = L.residual != nullptr ? bf16_to_f32(L.residual[size_t(t) * H + n]) : 0.0f;
+    float acc = 0.0f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      acc[2 * v] += bf16_lo(r[v]);
-      acc[2 * v + 1] += bf16_hi(r[v]);
-    }
-  }
-  u32x4 o;
+    for (int j = 0; j < 32; ++j)
+      if (j < L.k) acc = fmaf(wv[j], pv[j], acc);
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    o[v] = uint32_t(f32_to_bf16(acc[2 * v])) | (uint32_t(f32_to_bf16(acc[2 * v + 1])) << 16);
-  *reinterpret_cast<u32x4*>(y + size_t(t) * H + c * 8) = o;
+    for (int s = 0; s < 4; ++s)
+      if (s < L.S) acc += sv[s];
+    if (L.residual != nullptr) acc += r;
+    L.y[size_t(t) * H + n] = f32_to_bf16(acc);
+  }
 }
 
-int cpl_for(int chunks) { return chunks <= 64 ? 1 : (chunks <= 128 ? 2 : 4); }
+// Grid: [S * tiles shared] then [max_active * tiles routed]; tiles =
+// ceil(H / kRowsD), the last one ragged.
+__global__ __launch_bounds__(kThreads) void down_kernel(GemvLayer L) {
+  extern __shared__ u32x4 lds_raw[];
+  uint16_t* hsm = reinterpret_cast<uint16_t*>(lds_raw);
+  __shared__ int last;
+  const int tiles = (L.H + kRowsD - 1) / kRowsD;
+  const int shared_wgs = L.S * tiles;
+  const int b = blockIdx.x;
+  const int n_active = L.plan.n_active[0];
+  int tile;
+  if (b < shared_wgs) {
+    tile = b % tiles;
+    shared_down(L, b / tiles, tile, hsm);
+  } else {
+    const int a = (b - shared_wgs) / tiles;
+    tile = (b - shared_wgs) % tiles;
+    if (a >= n_active) return;  // not a contributor
+    routed_down(L, a, tile, hsm);
+  }
+  // Partials were written through to the device-coherent level; wait for
+  // every store of the workgroup to complete before counting this
+  // contribution, so a workgroup that sees the final count also sees them.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev =
+        __hip_atomic_fetch_add(&L.tile_cnt[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == n_active + L.S - 1;
+  }
+  __syncthreads();
+  if (last) combine_tile(L, tile);
+}
 
 }  // namespace
 
-using GemvKernel = void (*)(GemvLayer);
-
-template <template <int, int> class Pick>
-GemvKernel pick(int cpl, int mt) {
-  if (cpl == 1) return mt == 1 ? Pick<1, 1>::fn : Pick<1, 2>::fn;
-  if (cpl == 2) return mt == 1 ? Pick<2, 1>::fn : Pick<2, 2>::fn;
-  return mt == 1 ? Pick<4, 1>::fn : Pick<4, 2>::fn;
+int tokens_per_pass(int T, int row_bytes) {
+  const int t = kLdsBudget / row_bytes;
+  return max(1, min(min(t, kCols), T));
 }
 
-template <int CPL, int MT>
-struct PickGateUp {
-  static constexpr GemvKernel fn = gateup_kernel<CPL, MT>;
-};
-
-template <int CPL, int MT>
-struct PickDown {
-  static constexpr GemvKernel fn = down_kernel<CPL, MT>;
-};
-
-hipError_t launch_gateup(const GemvLayer& L, hipStream_t stream) {
-  const int cpl = cpl_for(L.H / 32);
-  const int mt = L.T > 1 ? 2 : 1;
-  const int wgs = L.S * (L.I / kRowsGUS) + L.max_active * (L.I / kRowsGU);
-  hipLaunchKernelGGL(pick<PickGateUp>(cpl, mt), dim3(wgs), dim3(kThreads), 0, stream, L);
+hipError_t launch_gateup(GemvLayer L, hipStream_t stream) {
+  L.mtp_gu = tokens_per_pass(L.T, (L.H + 8) * 2);
+  const size_t lds = size_t(L.mtp_gu) * (L.H + 8) * 2;
+  const int wgs = (L.S + L.max_active) * (L.I / 32);
+  hipLaunchKernelGGL(gateup_kernel, dim3(wgs), dim3(kThreads), lds, stream, L);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const GemvLayer& L, hipStream_t stream) {
-  const int cpl = cpl_for(L.I / 32);
-  const int mt = L.T > 1 ? 2 : 1;
-  const int wgs = (L.S > 0 ? L.H / kRowsDS : 0) + L.max_active * (L.H / kRowsD);
-  hipLaunchKernelGGL(pick<PickDown>(cpl, mt), dim3(wgs), dim3(kThreads), 0, stream, L);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const GemvLayer& L, const float* w,
-                          const uint16_t* residual, uint16_t* y, hipStream_t stream) {
-  const size_t n = size_t(L.T) * (L.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, L, w,
-                     residual, y);
+hipError_t launch_down(GemvLayer L, hipStream_t stream) {
+  L.mtp_d = tokens_per_pass(L.T, (L.I + 8) * 4);
+  const size_t lds = size_t(L.mtp_d) * (L.I + 8) * 4;
+  const int wgs = (L.S + L.max_active) * ((L.H + kRowsD - 1) / kRowsD);
+  hipLaunchKernelGGL(down_kernel, dim3(wgs), dim3(kThreads), lds, stream, L);
   return hipGetLastError();
 }
 

@@ -54,33 +54,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------- dequant export -----
-// One thread per code byte of the chosen matrix.  Gate and up decode through
-// the bf16-pair conversion their GEMV uses, down through the fp32-pair
-// conversion its GEMV uses; the element times its block's E8M0 scale is an
-// exact fp32 product.
-__global__ __launch_bounds__(256) void dequant_export_kernel(const uint8_t* __restrict__ codes,
-                                                             const uint8_t* __restrict__ scales,
-                                                             int rows, int cols, int via_bf16,
+// One thread per (packed tile, lane): the lane's 16 code bytes are decoded by
+// the same scaled convert the expert kernels use (fp4x8_scaled), widened to
+// fp32 and written at their canonical place out[row][k].
+__global__ __launch_bounds__(256) void dequant_export_kernel(const uint8_t* __restrict__ mat,
+                                                             int rows, int cols,
                                                              float* __restrict__ out) {
+  const PackedMx pm(rows, cols);
+  const size_t n = size_t(rows / 16) * pm.nkb * 64;
   const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const size_t nbytes = size_t(rows) * cols / 2;
-  if (i >= nbytes) return;
-  const size_t r = i / (cols / 2);
-  const size_t k = (i % (cols / 2)) * 2;
-  const uint32_t w = codes[i];
-  const float sc = e8m0_to_f32(scales[r * (cols / 32) + k / 32]);
-  float a, b;
-  if (via_bf16) {
-    const uint32_t p = fp4x2_to_bf16x2<0>(w);
-    a = bf16_lo(p);
-    b = bf16_hi(p);
-  } else {
-    const f32x2_t p = fp4x2_to_f32x2<0>(w);
-    a = p[0];
-    b = p[1];
+  if (i >= n) return;
+  const int l = int(i % 64);
+  const size_t tile = i / 64;
+  const int kb = int(tile % pm.nkb);
+  const int rg = int(tile / pm.nkb);
+  const int bi = 4 * kb + l / 16;
+  if (bi >= pm.nb) return;
+  const int row = rg * 16 + l % 16;
+  const u32x4 codes = *reinterpret_cast<const u32x4*>(mat + tile * 1024 + 16 * l);
+  const float sc = e8m0_to_f32(mat[pm.code_bytes + (size_t(rg) * 64 + l) * pm.nkb4 + kb]);
+  float* o = out + size_t(row) * cols + size_t(bi) * 32;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const u32x4 v = fp4x8_scaled(codes[d], sc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[8 * d + 2 * q] = bf16_lo(v[q]);
+      o[8 * d + 2 * q + 1] = bf16_hi(v[q]);
+    }
   }
-  out[r * cols + k] = a * sc;
-  out[r * cols + k + 1] = b * sc;
 }
 
 // -------------------------------------------------------------- MXFP8 -----
@@ -162,14 +164,12 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, i
 
 hipError_t launch_dequant_export(const uint8_t* record, int H, int I, int matrix, float* out,
                                  hipStream_t stream) {
-  const size_t gu = size_t(I) * H / 2 + size_t(I) * H / 32;
-  const uint8_t* codes = record + size_t(matrix) * gu;
+  const uint8_t* mat = record + size_t(matrix) * packed_mxfp4_bytes(I, H);
   const int rows = matrix == 2 ? H : I;
   const int cols = matrix == 2 ? I : H;
-  const uint8_t* scales = codes + size_t(rows) * cols / 2;
-  const size_t nbytes = size_t(rows) * cols / 2;
-  hipLaunchKernelGGL(dequant_export_kernel, dim3(unsigned((nbytes + 255) / 256)), dim3(256), 0,
-                     stream, codes, scales, rows, cols, matrix == 2 ? 0 : 1, out);
+  const size_t n = size_t(rows / 16) * PackedMx(rows, cols).nkb * 64;
+  hipLaunchKernelGGL(dequant_export_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
+                     mat, rows, cols, out);
   return hipGetLastError();
 }
 

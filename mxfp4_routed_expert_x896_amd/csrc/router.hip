@@ -7,6 +7,7 @@
 // over their sum) is the reading stated in include/moe_mxfp4.h.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "plan.hpp"
 
 namespace moe {
 
@@ -77,22 +78,13 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(uint32_t(v), m, kWave);
-  const uint32_t hi = __shfl_xor(uint32_t(v >> 32), m, kWave);
-  return (uint64_t(hi) << 32) | lo;
-}
-
-// One wave per token: k rounds of a wave-wide arg-max over the E logits
-// (E <= 1024, 16 per lane), then s = sigmoid(l) and w = s / sum(s).
-__global__ __launch_bounds__(4 * kWave) void router_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ wout) {
-  const int wave = threadIdx.x / kWave;
+// Top-k of one token's logits by one wave (all 64 lanes active): k rounds
+// of a wave-wide arg-max over the E <= 1024 logits (16 per lane), then
+// s = sigmoid(l) and w = s / sum(s).  Selecting on the fp32 logit is the
+// same order as on the sigmoid score, without its saturation ties.
+__device__ __forceinline__ void select_token(const float* __restrict__ lrow, int E, int k,
+                                             int32_t* __restrict__ ids, float* __restrict__ wout) {
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float* lrow = logits + size_t(t) * E;
   uint64_t key[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -105,11 +97,7 @@ __global__ __launch_bounds__(4 * kWave) void router_topk_kernel(
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    best = wave_max_u64(best);
     const int e = int(0xFFFFFFFFu - uint32_t(best));
     if (lane == j) {
       my_id = e;
@@ -124,9 +112,30 @@ __global__ __launch_bounds__(4 * kWave) void router_topk_kernel(
   const float s = lane < k ? 1.0f / (1.0f + expf(-my_logit)) : 0.0f;
   const float tot = wave_sum(s);
   if (lane < k) {
-    ids[size_t(t) * k + lane] = my_id;
-    wout[size_t(t) * k + lane] = s / tot;
+    ids[lane] = my_id;
+    wout[lane] = s / tot;
   }
+}
+
+// One wave per token, four tokens per workgroup (any T).
+__global__ __launch_bounds__(4 * kWave) void router_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wout) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  select_token(logits + size_t(t) * E, E, k, ids + size_t(t) * k, wout + size_t(t) * k);
+}
+
+// Decode batches: one workgroup selects every token's experts (16 waves,
+// tokens round-robin) and then builds the token -> expert plan, saving a
+// launch between the router and the expert kernels.
+__global__ __launch_bounds__(kPlanThreads) void router_select_plan_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wout, Plan plan, int* zero, int n_zero) {
+  for (int t = threadIdx.x / kWave; t < T; t += kPlanThreads / kWave)
+    select_token(logits + size_t(t) * E, E, k, ids + size_t(t) * k, wout + size_t(t) * k);
+  __syncthreads();
+  build_plan(ids, T * k, E, plan, zero, n_zero);
 }
 
 }  // namespace
@@ -144,6 +153,14 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const flo
     hipLaunchKernelGGL(router_logits_kernel<8>, grid, block, lds, stream, x, wr, bias, logits, T, H, E);
   else
     hipLaunchKernelGGL(router_logits_kernel<16>, grid, block, lds, stream, x, wr, bias, logits, T, H, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_select_plan(const float* logits, int T, int E, int k, int32_t* ids,
+                                     float* w, Plan plan, int* zero, int n_zero,
+                                     hipStream_t stream) {
+  hipLaunchKernelGGL(router_select_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, logits, T,
+                     E, k, ids, w, plan, zero, n_zero);
   return hipGetLastError();
 }
 

@@ -24,21 +24,31 @@ def rel_l2_per_token(y_bits, y_ref):
 
 
 class Built:
-    """One synthetic layer on the device plus its oracle description."""
+    """One synthetic layer on the device plus its oracle description.
+
+    dev holds the canonical device tensors (mutable by tests); lib is the
+    library's layer over their packed copies -- call repack() after changing
+    dev["experts"] or the shared matrices.
+    """
 
     def __init__(self, cfg, seed=0, layer=0, bias=False):
-        from mxfp4_routed_expert_x896_amd import binding
         self.cfg = cfg
         self.seed, self.layer_idx = seed, layer
         d = SD.upload_layer(cfg, seed, layer, bias=bias)
         self.dev = d
-        self.lib = binding.Layer(cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["top_k"],
-                                 d["router_w"], d["experts"], d["shared_gate"], d["shared_up"],
-                                 d["shared_down"], d["router_bias"])
+        self.repack()
         H, I = cfg["hidden"], cfg["inter"]
         self.oracle = M.Layer(H, I, cfg["n_experts"], cfg["top_k"], d["host_router_w"],
                               expert_record=lambda e: synth.expert_record(seed, layer, e, H, I),
                               shared=d["host_shared"], router_bias=d["host_bias"])
+
+    def repack(self):
+        from mxfp4_routed_expert_x896_amd import binding
+        c, d = self.cfg, self.dev
+        self.lib = binding.Layer.from_canonical(
+            c["hidden"], c["inter"], c["n_experts"], c["top_k"], d["router_w"], d["experts"],
+            d["shared_gate"], d["shared_up"], d["shared_down"], d["router_bias"])
+        torch.cuda.synchronize()
 
 
 def check_routing(gpu_ids, gpu_w, scores, k, eps=TIE_EPS):

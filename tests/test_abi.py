@@ -43,12 +43,38 @@ def test_abi_version_and_record_bytes(lib):
     assert lib.lib().moe_record_bytes(256, 64, None) == -1
 
 
+PACKED_TINY = 38_912  # packed record of H=256, I=64 (K=64 padded to 128 columns, scales to 4 tiles)
+
+
 def _desc(lib, **kw):
     d = dict(hidden=256, inter=64, n_experts=32, top_k=4, n_shared=1, reserved0=0,
-             router_w=0x10000, router_bias=None, experts=0x20000, expert_stride=26_112,
+             router_w=0x10000, router_bias=None, experts=0x20000, expert_stride=PACKED_TINY,
              shared_gate=0x30000, shared_up=0x40000, shared_down=0x50000)
     d.update(kw)
     return lib.LayerDesc(**d)
+
+
+def test_packed_record_bytes(lib):
+    assert lib.packed_record_bytes(7168, 1536) == 17_547_264  # same bytes as canonical
+    assert lib.packed_record_bytes(256, 64) == PACKED_TINY
+    out = ctypes.c_uint64()
+    assert lib.lib().moe_packed_record_bytes(96, 64, ctypes.byref(out)) == 0
+    assert lib.lib().moe_packed_record_bytes(100, 64, ctypes.byref(out)) == -3
+
+
+def test_pack_calls_reject_bad_arguments(lib):
+    L = lib.lib()
+    P = ctypes.c_void_p
+    a, b = P(0x100000), P(0x900000)
+    assert L.moe_pack_experts(None, 26_112, b, PACKED_TINY, 4, 256, 64, None) == -1
+    assert L.moe_pack_experts(a, 26_112, b, PACKED_TINY, 0, 256, 64, None) == -1
+    assert L.moe_pack_experts(a, 26_112, b, PACKED_TINY, 4, 250, 64, None) == -3
+    assert L.moe_pack_experts(a, 26_000, b, PACKED_TINY, 4, 256, 64, None) == -3
+    assert L.moe_pack_experts(a, 26_112, b, PACKED_TINY - 16, 4, 256, 64, None) == -3
+    assert L.moe_pack_experts(a, 26_112, P(0x900008), PACKED_TINY, 4, 256, 64, None) == -2
+    assert L.moe_pack_bf16(a, b, 2, 20, 64, None) == -3
+    assert L.moe_pack_bf16(a, b, 2, 16, 48, None) == -3
+    assert L.moe_pack_bf16(a, None, 2, 16, 64, None) == -1
 
 
 def _ws(lib, desc, t):
@@ -71,8 +97,8 @@ def _ws(lib, desc, t):
     (dict(shared_down=None), -1),
     (dict(n_shared=0, shared_gate=None, shared_up=None, shared_down=None), 0),
     (dict(router_w=0x10008), -2),
-    (dict(expert_stride=26_120), -2),
-    (dict(expert_stride=26_096), -3),
+    (dict(expert_stride=PACKED_TINY + 8), -2),
+    (dict(expert_stride=PACKED_TINY - 16), -3),
     (dict(reserved0=1), -1),
 ])
 def test_descriptor_validation(lib, kw, status):

@@ -98,7 +98,7 @@ def test_dequant_export_extreme_scales_and_every_code(b):
             scales[...] = pattern[np.arange(scales.size) % len(pattern)].reshape(scales.shape)
     experts = torch.from_numpy(recs).cuda()
     wr = torch.zeros((2, H), dtype=torch.int16, device="cuda")
-    layer = b.Layer(H, I, 2, 1, wr, experts)
+    layer = b.Layer.from_canonical(H, I, 2, 1, wr, experts)
     for j in range(2):
         for m in range(3):
             shape = (H, I) if m == 2 else (I, H)
@@ -176,6 +176,7 @@ def test_one_more_scale_exponent_doubles_output_bitwise(b):
     for e in range(8):
         R.split(ex[e], 256, 64)[3][...] += 1
     built.dev["experts"].copy_(torch.from_numpy(ex))
+    built.repack()
     _, _, y2 = _run_layer(b, built, xd)
     np.testing.assert_array_equal(F.bf16_decode(y2), 2.0 * F.bf16_decode(y1))
 
@@ -184,6 +185,7 @@ def test_zero_routed_experts_leave_shared_only(b):
     cfg = dict(hidden=256, inter=64, n_experts=8, top_k=3, n_shared=2)
     built = Built(cfg, seed=5)
     built.dev["experts"].zero_()
+    built.repack()
     xh, xd = SD.upload_tokens(1400, 4, 256)
     _, _, y = _run_layer(b, built, xd)
     ref = M.shared_sum(xh, built.oracle)
@@ -194,9 +196,11 @@ def test_all_experts_equal_is_routing_independent(b):
     cfg = dict(hidden=256, inter=64, n_experts=16, top_k=4, n_shared=1)
     built = Built(cfg, seed=6)
     built.dev["experts"][:] = built.dev["experts"][7]
+    built.repack()
     xh, xd = SD.upload_tokens(1500, 6, 256)
     ids1, _, y1 = _run_layer(b, built, xd)
     built.dev["router_w"].copy_(torch.flip(built.dev["router_w"], dims=[0]))
+    built.repack()
     ids2, _, y2 = _run_layer(b, built, xd)
     assert not np.array_equal(ids1, ids2)
     rec = synth.expert_record(6, 0, 7, 256, 64)
@@ -245,3 +249,28 @@ def test_mxfp8_quantize_bit_exact(b):
     rc, rs = F.mxfp8_quantize(F.bf16_decode(xh))
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_consecutive_calls_with_changing_inputs(b):
+    """Back-to-back calls on one workspace, each with new tokens and its own
+    check: partials of an earlier call must never leak into a later one."""
+    cfg = dict(hidden=512, inter=128, n_experts=64, top_k=6, n_shared=2)
+    built = Built(cfg, seed=8)
+    T = 3
+    ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+    ws = built.lib.workspace(T)
+    outs, xs = [], []
+    for i in range(12):
+        xh, xd = SD.upload_tokens(1800 + i, T, 512)
+        y = torch.empty((T, 512), dtype=torch.int16, device="cuda")
+        b.moe_layer(built.lib, xd, y, ids, w, ws, path=b.PATH_GEMV)
+        outs.append((y, ids.clone(), w.clone()))
+        xs.append(xh)
+    torch.cuda.synchronize()
+    for xh, (y, i_, w_) in zip(xs, outs):
+        _, _, s = M.route(xh, built.oracle)
+        ids_np = i_.cpu().numpy()
+        check_routing(ids_np, w_.cpu().numpy(), s, 6)
+        ref = M.moe_forward(xh, built.oracle, ids_np, oracle_weights(s, ids_np))
+        assert rel_l2_per_token(to_np_u16(y), ref).max() <= REL_TOL
