@@ -34,8 +34,7 @@ MAT_BYTES = 7168 * 1536 // 2 + 7168 * 1536 // 32   # one MXFP4 matrix: 5,849,088
 REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
 SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 # kernels of one moe_layer call, in launch order (see moe_profile_events)
-KERNELS_DECODE = ["router_logits", "select_plan", "gateup", "down"]
-KERNELS_LARGE = ["router_logits", "router_topk", "plan", "gateup", "down"]
+KERNELS = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
 
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
@@ -73,20 +72,20 @@ def source_hash():
 
 def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
     """Algorithmic HBM bytes of one launch: weights read once, activations in
-    and out; intermediates passed between kernels counted once."""
+    and out; intermediates passed between launches counted once where they
+    are written and once where they are read (h and the shared h as bf16
+    hi + lo, 4 bytes per element; shared outputs fp32).  The routed
+    partials that stay inside the down launch are not counted."""
     x = T * H * 2
-    if name == "router_logits":
-        return E * H * 2 + x + T * E * 4
-    if name == "router_topk":
-        return T * E * 4 + T * k * 8
-    if name == "plan":
-        return T * k * 4 * 2 + E * 8
-    if name == "select_plan":
-        return T * E * 4 + T * k * 8 + T * k * 4 * 2 + E * 8
-    if name == "gateup":
-        return D * 2 * MAT_BYTES + S * 2 * SHARED_MAT_BYTES + x + (T * k + S * T) * I * 4
-    if name == "down":  # includes the combine: bf16 output written once
-        return D * MAT_BYTES + S * SHARED_MAT_BYTES + (T * k + S * T) * I * 4 + T * k * 4 + x
+    if name == "router_shared_gateup":
+        return E * H * 2 + x + T * E * 4 + S * 2 * SHARED_MAT_BYTES + S * T * I * 4
+    if name == "select_shared_down":
+        return (T * E * 4 + T * k * 8 + T * k * 4 + E * 8
+                + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
+    if name == "routed_gateup":
+        return D * 2 * MAT_BYTES + x + T * k * I * 4
+    if name == "routed_down_combine":
+        return D * MAT_BYTES + T * k * I * 4 + T * k * 4 + S * T * H * 4 + x
     raise KeyError(name)
 
 
@@ -218,7 +217,6 @@ def main():
     import ctypes
     arr = (ctypes.c_void_p * n_ev)(*[e.cuda_event for e in evs])
     b.profile_events(arr, n_ev)
-    KERNELS = KERNELS_DECODE if T <= 64 else KERNELS_LARGE
     per_kernel = {name: [] for name in KERNELS}
     span = []
     prof_steps = min(args.steps, 100)

@@ -34,15 +34,21 @@
  *   moe_record_bytes() gives the size (17,547,264 at H=7168, I=1536).
  *
  * Packed layout (what the layer kernels read; moe_pack_experts writes it).
- * Each MXFP4 matrix of R rows x K columns becomes tiles of 16 rows x 128
- * columns, 1088 bytes each, ordered (row group, column group): bytes
- * 16 l .. 16 l + 15 hold the codes of block 4 kb + l / 16 of row
- * 16 rg + l % 16 and byte 1024 + l its scale (blocks past K/32 are zero
- * codes, scale 127).  A wave64 reads one tile as 1 KiB of contiguous codes
- * in which lane l holds exactly its MFMA operand.  Same bytes as the
- * canonical record when K is a multiple of 128 (17,547,264 at K3 shape).
- * bf16 shared matrices are packed the same way into 1 KiB tiles of 16 rows
- * x 32 columns (lane l: row 16 rg + l % 16, columns 8 (l / 16) .. +7).
+ * Each MXFP4 matrix of R rows x K columns (nb = K/32 blocks per row, nkb =
+ * ceil(nb/4) code tiles per row group, nkb4 = nkb rounded up to 4) is
+ *   codes:  tiles of 16 rows x 128 columns, 1 KiB each, tile (rg, kb) at
+ *           byte (rg nkb + kb) 1024; its bytes 16 l .. 16 l + 15 hold the
+ *           codes of block 4 kb + l/16 of row 16 rg + l%16 (zero codes past
+ *           block nb);
+ *   scales: after the codes; byte (rg 64 + l) nkb4 + kb is that block's
+ *           E8M0 exponent (127 past block nb).
+ * A wave64 reads one tile as 1 KiB of contiguous codes in which lane l holds
+ * exactly its MFMA operand, and a lane's exponents for four consecutive
+ * tiles as one dword.  A record is gate, up, down matrices back to back;
+ * same size as the canonical record when K is a multiple of 512
+ * (17,547,264 bytes at K3 shape).  bf16 shared matrices are packed into
+ * 1 KiB tiles of 16 rows x 32 columns (lane l: row 16 rg + l%16, columns
+ * 8 (l/16) .. +7), tile (rg, u) at element (rg K/32 + u) 512.
  *
  * Conventions for every call:
  *   - pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t
@@ -200,10 +206,10 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
  * its stream before its first kernel and events[i] right after its i-th
  * kernel (i < n_events); moe_profile_count() returns how many the last such
  * call recorded.  Kernel order: moe_route: router logits, top-k;
- * moe_forward (GEMV path): plan, gate/up, down (with the combine);
- * moe_layer (GEMV path, n_tokens <= 64): router logits, top-k with plan,
- * gate/up, down; above 64 tokens: router logits, top-k, plan, gate/up,
- * down.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
+ * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
+ * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
+ * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
+ * + combine.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
  * to stop.  Timing
  * records only add event markers; no kernel is skipped or changed.
  */

@@ -93,9 +93,12 @@ constexpr int64_t kMaxTokens = 1 << 16;
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
+int n_tiles(const moe_layer_desc* L) { return (L->hidden + moe::kDownRows - 1) / moe::kDownRows; }
+int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
+
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, total;
+  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt, total;
 };
 
 Carve carve(const moe_layer_desc* L, int64_t T) {
@@ -117,7 +120,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
   c.hs = take(S * t * I * 4);
   c.part = take(t * k * H * 4);
   c.ysh = take(S * t * H * 4);
-  c.tile_cnt = take(((H + 63) / 64) * 4);
+  c.tile_cnt = take(n_tiles(L) * 4);
+  c.sel_cnt = take(4);
   c.total = off;
   return c;
 }
@@ -140,20 +144,9 @@ int check_ws(const moe_layer_desc* L, int64_t T, void* ws, uint64_t ws_bytes) {
   return MOE_OK;
 }
 
-int do_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, int32_t* ids, float* w,
-             void* ws, hipStream_t stream) {
+moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T, void* ws) {
   const Carve c = carve(L, T);
-  float* logits = at<float>(ws, c.logits);
-  int st = launched(moe::launch_router_logits(x, L->router_w, L->router_bias, logits, int(T),
-                                              L->hidden, L->n_experts, stream), stream);
-  if (st) return st;
-  return launched(moe::launch_router_topk(logits, int(T), L->n_experts, L->top_k, ids, w, stream), stream);
-}
-
-moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
-                          const float* w, const uint16_t* residual, uint16_t* y, void* ws) {
-  const Carve c = carve(L, T);
-  moe::GemvLayer G;
+  moe::GemvLayer G = {};
   G.T = int(T);
   G.H = L->hidden;
   G.I = L->inter;
@@ -161,6 +154,10 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.k = L->top_k;
   G.S = L->n_shared;
   G.x = x;
+  G.wr = L->router_w;
+  G.rbias = L->router_bias;
+  G.logits = at<float>(ws, c.logits);
+  G.sel_cnt = at<int>(ws, c.sel_cnt);
   G.experts = L->experts;
   G.stride = L->expert_stride;
   G.sgate = L->shared_gate;
@@ -170,57 +167,95 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.plan.active = at<int32_t>(ws, c.active);
   G.plan.act_off = at<int32_t>(ws, c.act_off);
   G.plan.pairs = at<int32_t>(ws, c.pairs);
-  const int64_t pairs = T * L->top_k;
-  G.max_active = int(pairs < L->n_experts ? pairs : L->n_experts);
-  G.h = at<uint16_t>(ws, c.h);
+  G.h = at<uint32_t>(ws, c.h);
   G.hs = at<uint16_t>(ws, c.hs);
   G.part = at<float>(ws, c.part);
   G.ysh = at<float>(ws, c.ysh);
   G.tile_cnt = at<int>(ws, c.tile_cnt);
-  G.w = w;
-  G.residual = residual;
-  G.y = y;
   return G;
 }
 
-int n_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
-
-// Expert kernels once the plan exists.
-int run_experts(const moe::GemvLayer& G, hipStream_t stream) {
-  int st = launched(moe::launch_gateup(G, stream), stream);
-  if (st) return st;
-  return launched(moe::launch_down(G, stream), stream);
+// Workgroup counts of the roles (see layer.hip).
+int n_logit_wgs(const moe_layer_desc* L) { return (L->n_experts + 3) / 4; }
+int n_select_wgs(int64_t T) { return int((T + 3) / 4); }
+int max_active(const moe_layer_desc* L, int64_t T) {
+  const int64_t pairs = T * L->top_k;
+  return int(pairs < L->n_experts ? pairs : L->n_experts);
 }
 
+int stage(moe::StageKind kind, const moe::GemvLayer& G, const moe::Stage& st,
+          hipStream_t stream) {
+  return launched(moe::launch_stage(kind, G, st, stream), stream);
+}
+
+// Router only: logits, then the top-k.
+int do_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, int32_t* ids, float* w,
+             void* ws, hipStream_t stream) {
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_out = ids;
+  G.w_out = w;
+  moe::Stage s1;
+  s1.n_logits = n_logit_wgs(L);
+  int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
+  if (st) return st;
+  moe::Stage s2;
+  s2.n_select = n_select_wgs(T);
+  return stage(moe::StageKind::SelectSharedDown, G, s2, stream);
+}
+
+// Given routing: plan + shared gate/up, shared down + routed gate/up,
+// routed down + combine.
 int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
                     const float* w, const uint16_t* residual, uint16_t* y, void* ws,
                     hipStream_t stream) {
-  const moe::GemvLayer G = gemv_layer(L, x, T, w, residual, y, ws);
-  int st = launched(moe::launch_plan(ids, int(T * L->top_k), L->n_experts, G.plan, G.tile_cnt,
-                                     n_tiles(L), stream), stream);
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_in = ids;
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
+  moe::Stage s1;
+  s1.n_plan = 1;
+  s1.n_sgu = S * (L->inter / 16);
+  int st = stage(moe::StageKind::PlanSharedGateUp, G, s1, stream);
   if (st) return st;
-  return run_experts(G, stream);
+  moe::Stage s2;
+  s2.n_sdn = S * n_shared_tiles(L);
+  s2.n_rgu = ma * tiles_gu;
+  if ((st = stage(moe::StageKind::RoutedGateUp, G, s2, stream))) return st;
+  moe::Stage s3;
+  s3.n_rdn = ma * n_tiles(L);
+  return stage(moe::StageKind::RoutedDownCombine, G, s3, stream);
 }
 
-// Router, then the experts.  Decode batches select and plan in one launch.
+// Router and experts: logits + shared gate/up, top-k + plan + shared down,
+// routed gate/up, routed down + combine.
 int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                   const uint16_t* residual, uint16_t* y, int32_t* ids, float* w, void* ws,
                   hipStream_t stream) {
-  if (T > moe::kSelectPlanMaxTokens) {
-    int st = do_route(L, x, T, ids, w, ws, stream);
-    if (st) return st;
-    return do_forward_gemv(L, x, T, ids, w, residual, y, ws, stream);
-  }
-  const Carve c = carve(L, T);
-  float* logits = at<float>(ws, c.logits);
-  int st = launched(moe::launch_router_logits(x, L->router_w, L->router_bias, logits, int(T),
-                                              L->hidden, L->n_experts, stream), stream);
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_out = ids;
+  G.w_out = w;
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
+  moe::Stage s1;
+  s1.n_logits = n_logit_wgs(L);
+  s1.n_sgu = S * (L->inter / 16);
+  int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
   if (st) return st;
-  const moe::GemvLayer G = gemv_layer(L, x, T, w, residual, y, ws);
-  st = launched(moe::launch_router_select_plan(logits, int(T), L->n_experts, L->top_k, ids, w,
-                                               G.plan, G.tile_cnt, n_tiles(L), stream), stream);
-  if (st) return st;
-  return run_experts(G, stream);
+  moe::Stage s2;
+  s2.n_select = n_select_wgs(T);
+  s2.plan_after_select = 1;
+  s2.n_sdn = S * n_shared_tiles(L);
+  if ((st = stage(moe::StageKind::SelectSharedDown, G, s2, stream))) return st;
+  moe::Stage s3;
+  s3.n_rgu = ma * tiles_gu;
+  if ((st = stage(moe::StageKind::RoutedGateUp, G, s3, stream))) return st;
+  moe::Stage s4;
+  s4.n_rdn = ma * n_tiles(L);
+  return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
 }
 
 int resolve_path(int32_t path, int64_t T) {

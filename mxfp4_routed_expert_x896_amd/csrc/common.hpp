@@ -131,13 +131,13 @@ struct PackedMx {
 };
 
 // --------------------------------------------------------------- plan -----
-// Token -> expert grouping written by the plan kernel and read by the expert
-// kernels.  Pair p = t * top_k + j is slot j of token t.
+// Token -> expert grouping written by the plan builder (plan.hpp) and read
+// by the expert kernels.  Pair p = t * top_k + j is slot j of token t.
 struct Plan {
   int32_t* n_active;  // [1] number of experts with at least one pair
   int32_t* active;    // [E] expert ids with pairs, ascending
   int32_t* act_off;   // [E + 1] start of each active expert's pairs in `pairs`
-  int32_t* pairs;     // [T * k] pair ids grouped by expert, ascending within
+  int32_t* pairs;     // [T * k] pair ids grouped by expert
 };
 
 }  // namespace moe

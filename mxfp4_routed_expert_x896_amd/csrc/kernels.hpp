@@ -8,43 +8,61 @@
 
 namespace moe {
 
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, const float* bias,
-                                float* logits, int T, int H, int E, hipStream_t stream);
-hipError_t launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                              hipStream_t stream);
-// Largest T for which one workgroup selects all tokens and builds the plan.
-constexpr int kSelectPlanMaxTokens = 64;
-hipError_t launch_router_select_plan(const float* logits, int T, int E, int k, int32_t* ids,
-                                     float* w, Plan plan, int* zero, int n_zero,
-                                     hipStream_t stream);
-// Also zeroes n_zero ints at zero (the down kernel's tile counters).
-hipError_t launch_plan(const int32_t* ids, int n_pairs, int E, Plan plan, int* zero, int n_zero,
-                       hipStream_t stream);
+// Output rows per routed down workgroup (and per combine tile).
+constexpr int kDownRows = 256;
 
-// Everything the decode-path expert kernels need.
+// Everything the layer kernels need (layer.hip).
 struct GemvLayer {
   int T, H, I, E, k, S;
   const uint16_t* x;        // bf16 [T][H]
+  const uint16_t* wr;       // bf16 [E][H] router weights
+  const float* rbias;       // fp32 [E] router bias or null
+  float* logits;            // fp32 [T][E]
+  const int32_t* ids_in;    // int32 [T][k] routing given by the caller (plan role)
+  int32_t* ids_out;         // int32 [T][k] routing written by the top-k role
+  float* w_out;             // fp32 [T][k] weights written by the top-k role
+  int* sel_cnt;             // [1] arrivals of top-k workgroups (zeroed by the logits launch)
   const uint8_t* experts;   // E packed records (MFMA-tiled, see pack.hip)
   uint64_t stride;          // bytes between records
   const uint16_t* sgate;    // bf16 [S] packed [I][H]
   const uint16_t* sup;      // bf16 [S] packed [I][H]
   const uint16_t* sdown;    // bf16 [S] packed [H][I]
   Plan plan;
-  int max_active;           // upper bound on plan.n_active (grid sizing)
-  int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launchers)
-  uint16_t* h;              // bf16 [2][T*k][I] routed SiLU(g)*u per pair, hi and lo parts
+  int n_tiles;              // ceil(H / kDownRows) routed down tiles (set by the launcher)
+  int n_stiles;             // ceil(H / 64) shared down tiles (set by the launcher)
+  int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launcher)
+  uint32_t* h;              // [T*k][I] routed SiLU(g)*u per pair: bf16 hi | bf16 lo << 16
   uint16_t* hs;             // bf16 [2][S][T][I] shared SiLU(g)*u, hi and lo parts
   float* part;              // fp32 [T*k][H]   routed expert outputs per pair
   float* ysh;               // fp32 [S][T][H]  shared expert outputs
-  int* tile_cnt;            // [ceil(H / 64)] arrivals per down tile (zeroed by the plan kernel)
+  int* tile_cnt;            // [n_tiles] routed down arrivals per output tile (zeroed by
+                            // the plan builder of the same call)
   const float* w;           // fp32 [T][k] combine weights
   const uint16_t* residual; // bf16 [T][H] or null
   uint16_t* y;              // bf16 [T][H]
 };
 
-hipError_t launch_gateup(GemvLayer L, hipStream_t stream);
-hipError_t launch_down(GemvLayer L, hipStream_t stream);
+// Workgroups of each role in one launch (0 = role absent).
+struct Stage {
+  int n_logits = 0;           // ceil(E / 4)
+  int n_select = 0;           // ceil(T / 4)
+  int plan_after_select = 0;  // the last top-k workgroup builds the plan
+  int n_plan = 0;             // 0 or 1
+  int n_sgu = 0;              // S * I / 16
+  int n_sdn = 0;              // S * ceil(H / 64)
+  int n_rgu = 0;              // max_active * I / 32
+  int n_rdn = 0;              // max_active * ceil(H / kDownRows)
+};
+
+enum class StageKind {
+  RouterSharedGateUp,  // roles: logits, shared gate/up
+  SelectSharedDown,    // roles: top-k (+ plan), shared down
+  PlanSharedGateUp,    // roles: plan, shared gate/up
+  RoutedGateUp,        // roles: shared down, routed gate/up
+  RoutedDownCombine,   // roles: routed down + combine
+};
+
+hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t stream);
 
 // Repacking (pack.hip).
 size_t packed_mxfp4_bytes(int R, int K);

@@ -1,0 +1,727 @@
+// The layer's kernels.  Every launch is one role-dispatch kernel whose
+// workgroups take different roles by block index, so that independent work
+// shares a launch: moe_layer runs
+//   1. router logits            + shared experts' gate/up
+//   2. top-k and plan           + shared experts' down
+//   3. routed gate/up
+//   4. routed down and the weighted combine
+// and moe_forward (routing given) runs plan + shared gate/up, routed gate/up
+// + shared down, routed down + combine.  The shared experts do not depend on
+// the routing, so their weights stream while the router and the top-k run.
+//
+// Expert products.  Deltafin README ("An experiment in running Kimi K3 ..."),
+// "Techniques / Compute": the MXFP4 weights are decoded inside the product
+// instead of being dequantised to a temporary first; the Deltafin explainer
+// (bhfrc.com), section 6.2, gives the reason (a separate pass costs memory
+// and another trip through memory bandwidth).  Here a weight never exists in
+// dequantised form outside registers.  Each lane loads 16 bytes of codes --
+// one whole 32-element block of one row, so one E8M0 exponent -- converts
+// them with v_cvt_scalef32_pk_bf16_fp4 (the block exponent applied in the
+// convert; exact, since an E2M1 value times a power of two is a bf16,
+// subnormals included) and feeds them as the A operand of
+// v_mfma_f32_16x16x32_bf16.  The tokens routed to the expert are the B
+// columns (up to 16 per pass), accumulation is fp32.  At batch 1 only one B
+// column is live: the matrix core takes the multiply-accumulate off the
+// vector ALU (one convert per code byte remains), which is what lets the
+// weight stream run near the HBM roof; batched decode then reuses every
+// converted weight for all tokens of the expert at no extra cost.
+//
+// Operand mapping (wave64, lane l: g = l / 16, c = l % 16): weights are read
+// in the MFMA-tiled layout written by pack.hip, so for tile kb a wave loads
+// 1 KiB of contiguous codes in which lane l holds block bi = 4 kb + g of row
+// 16 rg + c; the lane's scales of four consecutive tiles are one dword of
+// the scale region.  MFMA step s (0..3) takes elements 8 s .. 8 s + 7 of
+// that block, i.e. contraction index K = 32 bi + 8 s + j; the B lane (g, c)
+// supplies the same K indices of token c.  The 16 x 16 fp32 result leaves
+// rows 4 g + i (i = 0..3) of token c in lane (g, c).  bf16 (shared)
+// matrices use 1 KiB tiles of 16 rows x 32 columns, lane l holding columns
+// 8 g .. 8 g + 7.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "router.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRowsD = kDownRows;  // routed down rows per workgroup (4 row groups per wave)
+constexpr int kRowsSD = 64;        // shared down rows per workgroup (one row group per wave)
+constexpr int kCols = 16;         // B columns of one MFMA: at most 16 tokens per pass
+constexpr int kLdsBudget = 32768;  // bytes of staged activations per workgroup
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ u32x4 ld_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ f32x4_t mfma(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 hi + bf16 lo with hi + lo = v to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+// Partials cross workgroups (and XCDs, whose L2s are private): they are
+// stored and re-read with device-scope atomic accesses, which the compiler
+// emits as write-through stores and L2-bypassing loads, instead of fencing
+// (a device-scope fence writes back and invalidates the whole L2).
+template <typename V>
+__device__ __forceinline__ void store_coherent(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V load_coherent(const V* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts this workgroup's arrival on *cnt once all its global stores have
+// completed; true in every thread of the last of n arrivals.  With the
+// stores made through the coherent level (store_coherent), the last
+// workgroup then sees every other workgroup's results.
+__device__ __forceinline__ bool arrive_last(int* cnt, int n) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == n - 1;
+  }
+  __syncthreads();
+  return last != 0;
+}
+
+// Contraction length padded to whole 4-tile super-steps (512 columns of
+// MXFP4 tiles, four 128-column groups of bf16 tiles).  Activations are
+// staged zero-filled up to it, so the clamped tail loads (see load_gu)
+// multiply zeros.
+__host__ __device__ __forceinline__ int pad_k(int K) { return (K + 511) / 512 * 512; }
+
+// Stage the bf16 rows of mt tokens into LDS rows of `stride` elements:
+// dst[j][0..K) = src(j)[0..K), dst[j][K..Kp) = 0; sources via src(j).
+template <typename Src>
+__device__ __forceinline__ void stage_rows(uint16_t* dst, int stride, int mt, int K, int Kp,
+                                           Src src) {
+  const int nch = Kp / 8;
+  for (int i = threadIdx.x; i < mt * nch; i += kThreads) {
+    const int j = i / nch, q = i % nch;
+    *reinterpret_cast<u32x4*>(dst + j * stride + q * 8) =
+        q * 8 < K ? ld16(src(j) + q * 8) : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Stage packed h rows (uint32: bf16 hi in the low half, lo in the high
+// half) into separate hi and lo LDS rows (zero-filled from K to Kp).
+template <typename Src>
+__device__ __forceinline__ void stage_h(uint16_t* hi, uint16_t* lo, int stride, int mt, int K,
+                                        int Kp, Src src) {
+  const int nch = Kp / 4;
+  for (int i = threadIdx.x; i < mt * nch; i += kThreads) {
+    const int j = i / nch, q = i % nch;
+    const u32x4 v = q * 4 < K ? ld16(src(j) + q * 4) : u32x4{0, 0, 0, 0};
+    const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+    *reinterpret_cast<u32x2*>(hi + j * stride + q * 4) =
+        u32x2{(w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16)};
+    *reinterpret_cast<u32x2*>(lo + j * stride + q * 4) =
+        u32x2{(w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u)};
+  }
+}
+
+__device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Wave index within the workgroup as a scalar (uniform) value, so that loop
+// bounds and tile addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
+
+// Two-stage software pipeline over steps s0 .. s1 - 1 with two register
+// buffers used alternately: while step s is computed from one buffer, the
+// loads of step s + 1 are in flight into the other.  The caller has issued
+// load(a, s0).  Two things keep the loads of step s + 1 in flight while
+// step s computes: the buffers alternate instead of being copied (a copy
+// would wait for them), and the steady-state loop issues its loads without
+// conditions, so the compiler can count exactly how many are outstanding
+// (loads under a branch make it wait for all of them).
+template <typename Buf, typename Load, typename Comp>
+__device__ __forceinline__ void pipeline2(int s0, int s1, Buf& a, Buf& b, Load load, Comp comp) {
+  int s = s0;
+  for (; s + 2 < s1; s += 2) {
+    load(b, s + 1);
+    comp(a, s);
+    load(a, s + 2);
+    comp(b, s + 1);
+  }
+  if (s + 1 < s1) {
+    load(b, s + 1);
+    comp(a, s);
+    comp(b, s + 1);
+  } else if (s < s1) {
+    comp(a, s);
+  }
+}
+
+// ------------------------------------------------------------------------
+// Gate/up.  Workgroup = (expert, 32 rows): wave w takes row group w / 2 of
+// the tile and half w % 2 of the contraction; the halves meet in LDS.  The
+// tokens' x rows are staged in LDS (B operand), mtp at a time.  Weight
+// tiles are double-buffered (pipeline2): the loads of super-step kq + 1 are
+// in flight while super-step kq is converted and multiplied.
+
+struct GuTiles {
+  u32x4 g[4], u[4];
+  uint32_t sg, su;
+};
+
+// Tiles past the row group's last (kb >= nkb, only when nkb is not a
+// multiple of 4) are loaded from the last tile instead: a valid address and
+// no branch; their scale bytes are the 127 padding and the staged
+// activations there are zero, so they add nothing.
+__device__ __forceinline__ void load_gu(GuTiles& t, const uint8_t* gcodes, const uint8_t* ucodes,
+                                        const uint8_t* gscl, const uint8_t* uscl, int kq, int nkb,
+                                        int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int kb = min(4 * kq + j, nkb - 1);
+    t.g[j] = ld_nt(gcodes + size_t(kb) * 1024 + 16 * lane);
+    t.u[j] = ld_nt(ucodes + size_t(kb) * 1024 + 16 * lane);
+  }
+  t.sg = *reinterpret_cast<const uint32_t*>(gscl + 4 * kq);
+  t.su = *reinterpret_cast<const uint32_t*>(uscl + 4 * kq);
+}
+
+__device__ __forceinline__ void mma_gu(const GuTiles& t, const uint16_t* xrow, int kq, int g,
+                                       f32x4_t& ag, f32x4_t& au) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bi = 16 * kq + 4 * j + g;
+    const float sg = e8m0_to_f32((t.sg >> (8 * j)) & 0xFFu);
+    const float su = e8m0_to_f32((t.su >> (8 * j)) & 0xFFu);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 bx = lds16(xrow + bi * 32 + 8 * s);
+      ag = mfma(fp4x8_scaled(t.g[j][s], sg), bx, ag);
+      au = mfma(fp4x8_scaled(t.u[j][s], su), bx, au);
+    }
+  }
+}
+
+// Adds the tiles of waves 1..3 into wave 0 (contraction split in four).
+__device__ __forceinline__ void join_quarters(f32x4_t& a, f32x4_t& b, float* red) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  __syncthreads();
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[(wave * kWave + lane) * 8 + i] = a[i];
+      red[(wave * kWave + lane) * 8 + 4 + i] = b[i];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] += red[(w * kWave + lane) * 8 + i];
+        b[i] += red[(w * kWave + lane) * 8 + 4 + i];
+      }
+    }
+  }
+}
+
+// Adds the partner half's tiles (wave w ^ 1) into waves with even index.
+__device__ __forceinline__ void join_halves(f32x4_t& a, f32x4_t& b, float* red) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  __syncthreads();
+  if (wave & 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[(wave * kWave + lane) * 8 + i] = a[i];
+      red[(wave * kWave + lane) * 8 + 4 + i] = b[i];
+    }
+  }
+  __syncthreads();
+  if (!(wave & 1)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] += red[((wave + 1) * kWave + lane) * 8 + i];
+      b[i] += red[((wave + 1) * kWave + lane) * 8 + 4 + i];
+    }
+  }
+}
+
+__device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
+  if (a >= L.plan.n_active[0]) return;
+  const int e = L.plan.active[a];
+  const int p0 = L.plan.act_off[a];
+  const int p1 = L.plan.act_off[a + 1];
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const PackedMx pm(I, H);
+  const int nkq = pm.nkb4 / 4;
+  const int kqh = (nkq + 1) / 2;
+  const int kq0 = (wave & 1) * kqh, kq1 = min(kq0 + kqh, nkq);
+  const int rg = tile * 2 + wave / 2;
+  const uint8_t* gbase = L.experts + size_t(e) * L.stride;
+  const uint8_t* ubase = gbase + pm.bytes;
+  const uint8_t* gcodes = gbase + size_t(rg) * pm.nkb * 1024;
+  const uint8_t* ucodes = ubase + size_t(rg) * pm.nkb * 1024;
+  const uint8_t* gscl = gbase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  const uint8_t* uscl = ubase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  const int xstride = pad_k(H) + 8;
+
+  for (int t0 = p0; t0 < p1; t0 += L.mtp_gu) {
+    const int mt = min(L.mtp_gu, p1 - t0);
+    GuTiles ta, tb;
+    auto load = [&](GuTiles& t, int kq) { load_gu(t, gcodes, ucodes, gscl, uscl, kq, pm.nkb, lane); };
+    if (kq0 < kq1) load(ta, kq0);
+    __syncthreads();
+    stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) {
+      return L.x + size_t(min(L.plan.pairs[t0 + j] / L.k, L.T - 1)) * H;
+    });
+    __syncthreads();
+    const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+    pipeline2(kq0, kq1, ta, tb, load,
+              [&](const GuTiles& t, int kq) { mma_gu(t, xrow, kq, g, ag, au); });
+    join_halves(ag, au, red);
+    if (!(wave & 1) && c < mt) {
+      const int pair = L.plan.pairs[t0 + c];
+      uint32_t hv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t hi, lo;
+        split_bf16(silu(ag[i]) * au[i], hi, lo);
+        hv[i] = uint32_t(hi) | (uint32_t(lo) << 16);
+      }
+      *reinterpret_cast<u32x4*>(L.h + size_t(pair) * I + rg * 16 + 4 * g) =
+          u32x4{hv[0], hv[1], hv[2], hv[3]};
+    }
+  }
+}
+
+// Shared gate/up (bf16): 1 KiB tiles of 16 rows x 32 columns are the A
+// operand as loaded; four tiles per super-step, double-buffered.  A bf16
+// row is 3.8x the bytes of an MXFP4 row, so a workgroup takes one row group
+// and its four waves split the contraction in quarters (more waves in
+// flight for the same bytes).
+__device__ void shared_gateup(const GemvLayer& L, int sx, int rg, uint16_t* xs, float* red) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const int nu = H / 32;
+  const int nq = (nu + 3) / 4;
+  const int qq = (nq + kWaves - 1) / kWaves;
+  const int q0 = min(wave * qq, nq), q1 = min(q0 + qq, nq);
+  const uint16_t* gt = L.sgate + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
+  const uint16_t* ut = L.sup + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
+  const int xstride = pad_k(H) + 8;
+  const size_t plane = size_t(L.S) * L.T * I;
+  struct Bf16Tiles {
+    u32x4 g[4], u[4];
+  };
+  auto load = [&](Bf16Tiles& t, int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = min(4 * q + j, nu - 1);  // past the end: multiplied by zeros
+      t.g[j] = ld_nt(gt + size_t(u) * 512 + 8 * lane);
+      t.u[j] = ld_nt(ut + size_t(u) * 512 + 8 * lane);
+    }
+  };
+  for (int t0 = 0; t0 < L.T; t0 += L.mtp_gu) {
+    const int mt = min(L.mtp_gu, L.T - t0);
+    Bf16Tiles ta, tb;
+    if (q0 < q1) load(ta, q0);
+    __syncthreads();
+    stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) { return L.x + size_t(t0 + j) * H; });
+    __syncthreads();
+    const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+    pipeline2(q0, q1, ta, tb, load, [&](const Bf16Tiles& t, int q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 bx = lds16(xrow + (4 * q + j) * 32 + 8 * g);
+        ag = mfma(t.g[j], bx, ag);
+        au = mfma(t.u[j], bx, au);
+      }
+    });
+    join_quarters(ag, au, red);
+    if (wave == 0 && c < mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t hi, lo;
+        split_bf16(silu(ag[i]) * au[i], hi, lo);
+        const size_t o = (size_t(sx) * L.T + t0 + c) * I + rg * 16 + 4 * g + i;
+        L.hs[o] = hi;
+        L.hs[plane + o] = lo;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Down projections and the combine.  Workgroups are (expert, tile of kRowsD
+// output rows, 16 per wave); h enters as bf16 hi + lo, staged in LDS, two
+// MFMAs per step.  The shared experts' down runs in an earlier launch and
+// leaves fp32 outputs in ysh.  Each routed workgroup writes fp32 partials
+// for its rows and tokens; the last one to finish a tile (device-scope
+// counter, zeroed by the plan builder of the same call) sums the tile's
+// partials in a fixed order -- routed slots j = 0..k-1 weighted by w, then
+// the shared experts, then the residual -- and writes the bf16 output.  The
+// sum order does not depend on which workgroup arrives last, so the output
+// is deterministic.
+
+struct DnTiles {
+  u32x4 w[4];
+  uint32_t sc;
+};
+
+// Routed down: workgroup = (expert, tile of kRowsD rows); wave w takes the
+// tile's row groups 4 w .. 4 w + 3 one after the other as one continuous
+// pipeline of (row group, super-step) steps, so its loads never drain
+// between row groups; a row group's partials are stored after its last
+// super-step.
+__device__ void routed_down(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int e = L.plan.active[a];
+  const int p0 = L.plan.act_off[a];
+  const int p1 = L.plan.act_off[a + 1];
+  const int H = L.H, I = L.I;
+  const PackedMx pgu(I, H), pd(H, I);
+  const int nkq = pd.nkb4 / 4;
+  constexpr int kGroups = kRowsD / 16 / kWaves;  // row groups per wave
+  const int rg0 = tile * (kRowsD / 16) + wave * kGroups;
+  const int nrg = max(0, min(kGroups, H / 16 - rg0));  // live row groups (ragged last tile)
+  const int nsteps = nrg * nkq;
+  const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
+  const uint8_t* codes = base + size_t(rg0) * pd.nkb * 1024 + 16 * lane;
+  const uint8_t* scl = base + pd.code_bytes + (size_t(rg0) * 64 + lane) * pd.nkb4;
+  const int hstride = pad_k(I) + 8;
+  uint16_t* hs_hi = hsm;
+  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
+  auto load = [&](DnTiles& t, int s) {
+    const int r = s / nkq, kq = s - r * nkq;
+    const uint8_t* cr = codes + size_t(r) * pd.nkb * 1024;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      t.w[j] = ld_nt(cr + size_t(min(4 * kq + j, pd.nkb - 1)) * 1024);
+    t.sc = *reinterpret_cast<const uint32_t*>(scl + size_t(r) * 64 * pd.nkb4 + 4 * kq);
+  };
+
+  for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
+    const int mt = min(L.mtp_d, p1 - t0);
+    DnTiles ta, tb;
+    if (nsteps > 0) load(ta, 0);
+    __syncthreads();
+    stage_h(hs_hi, hs_lo, hstride, mt, I, pad_k(I),
+            [&](int j) { return L.h + size_t(L.plan.pairs[t0 + j]) * I; });
+    __syncthreads();
+    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
+    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
+    const int pair = L.plan.pairs[t0 + (c < mt ? c : 0)];
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    pipeline2(0, nsteps, ta, tb, load, [&](const DnTiles& t, int s) {
+      const int r = s / nkq, kq = s - r * nkq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int bi = 16 * kq + 4 * j + g;
+        const float sd = e8m0_to_f32((t.sc >> (8 * j)) & 0xFFu);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 aw = fp4x8_scaled(t.w[j][q], sd);
+          acc = mfma(aw, lds16(bh + bi * 32 + 8 * q), acc);
+          acc = mfma(aw, lds16(bl + bi * 32 + 8 * q), acc);
+        }
+      }
+      if (kq == nkq - 1) {  // row group rg0 + r complete
+        if (c < mt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            store_coherent(&L.part[size_t(pair) * H + (rg0 + r) * 16 + 4 * g + i], acc[i]);
+        }
+        acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    });
+  }
+}
+
+__device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int rg = tile * (kRowsSD / 16) + wave;
+  const bool live = rg < L.H / 16;
+  const int H = L.H, I = L.I;
+  const int nu = I / 32;
+  const int nq = (nu + 3) / 4;
+  const uint16_t* dt = L.sdown + sx * (size_t(H) * I) + size_t(live ? rg : 0) * nu * 512;
+  const int hstride = pad_k(I) + 8;
+  uint16_t* hs_hi = hsm;
+  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
+  const size_t plane = size_t(L.S) * L.T * I;
+  struct Bf16Tile4 {
+    u32x4 w[4];
+  };
+  auto load = [&](Bf16Tile4& t, int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = 4 * q + j;
+      t.w[j] = ld_nt(dt + size_t(min(u, nu - 1)) * 512 + 8 * lane);
+    }
+  };
+  for (int t0 = 0; t0 < L.T; t0 += L.mtp_d) {
+    const int mt = min(L.mtp_d, L.T - t0);
+    Bf16Tile4 ta, tb;
+    if (live) load(ta, 0);
+    __syncthreads();
+    stage_rows(hs_hi, hstride, mt, I, pad_k(I),
+               [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
+    stage_rows(hs_lo, hstride, mt, I, pad_k(I),
+               [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
+    __syncthreads();
+    if (!live) continue;
+    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
+    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    pipeline2(0, nq, ta, tb, load, [&](const Bf16Tile4& t, int q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int u = 4 * q + j;
+        const u32x4 vh = lds16(bh + u * 32 + 8 * g);
+        const u32x4 vl = lds16(bl + u * 32 + 8 * g);
+        acc = mfma(t.w[j], vh, acc);
+        acc = mfma(t.w[j], vl, acc);
+      }
+    });
+    if (c < mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        L.ysh[(size_t(sx) * L.T + t0 + c) * H + rg * 16 + 4 * g + i] = acc[i];
+    }
+  }
+}
+
+// The last routed workgroup of a tile sums the partials into the bf16 output.
+// All of a token's partial loads are issued before the first add, so the
+// tail costs one memory round trip, not k of them.
+__device__ void combine_tile(const GemvLayer& L, int tile) {
+  const int H = L.H;
+  const int n_out = L.T * kRowsD;
+  for (int idx = threadIdx.x; idx < n_out; idx += kThreads) {
+    const int t = idx / kRowsD;
+    const int n = tile * kRowsD + idx % kRowsD;
+    if (n >= H) continue;
+    float pv[32], wv[32], sv[4];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const size_t p = size_t(t) * L.k + j;
+      pv[j] = j < L.k ? load_coherent(&L.part[p * H + n]) : 0.0f;
+      wv[j] = j < L.k ? L.w[p] : 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sv[s] = s < L.S ? L.ysh[(size_t(s) * L.T + t) * H + n] : 0.0f;
+    const float r = L.residual != nullptr ? bf16_to_f32(L.residual[size_t(t) * H + n]) : 0.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < L.k) acc = fmaf(wv[j], pv[j], acc);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (s < L.S) acc += sv[s];
+    if (L.residual != nullptr) acc += r;
+    L.y[size_t(t) * H + n] = f32_to_bf16(acc);
+  }
+}
+
+
+// ------------------------------------------------------------------------
+// Role dispatch.  A launch's grid is the concatenation, in this order, of
+// the role segments present in it (Stage counts, 0 = absent).
+
+enum : unsigned {
+  kRoleLogits = 1u,       // router logits, 4 experts per workgroup
+  kRoleSelect = 2u,       // top-k, 4 tokens per workgroup (+ plan by the last)
+  kRolePlan = 4u,         // plan from a given routing (one workgroup)
+  kRoleSharedGU = 8u,     // shared gate/up, (expert, 32 rows) per workgroup
+  kRoleSharedDown = 16u,  // shared down, (expert, 64 rows) per workgroup
+  kRoleRoutedGU = 32u,    // routed gate/up, (active slot, 32 rows)
+  kRoleRoutedDown = 64u,  // routed down, (active slot, 256 rows) + combine
+};
+
+__device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int t = b * 4 + wave;
+  if (t < L.T) {
+    int id;
+    float w;
+    select_token(L.logits + size_t(t) * L.E, L.E, L.k, id, w);
+    if (lane < L.k) {
+      store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
+      store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
+    }
+  }
+  if (!st.plan_after_select) return;
+  if (!arrive_last(L.sel_cnt, st.n_select)) return;
+  const int32_t* ids = L.ids_out;
+  build_plan([&](int p) { return load_coherent(ids + p); }, L.T * L.k, L.E, L.plan, L.tile_cnt,
+             L.n_tiles);
+}
+
+__device__ void routed_down_role(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
+  const int n_active = L.plan.n_active[0];
+  if (a >= n_active) return;  // slot beyond this routing's experts
+  routed_down(L, a, tile, hsm);
+  if (arrive_last(&L.tile_cnt[tile], n_active)) combine_tile(L, tile);
+}
+
+template <unsigned R, int NCH>
+__device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) {
+  extern __shared__ u32x4 lds_raw[];
+  uint16_t* lds16p = reinterpret_cast<uint16_t*>(lds_raw);
+  __shared__ float red[(R & (kRoleSharedGU | kRoleRoutedGU)) ? kWaves * kWave * 8 : 1];
+  int b = blockIdx.x;
+  if constexpr ((R & kRoleLogits) != 0) {
+    if (b < st.n_logits) {
+      // the select workgroups of the next launch count their arrivals here
+      if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
+      router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
+      return;
+    }
+    b -= st.n_logits;
+  }
+  if constexpr ((R & kRoleSelect) != 0) {
+    if (b < st.n_select) {
+      select_role(L, st, b);
+      return;
+    }
+    b -= st.n_select;
+  }
+  if constexpr ((R & kRolePlan) != 0) {
+    if (b < st.n_plan) {
+      const int32_t* ids = L.ids_in;
+      build_plan([&](int p) { return ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt,
+                 L.n_tiles);
+      return;
+    }
+    b -= st.n_plan;
+  }
+  const int gu_tiles = L.I / 32;
+  if constexpr ((R & kRoleSharedGU) != 0) {
+    if (b < st.n_sgu) {
+      shared_gateup(L, b / (L.I / 16), b % (L.I / 16), lds16p, red);
+      return;
+    }
+    b -= st.n_sgu;
+  }
+  if constexpr ((R & kRoleSharedDown) != 0) {
+    if (b < st.n_sdn) {
+      shared_down(L, b / L.n_stiles, b % L.n_stiles, lds16p);
+      return;
+    }
+    b -= st.n_sdn;
+  }
+  if constexpr ((R & kRoleRoutedGU) != 0) {
+    if (b < st.n_rgu) {
+      routed_gateup(L, b / gu_tiles, b % gu_tiles, lds16p, red);
+      return;
+    }
+    b -= st.n_rgu;
+  }
+  if constexpr ((R & kRoleRoutedDown) != 0) {
+    if (b < st.n_rdn) routed_down_role(L, b / L.n_tiles, b % L.n_tiles, lds16p);
+  }
+}
+
+// The launches, named for what they run.
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void moe_router_shared_gateup(GemvLayer L, Stage st) {
+  stage_body<kRoleLogits | kRoleSharedGU, NCH>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_select_shared_down(GemvLayer L, Stage st) {
+  stage_body<kRoleSelect | kRoleSharedDown, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_plan_shared_gateup(GemvLayer L, Stage st) {
+  stage_body<kRolePlan | kRoleSharedGU, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_routed_gateup(GemvLayer L, Stage st) {
+  stage_body<kRoleSharedDown | kRoleRoutedGU, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_routed_down_combine(GemvLayer L, Stage st) {
+  stage_body<kRoleRoutedDown, 0>(L, st);
+}
+
+int tokens_per_pass(int T, int row_bytes) {
+  const int t = kLdsBudget / row_bytes;
+  return max(1, min(min(t, kCols), T));
+}
+
+}  // namespace
+
+static_assert(kThreads == kPlanThreads, "the plan builder runs on one stage workgroup");
+
+hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t stream) {
+  L.n_tiles = (L.H + kRowsD - 1) / kRowsD;
+  L.n_stiles = (L.H + kRowsSD - 1) / kRowsSD;
+  const int xrow = pad_k(L.H) + 8, hrow = pad_k(L.I) + 8;  // staged row lengths
+  L.mtp_gu = tokens_per_pass(L.T, xrow * 2);
+  L.mtp_d = tokens_per_pass(L.T, hrow * 4);
+  size_t lds = 0;
+  if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
+  if (st.n_sgu > 0 || st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
+  if (st.n_sdn > 0 || st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
+  const int wgs =
+      st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu + st.n_rdn;
+  if (wgs <= 0) return hipSuccess;
+  const dim3 grid(wgs), block(kThreads);
+  switch (kind) {
+    case StageKind::RouterSharedGateUp: {
+      const int per_lane = (L.H / 8 + kWave - 1) / kWave;
+      if (per_lane <= 4)
+        hipLaunchKernelGGL(moe_router_shared_gateup<4>, grid, block, lds, stream, L, st);
+      else if (per_lane <= 8)
+        hipLaunchKernelGGL(moe_router_shared_gateup<8>, grid, block, lds, stream, L, st);
+      else
+        hipLaunchKernelGGL(moe_router_shared_gateup<16>, grid, block, lds, stream, L, st);
+      break;
+    }
+    case StageKind::SelectSharedDown:
+      hipLaunchKernelGGL(moe_select_shared_down, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::PlanSharedGateUp:
+      hipLaunchKernelGGL(moe_plan_shared_gateup, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::RoutedGateUp:
+      hipLaunchKernelGGL(moe_routed_gateup, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::RoutedDownCombine:
+      hipLaunchKernelGGL(moe_routed_down_combine, grid, block, lds, stream, L, st);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,16 +1,19 @@
-// Token -> expert grouping, as a device routine for one 1024-thread
-// workgroup (used by the stand-alone plan kernel and by the fused
-// select-and-plan kernel of the router).
+// Token -> expert grouping ("plan") built by one 256-thread workgroup, so
+// that each routed expert's weights are streamed once per call however many
+// tokens chose it (Deltafin README, "How it works": each token reads only
+// the experts it selected; a batch reads the union of their selections).
 #pragma once
 
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
+constexpr int kPlanExperts = 1024;  // largest expert count the plan handles
 
-// Inclusive scan of one int per thread across the 1024-thread workgroup.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* warp_tot) {
+// Inclusive scan of one int per thread across a 256-thread workgroup.
+// wtot: kPlanThreads / kWave ints of LDS; every thread must call it.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wtot) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
 #pragma unroll
@@ -18,61 +21,83 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* warp_tot) {
     const int o = __shfl_up(v, off, kWave);
     if (lane >= off) v += o;
   }
-  if (lane == kWave - 1) warp_tot[wave] = v;
+  if (lane == kWave - 1) wtot[wave] = v;
   __syncthreads();
-  if (wave == 0) {
-    int s = lane < kPlanThreads / kWave ? warp_tot[lane] : 0;
+  int add = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(s, off, kWave);
-      if (lane >= off) s += o;
-    }
-    if (lane < kPlanThreads / kWave) warp_tot[lane] = s;
-  }
-  __syncthreads();
-  const int add = wave > 0 ? warp_tot[wave - 1] : 0;
+  for (int w = 0; w < kPlanThreads / kWave; ++w)
+    if (w < wave) add += wtot[w];
   __syncthreads();
   return v + add;
 }
 
-// Builds `plan` from ids[n_pairs] (E <= 1024) and zeroes zero[0..n_zero).
-// Ids outside [0, E) are clamped so no access leaves the buffers; such
-// routings are the caller's error.  Pairs of one expert are listed in the
-// order the workgroup's atomics hand out slots (the results do not depend
-// on it: every pair is computed the same way wherever it sits).
-__device__ __forceinline__ void build_plan(const int32_t* ids, int n_pairs, int E, Plan plan,
-                                           int* zero, int n_zero) {
-  __shared__ int cnt[1024];
-  __shared__ int fill[1024];
-  __shared__ int warp_tot[kPlanThreads / kWave];
+// Builds `plan` from the routing ids(p), p < n_pairs (E <= kPlanExperts),
+// and zeroes zero[0 .. n_zero).  ids(p) is a callback so the routing can be
+// read either plainly or through the device-coherent level.  Ids outside
+// [0, E) are clamped, so nothing is read or written out of bounds; such a
+// routing is the caller's error.  The pairs of one expert are listed in the
+// order the LDS atomics hand out slots; no result depends on that order
+// (each pair is computed on its own and combined by slot index).
+template <typename Ids>
+__device__ void build_plan(Ids ids, int n_pairs, int E, Plan plan, int* zero, int n_zero) {
+  __shared__ int cnt[kPlanExperts];
+  __shared__ int wtot[kPlanThreads / kWave];
   const int tid = threadIdx.x;
   for (int i = tid; i < n_zero; i += kPlanThreads) zero[i] = 0;
-  cnt[tid] = 0;
+  for (int i = tid; i < kPlanExperts; i += kPlanThreads) cnt[i] = 0;
   __syncthreads();
-  for (int p = tid; p < n_pairs; p += kPlanThreads) {
-    const int e = min(max(ids[p], 0), E - 1);
-    atomicAdd(&cnt[e], 1);
+  // Eight loads in flight before their atomics: the ids may come from far
+  // memory, one round trip per batch instead of per pair.
+  constexpr int kBatch = 8;
+  for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kPlanThreads) {
+    int e[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j * kPlanThreads + tid;
+      e[j] = p < n_pairs ? min(max(ids(p), 0), E - 1) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (e[j] >= 0) atomicAdd(&cnt[e[j]], 1);
   }
   __syncthreads();
-  const int c = tid < E ? cnt[tid] : 0;
-  const int incl = block_inclusive_scan(c, warp_tot);
-  const int flag = c > 0 ? 1 : 0;
-  const int aincl = block_inclusive_scan(flag, warp_tot);
-  const int excl = incl - c;
-  if (flag) {
-    plan.active[aincl - 1] = tid;
-    plan.act_off[aincl - 1] = excl;
+  // Thread tid owns experts 4 tid .. 4 tid + 3.
+  int c[4], s = 0, a = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = cnt[4 * tid + q];
+    s += c[q];
+    a += c[q] > 0 ? 1 : 0;
   }
-  fill[tid] = excl;
+  const int s_incl = block_inclusive_scan(s, wtot);
+  const int a_incl = block_inclusive_scan(a, wtot);
+  int off = s_incl - s, ao = a_incl - a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
+    if (c[q] > 0) {
+      plan.active[ao] = e;
+      plan.act_off[ao] = off;
+      ++ao;
+    }
+    cnt[e] = off;  // from here on: next free slot of expert e
+    off += c[q];
+  }
   if (tid == kPlanThreads - 1) {
-    plan.n_active[0] = aincl;
-    plan.act_off[aincl] = n_pairs;
+    plan.n_active[0] = a_incl;
+    plan.act_off[a_incl] = n_pairs;
   }
   __syncthreads();
-  for (int p = tid; p < n_pairs; p += kPlanThreads) {
-    const int e = min(max(ids[p], 0), E - 1);
-    const int slot = atomicAdd(&fill[e], 1);
-    plan.pairs[slot] = p;
+  for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kPlanThreads) {
+    int e[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j * kPlanThreads + tid;
+      e[j] = p < n_pairs ? min(max(ids(p), 0), E - 1) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (e[j] >= 0) plan.pairs[atomicAdd(&cnt[e[j]], 1)] = p0 + j * kPlanThreads + tid;
   }
 }
 

@@ -129,6 +129,46 @@ def test_route_exact_ties_lower_index(b):
     np.testing.assert_allclose(w, 0.25, atol=1e-7)
 
 
+def _route(b, built, x_dev):
+    T, k = x_dev.shape[0], built.cfg["top_k"]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    b.route(built.lib, x_dev, ids, w, built.lib.workspace(T))
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def test_route_entry_matches_oracle_and_layer_routing(b):
+    # 70 tokens: 18 top-k workgroups, the last of which builds the plan
+    built = Built(MANY, seed=5, bias=True)
+    xh, xd = SD.upload_tokens(1300, 70, MANY["hidden"])
+    ids, w = _route(b, built, xd)
+    _, _, s = M.route(xh, built.oracle)
+    check_routing(ids, w, s, MANY["top_k"])
+    np.testing.assert_allclose(w, oracle_weights(s, ids), rtol=0, atol=2e-6)
+    ids2, w2, _ = _run_layer(b, built, xd)
+    assert np.array_equal(ids, ids2) and np.array_equal(w.view(np.uint32), w2.view(np.uint32))
+
+
+def test_route_many_winners_in_one_lane(b):
+    # Experts 5, 69, 133, ... (e = 5 mod 64) sit in one lane of the top-k
+    # wave; a large bias makes all 16 of them winners, more than the lane's
+    # candidate list holds, so the selection must take its exact path.
+    built = Built(MANY, seed=6, bias=True)
+    bias = built.dev["host_bias"].copy()
+    bias[5::64] += 20.0
+    built.dev["router_bias"].copy_(torch.from_numpy(bias))
+    built.oracle.router_bias = bias
+    xh, xd = SD.upload_tokens(1301, 5, MANY["hidden"])
+    ids, w = _route(b, built, xd)
+    _, _, s = M.route(xh, built.oracle)
+    check_routing(ids, w, s, MANY["top_k"])
+    np.testing.assert_allclose(w, oracle_weights(s, ids), rtol=0, atol=2e-6)
+    for t in range(5):
+        assert set(range(5, 1024, 64)) <= set(ids[t].tolist())
+        assert np.all(ids[t][:16] % 64 == 5)
+
+
 # ------------------------------------------------------------- layer -----
 
 @pytest.mark.parametrize("T", [1, 3, 16])
@@ -143,7 +183,7 @@ def test_forward_tiny_given_oracle_routing(b, tiny, T):
 
 
 @pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY], ids=["tiny", "ragged", "wide", "many"])
-@pytest.mark.parametrize("T", [1, 7])
+@pytest.mark.parametrize("T", [1, 7, 70])
 def test_layer_matches_oracle(b, cfg, T):
     built = Built(cfg, seed=11)
     xh, xd = SD.upload_tokens(1100 + T, T, cfg["hidden"])
