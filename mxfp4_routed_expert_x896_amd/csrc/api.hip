@@ -90,15 +90,25 @@ int check_layer(const moe_layer_desc* L) {
 }
 
 constexpr int64_t kMaxTokens = 1 << 16;
+// MOE_PATH_AUTO switches to the MFMA (prefill) path from this many tokens.
+constexpr int64_t kMfmaMinTokens = 256;
 
 uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
 int n_tiles(const moe_layer_desc* L) { return (L->hidden + moe::kDownRows - 1) / moe::kDownRows; }
+uint64_t pad512(uint64_t v) { return (v + 511) / 512 * 512; }
+// Upper bound on the prefill token tiles (64 pairs of one expert each).
+int max_mtiles(const moe_layer_desc* L, int64_t T) {
+  const int64_t pairs = T * L->top_k;
+  const int64_t active = pairs < L->n_experts ? pairs : L->n_experts;
+  return int((pairs + 63 * active) / 64 + 1);
+}
 int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
 
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt, total;
+  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
+  uint64_t n_mtiles, mtiles, xq, xs, hq, hs8, total;
 };
 
 Carve carve(const moe_layer_desc* L, int64_t T) {
@@ -122,6 +132,13 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
   c.ysh = take(S * t * H * 4);
   c.tile_cnt = take(n_tiles(L) * 4);
   c.sel_cnt = take(4);
+  const uint64_t Kq = pad512(H), Iq = pad512(I);
+  c.n_mtiles = take(4);
+  c.mtiles = take(uint64_t(max_mtiles(L, T)) * 4);
+  c.xq = take(t * Kq);
+  c.xs = take(t * Kq / 32);
+  c.hq = take(t * k * Iq);
+  c.hs8 = take(t * k * Iq / 32);
   c.total = off;
   return c;
 }
@@ -172,6 +189,14 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.part = at<float>(ws, c.part);
   G.ysh = at<float>(ws, c.ysh);
   G.tile_cnt = at<int>(ws, c.tile_cnt);
+  G.plan.n_mtiles = at<int32_t>(ws, c.n_mtiles);
+  G.plan.mtiles = at<int32_t>(ws, c.mtiles);
+  G.Kq = int(pad512(L->hidden));
+  G.Iq = int(pad512(L->inter));
+  G.xq = at<uint8_t>(ws, c.xq);
+  G.xs = at<uint8_t>(ws, c.xs);
+  G.hq = at<uint8_t>(ws, c.hq);
+  G.hs8 = at<uint8_t>(ws, c.hs8);
   return G;
 }
 
@@ -256,6 +281,36 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   moe::Stage s4;
   s4.n_rdn = ma * n_tiles(L);
   return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
+}
+
+// Prefill (MFMA) path for a given routing: plan + x -> MXFP8 + shared
+// gate/up; routed gate/up (scaled MFMA) + shared down; routed down (scaled
+// MFMA) -> per-pair partials; combine.
+int do_forward_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
+                    const float* w, const uint16_t* residual, uint16_t* y, void* ws,
+                    hipStream_t stream) {
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_in = ids;
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  const int S = L->n_shared, mt = max_mtiles(L, T);
+  moe::Stage s1;
+  s1.n_plan = 1;
+  s1.n_xq = int((T * (G.Kq / 32) + 255) / 256);
+  s1.n_sgu = S * (L->inter / 16);
+  int st = stage(moe::StageKind::PlanQuantSharedGateUp, G, s1, stream);
+  if (st) return st;
+  moe::Stage s2;
+  s2.n_mgu = mt * ((L->inter + 127) / 128);
+  s2.n_sdn = S * n_shared_tiles(L);
+  if ((st = stage(moe::StageKind::MxGateUpSharedDown, G, s2, stream))) return st;
+  moe::Stage s3;
+  s3.n_mdn = mt * ((L->hidden + 255) / 256);
+  if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
+  moe::Stage s4;
+  s4.n_comb = int(T);
+  return stage(moe::StageKind::Combine, G, s4, stream);
 }
 
 int resolve_path(int32_t path, int64_t T) {
@@ -358,7 +413,7 @@ MOE_API int moe_workspace_bytes(const moe_layer_desc* layer, int64_t n_tokens,
   return MOE_OK;
 }
 
-MOE_API int64_t moe_mfma_min_tokens(void) { return INT64_MAX; }
+MOE_API int64_t moe_mfma_min_tokens(void) { return kMfmaMinTokens; }
 
 MOE_API int moe_route(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
                       int32_t* topk_ids, float* topk_w, void* workspace,
@@ -388,8 +443,9 @@ MOE_API int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t 
   if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
   prof_begin(stream);
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
+    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
   return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
 }
 
@@ -407,8 +463,12 @@ MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) return MOE_EUNSUPPORTED;
   prof_begin(stream);
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) {
+    st = do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream);
+    if (st) return st;
+    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+  }
   return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
 }
 

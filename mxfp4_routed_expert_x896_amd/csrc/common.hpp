@@ -138,6 +138,44 @@ struct Plan {
   int32_t* active;    // [E] expert ids with pairs, ascending
   int32_t* act_off;   // [E + 1] start of each active expert's pairs in `pairs`
   int32_t* pairs;     // [T * k] pair ids grouped by expert
+  int32_t* n_mtiles;  // [1] number of token tiles (kPlanTileTokens pairs of one expert)
+  int32_t* mtiles;    // [<= E + T * k / kPlanTileTokens] slot << 16 | tile index within the slot
 };
+
+// Pairs per token tile of the prefill (MFMA) path.
+constexpr int kPlanTileTokens = 64;
+
+// floor(log2 |a|) of a non-zero finite fp32 (normal or subnormal).
+__device__ __forceinline__ int floor_log2_f32(float a) {
+  const uint32_t u = __float_as_uint(a) & 0x7FFFFFFFu;
+  const int f = int(u >> 23);
+  if (f > 0) return f - 127;
+  return (31 - __clz(int(u))) - 149;
+}
+
+// E4M3FN code of v (finite), round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9
+    const uint32_t q = uint32_t(rintf(a * 512.0f));  // 0..8; 8 is the first normal
+    return sign | q;
+  }
+  int e = floor_log2_f32(a);  // -6 .. 8
+  uint32_t q = uint32_t(rintf(__builtin_ldexpf(a, 3 - e)));  // 8 .. 16
+  if (q == 16u) {
+    q = 8u;
+    e += 1;
+  }
+  return sign | (uint32_t(e + 7) << 3) | (q - 8u);
+}
+
+// MXFP8 block exponent for a block with largest magnitude amax (OCP MX
+// rule as read here): clamp(floor(log2 amax) - 8, -127, 127), -127 for 0.
+__device__ __forceinline__ int mxfp8_block_exp(float amax) {
+  const int E = amax == 0.0f ? -127 : floor_log2_f32(amax) - 8;
+  return max(-127, min(127, E));
+}
 
 }  // namespace moe

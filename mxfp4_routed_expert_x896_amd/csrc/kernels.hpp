@@ -37,6 +37,13 @@ struct GemvLayer {
   float* ysh;               // fp32 [S][T][H]  shared expert outputs
   int* tile_cnt;            // [n_tiles] routed down arrivals per output tile (zeroed by
                             // the plan builder of the same call)
+  // prefill (MFMA) path: MXFP8 activations, rows padded to Kq / Iq columns
+  // (multiples of 512, zero codes past H / I); scale rows in MFMA order
+  int Kq, Iq;
+  uint8_t* xq;              // E4M3 [T][Kq]
+  uint8_t* xs;              // E8M0 [T][Kq / 32]
+  uint8_t* hq;              // E4M3 [T*k][Iq]   routed SiLU(g)*u per pair
+  uint8_t* hs8;             // E8M0 [T*k][Iq / 32]
   const float* w;           // fp32 [T][k] combine weights
   const uint16_t* residual; // bf16 [T][H] or null
   uint16_t* y;              // bf16 [T][H]
@@ -52,6 +59,10 @@ struct Stage {
   int n_sdn = 0;              // S * ceil(H / 64)
   int n_rgu = 0;              // max_active * I / 32
   int n_rdn = 0;              // max_active * ceil(H / kDownRows)
+  int n_xq = 0;               // x quantisation, 256 blocks of 32 per workgroup
+  int n_mgu = 0;              // max token tiles * ceil(I / 128)  (prefill gate/up)
+  int n_mdn = 0;              // max token tiles * ceil(H / 256)  (prefill down)
+  int n_comb = 0;             // T  (prefill combine, one token per workgroup)
 };
 
 enum class StageKind {
@@ -60,6 +71,10 @@ enum class StageKind {
   PlanSharedGateUp,    // roles: plan, shared gate/up
   RoutedGateUp,        // roles: shared down, routed gate/up
   RoutedDownCombine,   // roles: routed down + combine
+  PlanQuantSharedGateUp,  // prefill: plan, x -> MXFP8, shared gate/up
+  MxGateUpSharedDown,  // prefill: routed gate/up (MFMA), shared down
+  MxDown,              // prefill: routed down (MFMA) -> per-pair partials
+  Combine,             // prefill: weighted combine of the partials
 };
 
 hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t stream);

@@ -38,6 +38,7 @@
 // 8 g .. 8 g + 7.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mxgemm.hpp"
 #include "plan.hpp"
 #include "router.hpp"
 
@@ -569,7 +570,226 @@ enum : unsigned {
   kRoleSharedDown = 16u,  // shared down, (expert, 64 rows) per workgroup
   kRoleRoutedGU = 32u,    // routed gate/up, (active slot, 32 rows)
   kRoleRoutedDown = 64u,  // routed down, (active slot, 256 rows) + combine
+  kRoleQuantX = 128u,     // prefill: x -> MXFP8 (256 blocks per workgroup)
+  kRoleMxGateUp = 256u,   // prefill: routed gate/up, (token tile, 128 rows)
+  kRoleMxDown = 512u,     // prefill: routed down, (token tile, 256 rows)
+  kRoleCombine = 1024u,   // prefill: combine, one token per workgroup
 };
+
+// ------------------------------------------------------------------------
+// Prefill roles.
+
+// x rows -> MXFP8: thread per 32-element block of the padded row (blocks
+// past H get zero codes and exponent 127).
+__device__ void quant_x_role(const GemvLayer& L, int b) {
+  const int nbq = L.Kq / 32;
+  const size_t gb = size_t(b) * kThreads + threadIdx.x;
+  if (gb >= size_t(L.T) * nbq) return;
+  const int t = int(gb / nbq), kb = int(gb % nbq);
+  uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int E = 0;
+  if (kb * 32 < L.H) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(L.x + size_t(t) * L.H + kb * 32);
+    u32x4 v[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = src[i];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][d])), fabsf(bf16_hi(v[i][d]))));
+    }
+    E = mxfp8_block_exp(amax);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t c0 = e4m3_rne_sat(__builtin_ldexpf(bf16_lo(v[i][d]), -E));
+        const uint32_t c1 = e4m3_rne_sat(__builtin_ldexpf(bf16_hi(v[i][d]), -E));
+        words[2 * i + d / 2] |= (c0 | (c1 << 8)) << (16 * (d % 2));
+      }
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(L.xq + size_t(t) * L.Kq + kb * 32);
+  dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+  dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  L.xs[size_t(t) * nbq + mx::scale_pos(kb)] = uint8_t(E + 127);
+}
+
+// Token tile ti of the plan: slot, first pair and number of pairs.
+struct MxTile {
+  int a, p0, mt;
+};
+__device__ __forceinline__ bool mx_tile(const GemvLayer& L, int ti, MxTile& t) {
+  if (ti >= L.plan.n_mtiles[0]) return false;
+  const int packed = L.plan.mtiles[ti];
+  t.a = packed >> 16;
+  t.p0 = L.plan.act_off[t.a] + (packed & 0xFFFF) * mx::kTok;
+  t.mt = min(mx::kTok, L.plan.act_off[t.a + 1] - t.p0);
+  return true;
+}
+
+// Prefill gate/up: workgroup = (token tile, 128 rows of I); wave w takes row
+// groups 2 w, 2 w + 1 of gate and up (4 A streams) against the tile's 64
+// tokens.  Epilogue: h = SiLU(g) * u in fp32, then MXFP8 along I -- the
+// wave's 32 rows are exactly one block per token.
+__device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int tiles_r = (L.I + 127) / 128;
+  MxTile tt;
+  if (!mx_tile(L, b / tiles_r, tt)) return;
+  const int rt = b % tiles_r;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const int e = L.plan.active[tt.a];
+  const PackedMx pm(I, H);
+  const int ngroups = I / 16;
+  const int rg0 = rt * 8 + 2 * wave;
+  const uint8_t* base[2] = {L.experts + size_t(e) * L.stride,
+                            L.experts + size_t(e) * L.stride + pm.bytes};
+  mx::AStreams st;
+  st.nkb = pm.nkb;
+#pragma unroll
+  for (int s = 0; s < mx::kNS; ++s) {
+    const int rg = min(rg0 + (s & 1), ngroups - 1);
+    st.codes[s] = base[s >> 1] + size_t(rg) * pm.nkb * 1024 + 16 * lane;
+    st.scl[s] = base[s >> 1] + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  }
+  const int* pairs = L.plan.pairs + tt.p0;
+  const int last = tt.mt - 1;
+  auto tok = [&](int j) { return pairs[min(j, last)] / L.k; };
+  mx::f32x4 acc[mx::kNS][mx::kSub];
+  mx::gemm_tile(
+      acc, st, pm.nkb4 / 4, lds, [&](int j) { return L.xq + size_t(tok(j)) * L.Kq; },
+      [&](int j) { return L.xs + size_t(tok(j)) * (L.Kq / 32); });
+  if (rt == tiles_r - 1 && L.Iq > I) {
+    // h columns I .. Iq are read by the down GEMM against clamped weight
+    // tiles: zero codes with a finite exponent make them contribute 0
+    const int pad16 = (L.Iq - I) / 16, pad_blocks = (L.Iq - I) / 32;
+    for (int i = threadIdx.x; i < tt.mt * pad16; i += kThreads)
+      *reinterpret_cast<u32x4*>(L.hq + size_t(pairs[i / pad16]) * L.Iq + I + 16 * (i % pad16)) =
+          u32x4{0, 0, 0, 0};
+    for (int i = threadIdx.x; i < tt.mt * pad_blocks; i += kThreads)
+      L.hs8[size_t(pairs[i / pad_blocks]) * (L.Iq / 32) +
+            mx::scale_pos(I / 32 + i % pad_blocks)] = 127;
+  }
+  if (rg0 >= ngroups) return;  // no rows for this wave (I not a multiple of 128)
+  const int blk = (rt * 128 + 32 * wave) / 32;  // MX block of the wave's rows along I
+#pragma unroll
+  for (int u = 0; u < mx::kSub; ++u) {
+    float h[2][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[r][i] = silu(acc[r][u][i]) * acc[2 + r][u][i];
+        amax = fmaxf(amax, fabsf(h[r][i]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    const int E = mxfp8_block_exp(amax);
+    const int j = 16 * u + c;
+    if (j < tt.mt) {
+      const int pair = pairs[j];
+      uint8_t* hrow = L.hq + size_t(pair) * L.Iq + rt * 128 + 32 * wave;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(__builtin_ldexpf(h[r][i], -E)) << (8 * i);
+        *reinterpret_cast<uint32_t*>(hrow + 16 * r + 4 * g) = word;
+      }
+      if (g == 0) L.hs8[size_t(pair) * (L.Iq / 32) + mx::scale_pos(blk)] = uint8_t(E + 127);
+    }
+  }
+}
+
+// Prefill down: workgroup = (token tile, 256 rows of H); wave w takes row
+// groups 4 w .. 4 w + 3.  Writes fp32 partials per pair (combined later).
+__device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int tiles_r = (L.H + 255) / 256;
+  MxTile tt;
+  if (!mx_tile(L, b / tiles_r, tt)) return;
+  const int rt = b % tiles_r;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const int e = L.plan.active[tt.a];
+  const PackedMx pgu(I, H), pd(H, I);
+  const int ngroups = H / 16;
+  const int rg0 = rt * 16 + 4 * wave;
+  const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
+  mx::AStreams st;
+  st.nkb = pd.nkb;
+#pragma unroll
+  for (int s = 0; s < mx::kNS; ++s) {
+    const int rg = min(rg0 + s, ngroups - 1);
+    st.codes[s] = base + size_t(rg) * pd.nkb * 1024 + 16 * lane;
+    st.scl[s] = base + pd.code_bytes + (size_t(rg) * 64 + lane) * pd.nkb4;
+  }
+  const int* pairs = L.plan.pairs + tt.p0;
+  const int last = tt.mt - 1;
+  mx::f32x4 acc[mx::kNS][mx::kSub];
+  mx::gemm_tile(
+      acc, st, pd.nkb4 / 4, lds,
+      [&](int j) { return L.hq + size_t(pairs[min(j, last)]) * L.Iq; },
+      [&](int j) { return L.hs8 + size_t(pairs[min(j, last)]) * (L.Iq / 32); });
+#pragma unroll
+  for (int u = 0; u < mx::kSub; ++u) {
+    const int j = 16 * u + c;
+    if (j >= tt.mt) continue;
+    float* prow = L.part + size_t(pairs[j]) * H;
+#pragma unroll
+    for (int s = 0; s < mx::kNS; ++s) {
+      if (rg0 + s >= ngroups) continue;
+      __builtin_nontemporal_store(acc[s][u],
+                                  reinterpret_cast<mx::f32x4*>(prow + (rg0 + s) * 16 + 4 * g));
+    }
+  }
+}
+
+// Prefill combine: y[t] = sum_j w[t][j] part[t k + j] + sum_s ysh[s][t]
+// (+ residual), rounded once to bf16; one token per workgroup, four outputs
+// per thread and step.
+__device__ void combine_role(const GemvLayer& L, int t) {
+  if (t >= L.T) return;
+  const int H = L.H, k = L.k;
+  float wv[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) wv[j] = j < k ? L.w[size_t(t) * k + j] : 0.0f;
+  for (int n = 4 * threadIdx.x; n < H; n += 4 * kThreads) {
+    mx::f32x4 pv[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < k)
+        pv[j] = __builtin_nontemporal_load(
+            reinterpret_cast<const mx::f32x4*>(L.part + (size_t(t) * k + j) * H + n));
+    mx::f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (j < k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wv[j], pv[j][i], acc[i]);
+    for (int sx = 0; sx < L.S; ++sx) {
+      const mx::f32x4 sv =
+          *reinterpret_cast<const mx::f32x4*>(L.ysh + (size_t(sx) * L.T + t) * H + n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += sv[i];
+    }
+    if (L.residual != nullptr) {
+      const u32x2 r = *reinterpret_cast<const u32x2*>(L.residual + size_t(t) * H + n);
+      acc[0] += bf16_lo(r[0]);
+      acc[1] += bf16_hi(r[0]);
+      acc[2] += bf16_lo(r[1]);
+      acc[3] += bf16_hi(r[1]);
+    }
+    *reinterpret_cast<u32x2*>(L.y + size_t(t) * H + n) =
+        u32x2{uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16),
+              uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16)};
+  }
+}
 
 __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const int wave = wave_id();
@@ -629,6 +849,34 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     }
     b -= st.n_plan;
   }
+  if constexpr ((R & kRoleQuantX) != 0) {
+    if (b < st.n_xq) {
+      quant_x_role(L, b);
+      return;
+    }
+    b -= st.n_xq;
+  }
+  if constexpr ((R & kRoleMxGateUp) != 0) {
+    if (b < st.n_mgu) {
+      mx_gateup_role(L, b, reinterpret_cast<uint8_t*>(lds_raw));
+      return;
+    }
+    b -= st.n_mgu;
+  }
+  if constexpr ((R & kRoleMxDown) != 0) {
+    if (b < st.n_mdn) {
+      mx_down_role(L, b, reinterpret_cast<uint8_t*>(lds_raw));
+      return;
+    }
+    b -= st.n_mdn;
+  }
+  if constexpr ((R & kRoleCombine) != 0) {
+    if (b < st.n_comb) {
+      combine_role(L, b);
+      return;
+    }
+    b -= st.n_comb;
+  }
   const int gu_tiles = L.I / 32;
   if constexpr ((R & kRoleSharedGU) != 0) {
     if (b < st.n_sgu) {
@@ -673,6 +921,18 @@ __global__ __launch_bounds__(kThreads) void moe_routed_gateup(GemvLayer L, Stage
 __global__ __launch_bounds__(kThreads) void moe_routed_down_combine(GemvLayer L, Stage st) {
   stage_body<kRoleRoutedDown, 0>(L, st);
 }
+__global__ __launch_bounds__(kThreads) void moe_plan_quant_shared_gateup(GemvLayer L, Stage st) {
+  stage_body<kRolePlan | kRoleQuantX | kRoleSharedGU, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_mx_gateup_shared_down(GemvLayer L, Stage st) {
+  stage_body<kRoleMxGateUp | kRoleSharedDown, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_mx_down(GemvLayer L, Stage st) {
+  stage_body<kRoleMxDown, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_combine(GemvLayer L, Stage st) {
+  stage_body<kRoleCombine, 0>(L, st);
+}
 
 int tokens_per_pass(int T, int row_bytes) {
   const int t = kLdsBudget / row_bytes;
@@ -693,8 +953,9 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
   if (st.n_sgu > 0 || st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
   if (st.n_sdn > 0 || st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
-  const int wgs =
-      st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu + st.n_rdn;
+  if (st.n_mgu > 0 || st.n_mdn > 0) lds = max(lds, size_t(2 * mx::kStageBytes));
+  const int wgs = st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu +
+                  st.n_rdn + st.n_xq + st.n_mgu + st.n_mdn + st.n_comb;
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs), block(kThreads);
   switch (kind) {
@@ -719,6 +980,18 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
       break;
     case StageKind::RoutedDownCombine:
       hipLaunchKernelGGL(moe_routed_down_combine, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::PlanQuantSharedGateUp:
+      hipLaunchKernelGGL(moe_plan_quant_shared_gateup, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::MxGateUpSharedDown:
+      hipLaunchKernelGGL(moe_mx_gateup_shared_down, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::MxDown:
+      hipLaunchKernelGGL(moe_mx_down, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::Combine:
+      hipLaunchKernelGGL(moe_combine, grid, block, lds, stream, L, st);
       break;
   }
   return hipGetLastError();

@@ -87,32 +87,6 @@ __global__ __launch_bounds__(256) void dequant_export_kernel(const uint8_t* __re
 
 // -------------------------------------------------------------- MXFP8 -----
 
-// floor(log2 |a|) of a non-zero finite fp32 (normal or subnormal).
-__device__ __forceinline__ int floor_log2_f32(float a) {
-  const uint32_t u = __float_as_uint(a) & 0x7FFFFFFFu;
-  const int f = int(u >> 23);
-  if (f > 0) return f - 127;
-  return (31 - __clz(int(u))) - 149;
-}
-
-// E4M3FN code of v (finite), round to nearest even, saturating at +-448.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a >= 448.0f) return sign | 0x7Eu;
-  if (a < 0.015625f) {  // below 2^-6: subnormal step 2^-9
-    const uint32_t q = uint32_t(rintf(a * 512.0f));  // 0..8; 8 is the first normal
-    return sign | q;
-  }
-  int e = floor_log2_f32(a);  // -6 .. 8
-  uint32_t q = uint32_t(rintf(__builtin_ldexpf(a, 3 - e)));  // 8 .. 16
-  if (q == 16u) {
-    q = 8u;
-    e += 1;
-  }
-  return sign | (uint32_t(e + 7) << 3) | (q - 8u);
-}
-
 // One thread per 32-element block: E = clamp(floor(log2 amax) - 8, -127,
 // 127) (-127 for an all-zero block), codes = E4M3(v / 2^E).
 __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __restrict__ x,
@@ -131,8 +105,7 @@ __global__ __launch_bounds__(256) void mxfp8_quant_kernel(const uint16_t* __rest
     for (int d = 0; d < 4; ++d)
       amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][d])), fabsf(bf16_hi(v[i][d]))));
   }
-  int E = amax == 0.0f ? -127 : floor_log2_f32(amax) - 8;
-  E = max(-127, min(127, E));
+  const int E = mxfp8_block_exp(amax);
   uint32_t words[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

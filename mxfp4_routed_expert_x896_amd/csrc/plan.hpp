@@ -32,7 +32,8 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wtot) {
 }
 
 // Builds `plan` from the routing ids(p), p < n_pairs (E <= kPlanExperts),
-// and zeroes zero[0 .. n_zero).  ids(p) is a callback so the routing can be
+// including the list of token tiles (kPlanTileTokens pairs of one expert,
+// in slot order), and zeroes zero[0 .. n_zero).  ids(p) is a callback so the routing can be
 // read either plainly or through the device-coherent level.  Ids outside
 // [0, E) are clamped, so nothing is read or written out of bounds; such a
 // routing is the caller's error.  The pairs of one expert are listed in the
@@ -62,20 +63,23 @@ __device__ void build_plan(Ids ids, int n_pairs, int E, Plan plan, int* zero, in
   }
   __syncthreads();
   // Thread tid owns experts 4 tid .. 4 tid + 3.
-  int c[4], s = 0, a = 0;
+  int c[4], s = 0, a = 0, m = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     c[q] = cnt[4 * tid + q];
     s += c[q];
     a += c[q] > 0 ? 1 : 0;
+    m += (c[q] + kPlanTileTokens - 1) / kPlanTileTokens;
   }
   const int s_incl = block_inclusive_scan(s, wtot);
   const int a_incl = block_inclusive_scan(a, wtot);
-  int off = s_incl - s, ao = a_incl - a;
+  const int m_incl = block_inclusive_scan(m, wtot);
+  int off = s_incl - s, ao = a_incl - a, mo = m_incl - m;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * tid + q;
     if (c[q] > 0) {
+      for (int j = 0; j * kPlanTileTokens < c[q]; ++j) plan.mtiles[mo++] = (ao << 16) | j;
       plan.active[ao] = e;
       plan.act_off[ao] = off;
       ++ao;
@@ -86,6 +90,7 @@ __device__ void build_plan(Ids ids, int n_pairs, int E, Plan plan, int* zero, in
   if (tid == kPlanThreads - 1) {
     plan.n_active[0] = a_incl;
     plan.act_off[a_incl] = n_pairs;
+    plan.n_mtiles[0] = m_incl;
   }
   __syncthreads();
   for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kPlanThreads) {

@@ -1,0 +1,108 @@
+"""GPU parity of the prefill (MFMA) path: routed experts on the block-scaled
+FP4 x FP8 matrix cores, x and h quantised to MXFP8 along the contraction.
+
+Reference: the float64 oracle with its MXFP8 activation reading (x and h
+replaced by their MXFP8 values, Deltafin explainer section 2.1), under the
+same routing.  The GPU quantises its fp32 h where the oracle quantises fp64
+h, so an element on an E4M3 rounding boundary may take the neighbouring
+code; that, fp32 accumulation and the final bf16 rounding stay inside the
+per-token relative L2 bar.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import synth.device as SD
+from oracle import moe as M
+
+from tests._gpu import (Built, check_mxfp8_parity, check_routing, mxfp8_h_flip_allowance,
+                        oracle_weights, rel_l2_per_token, to_np_u16)
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = dict(hidden=288, inter=96, n_experts=40, top_k=5, n_shared=2)
+WIDE = dict(hidden=8192, inter=64, n_experts=24, top_k=3, n_shared=1)
+MANY = dict(hidden=128, inter=32, n_experts=1024, top_k=32, n_shared=0)
+MID = dict(hidden=1024, inter=512, n_experts=16, top_k=4, n_shared=1)
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mxfp4_routed_expert_x896_amd import binding
+    return binding
+
+
+def _forward(b, built, x_dev, ids_np, w_np, residual=None):
+    T = x_dev.shape[0]
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    w = torch.from_numpy(np.ascontiguousarray(w_np, dtype=np.float32)).cuda()
+    y = torch.empty((T, built.cfg["hidden"]), dtype=torch.int16, device="cuda")
+    ws = built.lib.workspace(T)
+    b.forward(built.lib, x_dev, ids, w, y, ws, residual=residual, path=b.PATH_MFMA)
+    torch.cuda.synchronize()
+    return to_np_u16(y)
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY, MID],
+                         ids=["tiny", "ragged", "wide", "many", "mid"])
+@pytest.mark.parametrize("T", [1, 7, 70, 200])
+def test_mfma_forward_matches_oracle_mxfp8(b, cfg, T):
+    built = Built(cfg, seed=21)
+    xh, xd = SD.upload_tokens(1400 + T, T, cfg["hidden"])
+    ids, w, _ = M.route(xh, built.oracle)
+    w32 = w.astype(np.float32)
+    y = _forward(b, built, xd, ids, w32)
+    ref = M.moe_forward(xh, built.oracle, ids, w32.astype(np.float64), act_mxfp8=True)
+    allow = mxfp8_h_flip_allowance(xh, built.oracle, ids, w32)
+    check_mxfp8_parity(y, ref, allow)
+
+
+def test_mfma_skewed_routing_many_tiles_per_expert(b):
+    # every token picks experts 0..3: 300 pairs per expert, five 64-token tiles each
+    built = Built(MID, seed=22)
+    T = 300
+    xh, xd = SD.upload_tokens(1450, T, MID["hidden"])
+    ids = np.tile(np.arange(4, dtype=np.int32), (T, 1))
+    rng = np.random.default_rng(5)
+    w = rng.random((T, 4)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    y = _forward(b, built, xd, ids, w)
+    ref = M.moe_forward(xh, built.oracle, ids, w.astype(np.float64), act_mxfp8=True)
+    check_mxfp8_parity(y, ref, mxfp8_h_flip_allowance(xh, built.oracle, ids, w))
+
+
+def test_mfma_residual_and_layer_entry(b):
+    built = Built(RAGGED, seed=23, bias=True)
+    T = 90
+    xh, xd = SD.upload_tokens(1460, T, RAGGED["hidden"])
+    rh, rd = SD.upload_tokens(1461, T, RAGGED["hidden"])
+    ids = torch.empty((T, 5), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 5), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, RAGGED["hidden"]), dtype=torch.int16, device="cuda")
+    b.moe_layer(built.lib, xd, y, ids, w, built.lib.workspace(T), residual=rd, path=b.PATH_MFMA)
+    torch.cuda.synchronize()
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    _, _, s = M.route(xh, built.oracle)
+    check_routing(ids_np, w_np, s, 5)
+    wref = oracle_weights(s, ids_np)
+    ref = M.moe_forward(xh, built.oracle, ids_np, wref, act_mxfp8=True, residual_bits=rh)
+    check_mxfp8_parity(to_np_u16(y), ref, mxfp8_h_flip_allowance(xh, built.oracle, ids_np, wref))
+
+
+def test_mfma_and_gemv_paths_agree_closely(b):
+    # the two paths differ only by the MXFP8 rounding of x and h
+    built = Built(MID, seed=24)
+    T = 40
+    xh, xd = SD.upload_tokens(1470, T, MID["hidden"])
+    ids, w, _ = M.route(xh, built.oracle)
+    w32 = w.astype(np.float32)
+    y_mx = _forward(b, built, xd, ids, w32)
+    ref_exact = M.moe_forward(xh, built.oracle, ids, w32.astype(np.float64))
+    err = rel_l2_per_token(y_mx, ref_exact)
+    assert err.max() < 0.1  # MXFP8 activations: a few percent from the exact layer
+
+
+def test_auto_path_threshold(b):
+    assert b.mfma_min_tokens() >= 1
