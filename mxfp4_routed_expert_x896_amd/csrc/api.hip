@@ -283,9 +283,56 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
 }
 
-// Prefill (MFMA) path for a given routing: plan + x -> MXFP8 + shared
-// gate/up; routed gate/up (scaled MFMA) + shared down; routed down (scaled
-// MFMA) -> per-pair partials; combine.
+int round8(int v) { return (v + 7) / 8 * 8; }
+int n_quant_wgs(const moe::GemvLayer& G, int64_t T) { return int((T * (G.Kq / 32) + 255) / 256); }
+int n_token_tiles(int64_t T) { return int((T + 63) / 64); }
+// Grid of an XCD-ordered role over (pairs, token tiles): see xcd_split.
+int xcd_grid(int n_pairs, int64_t T) { return 8 * ((n_pairs + 7) / 8) * n_token_tiles(T); }
+
+// Prefill experts once the plan and the MXFP8 x exist: routed gate/up
+// (scaled MFMA) + shared gate/up (bf16 MFMA); routed down -> per-pair
+// partials + shared down; combine.  Segments before an XCD-ordered role are
+// padded to multiples of 8 so its block index keeps the XCD of blockIdx.
+int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hipStream_t stream) {
+  const int S = L->n_shared, mt = max_mtiles(L, T);
+  moe::Stage s2;
+  s2.n_mgu = round8(mt * ((L->inter + 127) / 128));
+  s2.n_sgmx = S > 0 ? xcd_grid(S * ((L->inter + 127) / 128), T) : 0;
+  int st = stage(moe::StageKind::MxGateUp, G, s2, stream);
+  if (st) return st;
+  moe::Stage s3;
+  s3.n_mdn = round8(mt * ((L->hidden + 255) / 256));
+  s3.n_sdmx = S > 0 ? xcd_grid(S * ((L->hidden + 255) / 256), T) : 0;
+  if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
+  moe::Stage s4;
+  s4.n_comb = int(T);
+  return stage(moe::StageKind::Combine, G, s4, stream);
+}
+
+// Prefill layer: x -> MXFP8 + router logits (MFMA); top-k + plan; experts.
+int do_layer_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                  const uint16_t* residual, uint16_t* y, int32_t* ids, float* w, void* ws,
+                  hipStream_t stream) {
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_out = ids;
+  G.w_out = w;
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  moe::Stage s0;
+  s0.n_xq = n_quant_wgs(G, T);
+  s0.n_rmx = ((L->n_experts + 255) / 256) * n_token_tiles(T);
+  int st = stage(moe::StageKind::RouterMxQuant, G, s0, stream);
+  if (st) return st;
+  moe::Stage s1;
+  s1.n_select = n_select_wgs(T);
+  s1.plan_after_select = 1;
+  if ((st = stage(moe::StageKind::SelectSharedDown, G, s1, stream))) return st;
+  return mfma_experts(L, G, T, stream);
+}
+
+// Prefill (MFMA) path for a given routing: plan + x -> MXFP8, then the
+// experts.
 int do_forward_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
                     const float* w, const uint16_t* residual, uint16_t* y, void* ws,
                     hipStream_t stream) {
@@ -294,23 +341,12 @@ int do_forward_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T, const
   G.w = w;
   G.residual = residual;
   G.y = y;
-  const int S = L->n_shared, mt = max_mtiles(L, T);
   moe::Stage s1;
   s1.n_plan = 1;
-  s1.n_xq = int((T * (G.Kq / 32) + 255) / 256);
-  s1.n_sgu = S * (L->inter / 16);
+  s1.n_xq = n_quant_wgs(G, T);
   int st = stage(moe::StageKind::PlanQuantSharedGateUp, G, s1, stream);
   if (st) return st;
-  moe::Stage s2;
-  s2.n_mgu = mt * ((L->inter + 127) / 128);
-  s2.n_sdn = S * n_shared_tiles(L);
-  if ((st = stage(moe::StageKind::MxGateUpSharedDown, G, s2, stream))) return st;
-  moe::Stage s3;
-  s3.n_mdn = mt * ((L->hidden + 255) / 256);
-  if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
-  moe::Stage s4;
-  s4.n_comb = int(T);
-  return stage(moe::StageKind::Combine, G, s4, stream);
+  return mfma_experts(L, G, T, stream);
 }
 
 int resolve_path(int32_t path, int64_t T) {
@@ -464,11 +500,8 @@ MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
   prof_begin(stream);
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA) {
-    st = do_route(layer, x, n_tokens, topk_ids, topk_w, workspace, stream);
-    if (st) return st;
-    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
-  }
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
+    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
   return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
 }
 

@@ -63,6 +63,9 @@ struct Stage {
   int n_mgu = 0;              // max token tiles * ceil(I / 128)  (prefill gate/up)
   int n_mdn = 0;              // max token tiles * ceil(H / 256)  (prefill down)
   int n_comb = 0;             // T  (prefill combine, one token per workgroup)
+  int n_rmx = 0;              // ceil(E / 256) * ceil(T / 64)  (prefill router)
+  int n_sgmx = 0;             // XCD-ordered grid over (S x ceil(I / 128), ceil(T / 64))
+  int n_sdmx = 0;             // XCD-ordered grid over (S x ceil(H / 256), ceil(T / 64))
 };
 
 enum class StageKind {
@@ -71,9 +74,10 @@ enum class StageKind {
   PlanSharedGateUp,    // roles: plan, shared gate/up
   RoutedGateUp,        // roles: shared down, routed gate/up
   RoutedDownCombine,   // roles: routed down + combine
-  PlanQuantSharedGateUp,  // prefill: plan, x -> MXFP8, shared gate/up
-  MxGateUpSharedDown,  // prefill: routed gate/up (MFMA), shared down
-  MxDown,              // prefill: routed down (MFMA) -> per-pair partials
+  PlanQuantSharedGateUp,  // plan, x -> MXFP8 (prefill), shared gate/up (decode)
+  RouterMxQuant,       // prefill: x -> MXFP8, router logits (MFMA)
+  MxGateUp,            // prefill: routed gate/up (scaled MFMA), shared gate/up (MFMA)
+  MxDown,              // prefill: routed down -> per-pair partials, shared down (MFMA)
   Combine,             // prefill: weighted combine of the partials
 };
 

@@ -38,6 +38,7 @@
 // 8 g .. 8 g + 7.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "bfgemm.hpp"
 #include "mxgemm.hpp"
 #include "plan.hpp"
 #include "router.hpp"
@@ -574,7 +575,147 @@ enum : unsigned {
   kRoleMxGateUp = 256u,   // prefill: routed gate/up, (token tile, 128 rows)
   kRoleMxDown = 512u,     // prefill: routed down, (token tile, 256 rows)
   kRoleCombine = 1024u,   // prefill: combine, one token per workgroup
+  kRoleRouterMx = 2048u,  // prefill: router logits, (256 experts, 64 tokens)
+  kRoleSharedGUMx = 4096u,    // prefill: shared gate/up, (expert, 128 rows, 64 tokens)
+  kRoleSharedDownMx = 8192u,  // prefill: shared down, (expert, 256 rows, 64 tokens)
 };
+
+// XCD-aware order for a grid over (pair, token tile): block b runs on XCD
+// b % 8 (the dispatcher's round robin), so pairs are dealt out to XCDs and
+// each XCD walks its pairs with the token tile fastest.  The workgroups
+// sharing a weight slice then run together on one XCD and read it through
+// its L2 once.  Returns false for the padding blocks.
+__device__ __forceinline__ bool xcd_split(int b, int n_pairs, int n_tt, int& pair, int& tt) {
+  const int xcd = b % 8, i = b / 8;
+  pair = xcd + 8 * (i / n_tt);
+  tt = i % n_tt;
+  return pair < n_pairs;
+}
+__host__ __device__ __forceinline__ int xcd_grid(int n_pairs, int n_tt) {
+  return 8 * ((n_pairs + 7) / 8) * n_tt;
+}
+
+// Prefill router: logits for 256 experts (4 row groups per wave, read from
+// the row-major router weights) x 64 tokens, plus the bias.
+__device__ void router_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
+  if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
+  const int n_tt = (L.T + bf::kTok - 1) / bf::kTok;
+  const int rt = b / n_tt, tt = b % n_tt;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, E = L.E;
+  const int rg0 = rt * 16 + 4 * wave;
+  const int t0 = tt * bf::kTok;
+  const int nkt = H / 32;
+  bf::f32x4 acc[bf::kNS][bf::kSub];
+  bf::gemm_tile<1>(
+      acc,
+      [&](int s, int kt) {
+        const int row = min((rg0 + s) * 16 + c, E - 1);
+        return L.wr + size_t(row) * H + 32 * min(kt, nkt - 1) + 8 * g;
+      },
+      H, lds, [&](int, int j) { return L.x + size_t(min(t0 + j, L.T - 1)) * H; });
+#pragma unroll
+  for (int u = 0; u < bf::kSub; ++u) {
+    const int t = t0 + 16 * u + c;
+    if (t >= L.T) continue;
+#pragma unroll
+    for (int s = 0; s < bf::kNS; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = (rg0 + s) * 16 + 4 * g + i;
+        if (e < E) L.logits[size_t(t) * E + e] = acc[s][u][i] + (L.rbias ? L.rbias[e] : 0.0f);
+      }
+    }
+  }
+}
+
+// Prefill shared gate/up: (shared expert, 128 rows of I, 64 tokens); wave w
+// takes row groups 2 w, 2 w + 1 of gate and up.  h = SiLU(g) * u leaves as
+// bf16 hi + lo, as on the decode path.
+__device__ void shared_gu_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int n_rt = (L.I + 127) / 128, n_tt = (L.T + bf::kTok - 1) / bf::kTok;
+  int pair, tt;
+  if (!xcd_split(b, L.S * n_rt, n_tt, pair, tt)) return;
+  const int sx = pair / n_rt, rt = pair % n_rt;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const int nu = H / 32, ngroups = I / 16;
+  const int rg0 = rt * 8 + 2 * wave;
+  const int t0 = tt * bf::kTok;
+  const uint16_t* mats[2] = {L.sgate + size_t(sx) * I * H, L.sup + size_t(sx) * I * H};
+  bf::f32x4 acc[bf::kNS][bf::kSub];
+  bf::gemm_tile<1>(
+      acc,
+      [&](int s, int kt) {
+        const int rg = min(rg0 + (s & 1), ngroups - 1);
+        return mats[s >> 1] + (size_t(rg) * nu + min(kt, nu - 1)) * 512 + 8 * lane;
+      },
+      H, lds, [&](int, int j) { return L.x + size_t(min(t0 + j, L.T - 1)) * H; });
+  if (rg0 >= ngroups) return;
+  const size_t plane = size_t(L.S) * L.T * I;
+#pragma unroll
+  for (int u = 0; u < bf::kSub; ++u) {
+    const int t = t0 + 16 * u + c;
+    if (t >= L.T) continue;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      uint32_t hi[2] = {0, 0}, lo[2] = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint16_t h16, l16;
+        split_bf16(silu(acc[r][u][i]) * acc[2 + r][u][i], h16, l16);
+        hi[i / 2] |= uint32_t(h16) << (16 * (i % 2));
+        lo[i / 2] |= uint32_t(l16) << (16 * (i % 2));
+      }
+      const size_t o = (size_t(sx) * L.T + t) * I + (rg0 + r) * 16 + 4 * g;
+      *reinterpret_cast<u32x2*>(L.hs + o) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(L.hs + plane + o) = u32x2{lo[0], lo[1]};
+    }
+  }
+}
+
+// Prefill shared down: (shared expert, 256 rows of H, 64 tokens); h enters
+// as its bf16 hi and lo parts (two token sources).
+__device__ void shared_down_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int n_rt = (L.H + 255) / 256, n_tt = (L.T + bf::kTok - 1) / bf::kTok;
+  int pair, tt;
+  if (!xcd_split(b, L.S * n_rt, n_tt, pair, tt)) return;
+  const int sx = pair / n_rt, rt = pair % n_rt;
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, I = L.I;
+  const int nu = I / 32, ngroups = H / 16;
+  const int rg0 = rt * 16 + 4 * wave;
+  const int t0 = tt * bf::kTok;
+  const uint16_t* dm = L.sdown + size_t(sx) * H * I;
+  const size_t plane = size_t(L.S) * L.T * I;
+  bf::f32x4 acc[bf::kNS][bf::kSub];
+  bf::gemm_tile<2>(
+      acc,
+      [&](int s, int kt) {
+        const int rg = min(rg0 + s, ngroups - 1);
+        return dm + (size_t(rg) * nu + min(kt, nu - 1)) * 512 + 8 * lane;
+      },
+      I, lds, [&](int src, int j) {
+        return L.hs + src * plane + (size_t(sx) * L.T + min(t0 + j, L.T - 1)) * I;
+      });
+#pragma unroll
+  for (int u = 0; u < bf::kSub; ++u) {
+    const int t = t0 + 16 * u + c;
+    if (t >= L.T) continue;
+#pragma unroll
+    for (int s = 0; s < bf::kNS; ++s) {
+      if (rg0 + s >= ngroups) continue;
+      *reinterpret_cast<bf::f32x4*>(L.ysh + (size_t(sx) * L.T + t) * H + (rg0 + s) * 16 + 4 * g) =
+          acc[s][u];
+    }
+  }
+}
 
 // ------------------------------------------------------------------------
 // Prefill roles.
@@ -619,6 +760,14 @@ __device__ void quant_x_role(const GemvLayer& L, int b) {
 struct MxTile {
   int a, p0, mt;
 };
+
+// The tile's pair ids (clamped to its last pair) in LDS, so the per-step
+// staging addresses come from LDS: a global load there would make every
+// staging pass wait for all outstanding loads, the weight prefetch included.
+__device__ __forceinline__ void load_tile_pairs(const GemvLayer& L, const MxTile& tt, int* lp) {
+  if (threadIdx.x < mx::kTok) lp[threadIdx.x] = L.plan.pairs[tt.p0 + min(int(threadIdx.x), tt.mt - 1)];
+  __syncthreads();
+}
 __device__ __forceinline__ bool mx_tile(const GemvLayer& L, int ti, MxTile& t) {
   if (ti >= L.plan.n_mtiles[0]) return false;
   const int packed = L.plan.mtiles[ti];
@@ -655,9 +804,9 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
     st.codes[s] = base[s >> 1] + size_t(rg) * pm.nkb * 1024 + 16 * lane;
     st.scl[s] = base[s >> 1] + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
   }
-  const int* pairs = L.plan.pairs + tt.p0;
-  const int last = tt.mt - 1;
-  auto tok = [&](int j) { return pairs[min(j, last)] / L.k; };
+  __shared__ int pairs[mx::kTok];
+  load_tile_pairs(L, tt, pairs);
+  auto tok = [&](int j) { return pairs[j] / L.k; };
   mx::f32x4 acc[mx::kNS][mx::kSub];
   mx::gemm_tile(
       acc, st, pm.nkb4 / 4, lds, [&](int j) { return L.xq + size_t(tok(j)) * L.Kq; },
@@ -729,13 +878,12 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
     st.codes[s] = base + size_t(rg) * pd.nkb * 1024 + 16 * lane;
     st.scl[s] = base + pd.code_bytes + (size_t(rg) * 64 + lane) * pd.nkb4;
   }
-  const int* pairs = L.plan.pairs + tt.p0;
-  const int last = tt.mt - 1;
+  __shared__ int pairs[mx::kTok];
+  load_tile_pairs(L, tt, pairs);
   mx::f32x4 acc[mx::kNS][mx::kSub];
   mx::gemm_tile(
-      acc, st, pd.nkb4 / 4, lds,
-      [&](int j) { return L.hq + size_t(pairs[min(j, last)]) * L.Iq; },
-      [&](int j) { return L.hs8 + size_t(pairs[min(j, last)]) * (L.Iq / 32); });
+      acc, st, pd.nkb4 / 4, lds, [&](int j) { return L.hq + size_t(pairs[j]) * L.Iq; },
+      [&](int j) { return L.hs8 + size_t(pairs[j]) * (L.Iq / 32); });
 #pragma unroll
   for (int u = 0; u < mx::kSub; ++u) {
     const int j = 16 * u + c;
@@ -877,6 +1025,27 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     }
     b -= st.n_comb;
   }
+  if constexpr ((R & kRoleRouterMx) != 0) {
+    if (b < st.n_rmx) {
+      router_mx_role(L, b, reinterpret_cast<uint8_t*>(lds_raw));
+      return;
+    }
+    b -= st.n_rmx;
+  }
+  if constexpr ((R & kRoleSharedGUMx) != 0) {
+    if (b < st.n_sgmx) {
+      shared_gu_mx_role(L, b, reinterpret_cast<uint8_t*>(lds_raw));
+      return;
+    }
+    b -= st.n_sgmx;
+  }
+  if constexpr ((R & kRoleSharedDownMx) != 0) {
+    if (b < st.n_sdmx) {
+      shared_down_mx_role(L, b, reinterpret_cast<uint8_t*>(lds_raw));
+      return;
+    }
+    b -= st.n_sdmx;
+  }
   const int gu_tiles = L.I / 32;
   if constexpr ((R & kRoleSharedGU) != 0) {
     if (b < st.n_sgu) {
@@ -924,11 +1093,14 @@ __global__ __launch_bounds__(kThreads) void moe_routed_down_combine(GemvLayer L,
 __global__ __launch_bounds__(kThreads) void moe_plan_quant_shared_gateup(GemvLayer L, Stage st) {
   stage_body<kRolePlan | kRoleQuantX | kRoleSharedGU, 0>(L, st);
 }
-__global__ __launch_bounds__(kThreads) void moe_mx_gateup_shared_down(GemvLayer L, Stage st) {
-  stage_body<kRoleMxGateUp | kRoleSharedDown, 0>(L, st);
+__global__ __launch_bounds__(kThreads) void moe_router_mx_quant(GemvLayer L, Stage st) {
+  stage_body<kRoleQuantX | kRoleRouterMx, 0>(L, st);
+}
+__global__ __launch_bounds__(kThreads) void moe_mx_gateup(GemvLayer L, Stage st) {
+  stage_body<kRoleMxGateUp | kRoleSharedGUMx, 0>(L, st);
 }
 __global__ __launch_bounds__(kThreads) void moe_mx_down(GemvLayer L, Stage st) {
-  stage_body<kRoleMxDown, 0>(L, st);
+  stage_body<kRoleMxDown | kRoleSharedDownMx, 0>(L, st);
 }
 __global__ __launch_bounds__(kThreads) void moe_combine(GemvLayer L, Stage st) {
   stage_body<kRoleCombine, 0>(L, st);
@@ -954,8 +1126,11 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   if (st.n_sgu > 0 || st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
   if (st.n_sdn > 0 || st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
   if (st.n_mgu > 0 || st.n_mdn > 0) lds = max(lds, size_t(2 * mx::kStageBytes));
+  if (st.n_rmx > 0 || st.n_sgmx > 0) lds = max(lds, size_t(2 * bf::kStageBytes));
+  if (st.n_sdmx > 0) lds = max(lds, size_t(4 * bf::kStageBytes));
   const int wgs = st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu +
-                  st.n_rdn + st.n_xq + st.n_mgu + st.n_mdn + st.n_comb;
+                  st.n_rdn + st.n_xq + st.n_mgu + st.n_mdn + st.n_comb + st.n_rmx + st.n_sgmx +
+                  st.n_sdmx;
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs), block(kThreads);
   switch (kind) {
@@ -984,8 +1159,11 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
     case StageKind::PlanQuantSharedGateUp:
       hipLaunchKernelGGL(moe_plan_quant_shared_gateup, grid, block, lds, stream, L, st);
       break;
-    case StageKind::MxGateUpSharedDown:
-      hipLaunchKernelGGL(moe_mx_gateup_shared_down, grid, block, lds, stream, L, st);
+    case StageKind::RouterMxQuant:
+      hipLaunchKernelGGL(moe_router_mx_quant, grid, block, lds, stream, L, st);
+      break;
+    case StageKind::MxGateUp:
+      hipLaunchKernelGGL(moe_mx_gateup, grid, block, lds, stream, L, st);
       break;
     case StageKind::MxDown:
       hipLaunchKernelGGL(moe_mx_down, grid, block, lds, stream, L, st);
