@@ -34,7 +34,10 @@ MAT_BYTES = 7168 * 1536 // 2 + 7168 * 1536 // 32   # one MXFP4 matrix: 5,849,088
 REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
 SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 # kernels of one moe_layer call, in launch order (see moe_profile_events)
-KERNELS = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
+KERNELS_GEMV = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
+KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4
 
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
@@ -45,14 +48,17 @@ CONFIGS = {
                 desc="K3 MoE layer batched decode, 64 tokens"),
     "stack12": dict(tokens=8, layers=12, replicas=1,
                     desc="12 stacked K3 MoE layers (RMSNorm -> MoE -> residual), batch 8"),
+    "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
+                    desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
+                         "MXFP8 activations on block-scaled MFMA"),
 }
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=None, help="default 200 (prefill 20)")
+    p.add_argument("--warmup", type=int, default=None, help="default 20 (prefill 3)")
     p.add_argument("--config", default="b1", choices=sorted(CONFIGS))
     p.add_argument("--replicas", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -86,7 +92,33 @@ def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
         return D * 2 * MAT_BYTES + x + T * k * I * 4
     if name == "routed_down_combine":
         return D * MAT_BYTES + T * k * I * 4 + T * k * 4 + S * T * H * 4 + x
+    # prefill (MFMA) path; MXFP8 rows are padded to multiples of 512 (exact at K3)
+    xq = T * H * (1 + 1 / 32)
+    hq = T * k * I * (1 + 1 / 32)
+    if name == "router_quant":
+        return E * H * 2 + x + xq + T * E * 4 + E * 4
+    if name == "select_plan":
+        return T * E * 4 + T * k * 8 + T * k * 4 * 2 + E * 8
+    if name == "mx_gateup":
+        return D * 2 * MAT_BYTES + S * 2 * SHARED_MAT_BYTES + xq + x + hq + S * T * I * 4
+    if name == "mx_down":
+        return D * MAT_BYTES + S * SHARED_MAT_BYTES + hq + S * T * I * 4 + T * k * H * 4 + S * T * H * 4
+    if name == "combine":
+        return T * k * H * 4 + T * k * 4 + S * T * H * 4 + T * H * 2
     raise KeyError(name)
+
+
+def mfma_flops(name, T, k, S, H=7168, I=1536, E=896):
+    """Matrix-core FLOPs of a prefill launch (routed on the scaled FP4 x FP8
+    MFMA, shared experts and router on bf16; the shared down counts its hi
+    and lo halves)."""
+    if name == "mx_gateup":
+        return 2 * 2 * T * k * H * I, 2 * 2 * S * T * H * I
+    if name == "mx_down":
+        return 2 * T * k * H * I, 2 * 2 * S * T * H * I
+    if name == "router_quant":
+        return 0, 2 * T * E * H
+    return 0, 0
 
 
 def cpu_baseline(cfg_name, n_tokens):
@@ -101,15 +133,19 @@ def cpu_baseline(cfg_name, n_tokens):
         threads = 1
     c = synth.K3
     H, I = c["hidden"], c["inter"]
+    cfg = CONFIGS[cfg_name]
+    mx = cfg.get("path") == "mfma"
+    bias = synth.router_bias(0, 0, c["n_experts"]) if cfg.get("bias") else None
     layer = M.Layer(H, I, c["n_experts"], c["top_k"], synth.router_weight(0, 0, c["n_experts"], H),
                     expert_record=lambda e: synth.expert_record(0, 0, e, H, I),
-                    shared=[synth.shared_expert(0, 0, s, H, I) for s in range(c["n_shared"])])
-    n_layers = CONFIGS[cfg_name]["layers"]
+                    shared=[synth.shared_expert(0, 0, s, H, I) for s in range(c["n_shared"])],
+                    router_bias=bias)
+    n_layers = cfg["layers"]
     t0 = time.perf_counter()
     done = 0
     for i in range(n_tokens):
         # one token of the workload's input through one layer (route + experts)
-        M.moe_layer(synth.activations(1000 + i, 1, H), layer)
+        M.moe_layer(synth.activations(1000 + i, 1, H), layer, act_mxfp8=mx)
         done += 1
         if time.perf_counter() - t0 > 30:
             break
@@ -118,7 +154,8 @@ def cpu_baseline(cfg_name, n_tokens):
     return {"value": round(done / dt / n_layers, 6), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} single-token layer call(s) of {cfg_name} through the float64 numpy "
-                      f"oracle (router + 16 experts dequantised and applied + 2 shared"
+                      f"oracle ({'MXFP8 activations, logit bias, ' if mx else ''}"
+                      f"router + 16 experts dequantised and applied + 2 shared"
                       f"{', scaled by 1/%d layers' % n_layers if n_layers > 1 else ''}), "
                       f"{dt:.1f} s; BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
 
@@ -138,6 +175,13 @@ def main():
 
     cfgd = CONFIGS[args.config]
     T, n_layers = cfgd["tokens"], cfgd["layers"]
+    if args.steps is None:
+        args.steps = cfgd.get("steps", 200)
+    if args.warmup is None:
+        args.warmup = cfgd.get("warmup", 20)
+    mfma = cfgd.get("path") == "mfma"
+    path = b.PATH_MFMA if mfma else b.PATH_GEMV
+    KERNELS = KERNELS_MFMA if mfma else KERNELS_GEMV
     replicas = args.replicas or cfgd["replicas"]
     c = synth.K3
     H, I, E, k, S = c["hidden"], c["inter"], c["n_experts"], c["top_k"], c["n_shared"]
@@ -149,9 +193,9 @@ def main():
     layers, keep = [], []
     n_distinct = n_layers
     for l in range(n_distinct):
-        d = SD.upload_layer(c, seed=0, layer=l)
+        d = SD.upload_layer(c, seed=0, layer=l, bias=bool(cfgd.get("bias")))
         L = b.Layer.from_canonical(H, I, E, k, d["router_w"], d["experts"], d["shared_gate"],
-                                   d["shared_up"], d["shared_down"])
+                                   d["shared_up"], d["shared_down"], d["router_bias"])
         del d  # canonical copies are not needed once packed
         keep.append(L)
         layers.append(L)
@@ -180,13 +224,13 @@ def main():
     def step(i):
         if n_layers == 1:
             L = layers[i % len(layers)]
-            b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=b.PATH_GEMV)
+            b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=path)
         else:
             cur = xs[i]
             for l in range(n_layers):
                 b.rmsnorm(cur, gammas[l], 1e-6, normed)
                 b.moe_layer(layers[l], normed, y[l + 1], ids[i, l], wts[i, l], ws,
-                            residual=cur, path=b.PATH_GEMV)
+                            residual=cur, path=path)
                 cur = y[l + 1]
 
     for i in range(args.warmup):
@@ -222,7 +266,7 @@ def main():
     prof_steps = min(args.steps, 100)
     for i in range(args.warmup, args.warmup + prof_steps):
         L = layers[i % len(layers)]
-        b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=b.PATH_GEMV)
+        b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=path)
         cnt = b.profile_count()
         torch.cuda.synchronize()
         for j, name in enumerate(KERNELS[:cnt - 1]):
@@ -231,6 +275,13 @@ def main():
     b.profile_events(None, 0)
     kern_us = {n: float(np.mean(v)) for n, v in per_kernel.items() if v}
     dom = max(kern_us, key=kern_us.get)
+    mfma_info = None
+    if mfma:
+        f8, f16 = mfma_flops(dom, T, k, S)
+        mfma_info = {"kernel": dom, "fp4xfp8_tflops": round(f8 / (kern_us[dom] * 1e-6) / 1e12, 1),
+                     "frac_of_fp8_peak": round(f8 / (kern_us[dom] * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                     "frac_of_fp4_peak": round(f8 / (kern_us[dom] * 1e-6) / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4),
+                     "bf16_tflops_same_launch": round(f16 / (kern_us[dom] * 1e-6) / 1e12, 1)}
     D0 = D[:prof_steps, 0]
     dom_bytes = float(np.mean([kernel_bytes(dom, T, k, d, S) for d in D0]))
     achieved = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
@@ -261,10 +312,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*bf16->f32",
-        "data": "synthetic (seeded; codes uniform, E8M0 118..126, N(0,0.02) bf16 router/shared, N(0,1) tokens)",
+        "dtype": "mxfp4*mxfp8->f32" if mfma else "mxfp4*bf16->f32",
+        "data": "synthetic (seeded; codes uniform, E8M0 118..126, N(0,0.02) bf16 router/shared, N(0,1) tokens"
+                + (", logit bias N(0,0.5))" if cfgd.get("bias") else ")"),
         "config": {"workload": cfgd["desc"], "tokens_per_step": T, "layers": n_layers,
-                   "resident_copies": len(layers), "path": "gemv"},
+                   "resident_copies": len(layers), "path": "mfma" if mfma else "gemv"},
         "expert_weight_gbs": round(float(exp_gbs), 1),
         "expert_weight_hbm_frac": round(float(exp_gbs) / HBM_PEAK_GBS, 4),
         "distinct_experts_mean": round(float(D.mean()), 2),
@@ -274,6 +326,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": round(dom_bytes)},
     }
+    if mfma_info is not None:
+        out["mfma"] = mfma_info
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)
