@@ -125,20 +125,29 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, int stride, int mt, in
 }
 
 // Stage packed h rows (uint32: bf16 hi in the low half, lo in the high
-// half) into separate hi and lo LDS rows (zero-filled from K to Kp).
+// half) of mt tokens into LDS as interleaved bf16 rows: row 2 j = hi and row
+// 2 j + 1 = lo of token j (zero-filled from K to Kp).  As B columns of one
+// MFMA, hi and lo of a token are then multiplied by the same weights in one
+// instruction; hi_sum() adds the two columns afterwards.
 template <typename Src>
-__device__ __forceinline__ void stage_h(uint16_t* hi, uint16_t* lo, int stride, int mt, int K,
-                                        int Kp, Src src) {
+__device__ __forceinline__ void stage_h(uint16_t* dst, int stride, int mt, int K, int Kp,
+                                        Src src) {
   const int nch = Kp / 4;
   for (int i = threadIdx.x; i < mt * nch; i += kThreads) {
     const int j = i / nch, q = i % nch;
     const u32x4 v = q * 4 < K ? ld16(src(j) + q * 4) : u32x4{0, 0, 0, 0};
     const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
-    *reinterpret_cast<u32x2*>(hi + j * stride + q * 4) =
+    *reinterpret_cast<u32x2*>(dst + (2 * j) * stride + q * 4) =
         u32x2{(w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16)};
-    *reinterpret_cast<u32x2*>(lo + j * stride + q * 4) =
+    *reinterpret_cast<u32x2*>(dst + (2 * j + 1) * stride + q * 4) =
         u32x2{(w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u)};
   }
+}
+
+// Sum of the MFMA result columns c and c ^ 1 (a token's hi and lo parts),
+// valid in the even lane of each pair.
+__device__ __forceinline__ float hi_lo_sum(float v) {
+  return v + __uint_as_float(dpp_or_zero<0xB1, 0xF>(__float_as_uint(v)));  // quad_perm [1,0,3,2]
 }
 
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) {
@@ -174,6 +183,40 @@ __device__ __forceinline__ void pipeline2(int s0, int s1, Buf& a, Buf& b, Load l
     comp(b, s + 1);
   } else if (s < s1) {
     comp(a, s);
+  }
+}
+
+// D-stage version: a ring of D register buffers, loads issued D - 1 steps
+// ahead of the step being computed.  The caller has issued nothing; the
+// prologue loads the first D - 1 steps.  Steady-state loads are
+// unconditional for the same reason as in pipeline2.  mid() runs after the
+// prologue's loads are issued (for work that overlaps them, e.g. staging).
+template <int D, typename Buf, typename Load, typename Mid, typename Comp>
+__device__ __forceinline__ void pipelineN(int s0, int s1, Buf (&b)[D], Load load, Mid mid,
+                                          Comp comp) {
+#pragma unroll
+  for (int d = 0; d < D - 1; ++d)
+    if (s0 + d < s1) load(b[d], s0 + d);
+  mid();
+  int s = s0;
+  for (; s + 2 * D - 1 <= s1; s += D) {  // all D prefetches of this round exist
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      load(b[(d + D - 1) % D], s + d + D - 1);
+      comp(b[d], s + d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {  // remaining < 2 D - 1 steps, conditions allowed
+    if (s + d >= s1) break;
+    if (s + d + D - 1 < s1) load(b[(d + D - 1) % D], s + d + D - 1);
+    comp(b[d], s + d);
+  }
+  s += D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (s + d >= s1) break;
+    comp(b[d], s + d);
   }
 }
 
@@ -270,10 +313,14 @@ __device__ __forceinline__ void join_halves(f32x4_t& a, f32x4_t& b, float* red) 
 }
 
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
-  if (a >= L.plan.n_active[0]) return;
+  // all four plan reads at once (in bounds for any a < E); the slot is
+  // checked after they land, so the expert's first weight loads wait for one
+  // round trip, not two
+  const int na = L.plan.n_active[0];
   const int e = L.plan.active[a];
   const int p0 = L.plan.act_off[a];
   const int p1 = L.plan.act_off[a + 1];
+  if (a >= na) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -398,18 +445,20 @@ struct DnTiles {
   uint32_t sc;
 };
 
+// Routed down waves stream 4 row groups x 3 super-steps of 4 KiB with about
+// 1.75 waves per SIMD; four stages keep 12 KiB per wave in flight.
+constexpr int kDownStages = 4;
+
 // Routed down: workgroup = (expert, tile of kRowsD rows); wave w takes the
 // tile's row groups 4 w .. 4 w + 3 one after the other as one continuous
 // pipeline of (row group, super-step) steps, so its loads never drain
 // between row groups; a row group's partials are stored after its last
 // super-step.
-__device__ void routed_down(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
+__device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, int tile,
+                            uint16_t* hsm) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
-  const int e = L.plan.active[a];
-  const int p0 = L.plan.act_off[a];
-  const int p1 = L.plan.act_off[a + 1];
   const int H = L.H, I = L.I;
   const PackedMx pgu(I, H), pd(H, I);
   const int nkq = pd.nkb4 / 4;
@@ -421,8 +470,6 @@ __device__ void routed_down(const GemvLayer& L, int a, int tile, uint16_t* hsm) 
   const uint8_t* codes = base + size_t(rg0) * pd.nkb * 1024 + 16 * lane;
   const uint8_t* scl = base + pd.code_bytes + (size_t(rg0) * 64 + lane) * pd.nkb4;
   const int hstride = pad_k(I) + 8;
-  uint16_t* hs_hi = hsm;
-  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
   auto load = [&](DnTiles& t, int s) {
     const int r = s / nkq, kq = s - r * nkq;
     const uint8_t* cr = codes + size_t(r) * pd.nkb * 1024;
@@ -434,34 +481,35 @@ __device__ void routed_down(const GemvLayer& L, int a, int tile, uint16_t* hsm) 
 
   for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
     const int mt = min(L.mtp_d, p1 - t0);
-    DnTiles ta, tb;
-    if (nsteps > 0) load(ta, 0);
-    __syncthreads();
-    stage_h(hs_hi, hs_lo, hstride, mt, I, pad_k(I),
-            [&](int j) { return L.h + size_t(L.plan.pairs[t0 + j]) * I; });
-    __syncthreads();
-    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
-    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
-    const int pair = L.plan.pairs[t0 + (c < mt ? c : 0)];
+    DnTiles bufs[kDownStages];
+    const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;  // column c: token c / 2, hi / lo
+    const int tok = c / 2;
+    const int pair = L.plan.pairs[t0 + (tok < mt ? tok : 0)];
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    pipeline2(0, nsteps, ta, tb, load, [&](const DnTiles& t, int s) {
+    auto stage = [&]() {
+      __syncthreads();
+      stage_h(hsm, hstride, mt, I, pad_k(I),
+              [&](int j) { return L.h + size_t(L.plan.pairs[t0 + j]) * I; });
+      __syncthreads();
+    };
+    pipelineN<kDownStages>(0, nsteps, bufs, load, stage, [&](const DnTiles& t, int s) {
       const int r = s / nkq, kq = s - r * nkq;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int bi = 16 * kq + 4 * j + g;
         const float sd = e8m0_to_f32((t.sc >> (8 * j)) & 0xFFu);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 aw = fp4x8_scaled(t.w[j][q], sd);
-          acc = mfma(aw, lds16(bh + bi * 32 + 8 * q), acc);
-          acc = mfma(aw, lds16(bl + bi * 32 + 8 * q), acc);
-        }
+        for (int q = 0; q < 4; ++q)
+          acc = mfma(fp4x8_scaled(t.w[j][q], sd), lds16(bh + bi * 32 + 8 * q), acc);
       }
       if (kq == nkq - 1) {  // row group rg0 + r complete
-        if (c < mt) {
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
+        if ((c & 1) == 0 && tok < mt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            store_coherent(&L.part[size_t(pair) * H + (rg0 + r) * 16 + 4 * g + i], acc[i]);
+            store_coherent(&L.part[size_t(pair) * H + (rg0 + r) * 16 + 4 * g + i], y[i]);
         }
         acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -480,8 +528,6 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm)
   const int nq = (nu + 3) / 4;
   const uint16_t* dt = L.sdown + sx * (size_t(H) * I) + size_t(live ? rg : 0) * nu * 512;
   const int hstride = pad_k(I) + 8;
-  uint16_t* hs_hi = hsm;
-  uint16_t* hs_lo = hsm + L.mtp_d * hstride;
   const size_t plane = size_t(L.S) * L.T * I;
   struct Bf16Tile4 {
     u32x4 w[4];
@@ -498,29 +544,26 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm)
     Bf16Tile4 ta, tb;
     if (live) load(ta, 0);
     __syncthreads();
-    stage_rows(hs_hi, hstride, mt, I, pad_k(I),
+    // interleaved rows: 2 j = hi, 2 j + 1 = lo of token j (see stage_h)
+    stage_rows(hsm, 2 * hstride, mt, I, pad_k(I),
                [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
-    stage_rows(hs_lo, hstride, mt, I, pad_k(I),
+    stage_rows(hsm + hstride, 2 * hstride, mt, I, pad_k(I),
                [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
     __syncthreads();
     if (!live) continue;
-    const uint16_t* bh = hs_hi + (c < mt ? c : 0) * hstride;
-    const uint16_t* bl = hs_lo + (c < mt ? c : 0) * hstride;
+    const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     pipeline2(0, nq, ta, tb, load, [&](const Bf16Tile4& t, int q) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u = 4 * q + j;
-        const u32x4 vh = lds16(bh + u * 32 + 8 * g);
-        const u32x4 vl = lds16(bl + u * 32 + 8 * g);
-        acc = mfma(t.w[j], vh, acc);
-        acc = mfma(t.w[j], vl, acc);
-      }
+      for (int j = 0; j < 4; ++j) acc = mfma(t.w[j], lds16(bh + (4 * q + j) * 32 + 8 * g), acc);
     });
-    if (c < mt) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
+    if ((c & 1) == 0 && c / 2 < mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        L.ysh[(size_t(sx) * L.T + t0 + c) * H + rg * 16 + 4 * g + i] = acc[i];
+        L.ysh[(size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g + i] = y[i];
     }
   }
 }
@@ -960,9 +1003,12 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
 }
 
 __device__ void routed_down_role(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
-  const int n_active = L.plan.n_active[0];
+  const int n_active = L.plan.n_active[0];  // plan reads issued together (see routed_gateup)
+  const int e = L.plan.active[a];
+  const int p0 = L.plan.act_off[a];
+  const int p1 = L.plan.act_off[a + 1];
   if (a >= n_active) return;  // slot beyond this routing's experts
-  routed_down(L, a, tile, hsm);
+  routed_down(L, a, e, p0, p1, tile, hsm);
   if (arrive_last(&L.tile_cnt[tile], n_active)) combine_tile(L, tile);
 }
 
@@ -1120,7 +1166,7 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   L.n_stiles = (L.H + kRowsSD - 1) / kRowsSD;
   const int xrow = pad_k(L.H) + 8, hrow = pad_k(L.I) + 8;  // staged row lengths
   L.mtp_gu = tokens_per_pass(L.T, xrow * 2);
-  L.mtp_d = tokens_per_pass(L.T, hrow * 4);
+  L.mtp_d = min(tokens_per_pass(L.T, hrow * 4), kCols / 2);  // hi + lo: two B columns per token
   size_t lds = 0;
   if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
   if (st.n_sgu > 0 || st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
