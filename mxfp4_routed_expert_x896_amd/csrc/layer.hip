@@ -986,16 +986,32 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int t = b * 4 + wave;
+  // With one top-k workgroup (T <= 4) it builds the plan straight from its
+  // own selections in LDS: no arrival count, and no round trips through the
+  // coherent level for the ids it has just computed.
+  const bool single = st.n_select == 1;
+  __shared__ int own_ids[4 * 32];
   if (t < L.T) {
     int id;
     float w;
     select_token(L.logits + size_t(t) * L.E, L.E, L.k, id, w);
     if (lane < L.k) {
-      store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
-      store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
+      if (single) {
+        L.ids_out[size_t(t) * L.k + lane] = id;
+        L.w_out[size_t(t) * L.k + lane] = w;
+        own_ids[t * L.k + lane] = id;
+      } else {
+        store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
+        store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
+      }
     }
   }
   if (!st.plan_after_select) return;
+  if (single) {
+    __syncthreads();
+    build_plan([&](int p) { return own_ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt, L.n_tiles);
+    return;
+  }
   if (!arrive_last(L.sel_cnt, st.n_select)) return;
   const int32_t* ids = L.ids_out;
   build_plan([&](int p) { return load_coherent(ids + p); }, L.T * L.k, L.E, L.plan, L.tile_cnt,
