@@ -235,6 +235,7 @@ int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const
                     hipStream_t stream) {
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
   G.ids_in = ids;
+  G.direct = T == 1;
   G.w = w;
   G.residual = residual;
   G.y = y;
@@ -260,6 +261,8 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                   hipStream_t stream) {
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
   G.ids_out = ids;
+  G.ids_in = ids;  // read back by the routed launches in direct mode
+  G.direct = T == 1;
   G.w_out = w;
   G.w = w;
   G.residual = residual;

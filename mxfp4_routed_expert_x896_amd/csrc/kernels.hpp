@@ -18,7 +18,8 @@ struct GemvLayer {
   const uint16_t* wr;       // bf16 [E][H] router weights
   const float* rbias;       // fp32 [E] router bias or null
   float* logits;            // fp32 [T][E]
-  const int32_t* ids_in;    // int32 [T][k] routing given by the caller (plan role)
+  const int32_t* ids_in;    // int32 [T][k] routing given by the caller (plan role), or
+                            // written by the top-k role of an earlier launch (direct mode)
   int32_t* ids_out;         // int32 [T][k] routing written by the top-k role
   float* w_out;             // fp32 [T][k] weights written by the top-k role
   int* sel_cnt;             // [1] arrivals of top-k workgroups (zeroed by the logits launch)
@@ -28,10 +29,14 @@ struct GemvLayer {
   const uint16_t* sup;      // bf16 [S] packed [I][H]
   const uint16_t* sdown;    // bf16 [S] packed [H][I]
   Plan plan;
+  // Direct mode (one token): expert slot a is pair a, its expert ids_in[a];
+  // no plan is built (the k experts of one token are distinct).
+  int direct;
   int n_tiles;              // ceil(H / kDownRows) routed down tiles (set by the launcher)
   int n_stiles;             // ceil(H / 64) shared down tiles (set by the launcher)
   int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launcher)
-  uint32_t* h;              // [T*k][I] routed SiLU(g)*u per pair: bf16 hi | bf16 lo << 16
+  uint32_t* h;              // [T*k][I] routed SiLU(g)*u in plan slot order (row p for
+                            // pairs[p]): bf16 hi | bf16 lo << 16
   uint16_t* hs;             // bf16 [2][S][T][I] shared SiLU(g)*u, hi and lo parts
   float* part;              // fp32 [T*k][H]   routed expert outputs per pair
   float* ysh;               // fp32 [S][T][H]  shared expert outputs

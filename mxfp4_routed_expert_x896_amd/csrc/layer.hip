@@ -312,14 +312,33 @@ __device__ __forceinline__ void join_halves(f32x4_t& a, f32x4_t& b, float* red) 
   }
 }
 
+// Expert slot a of the routed launches: the number of live slots, its
+// expert and its plan positions [p0, p1).  The plan reads are issued
+// together (all in bounds for any a < E) and the slot is checked after they
+// land, so the expert's first weight loads wait for one round trip.
+__device__ __forceinline__ void slot_of(const GemvLayer& L, int a, int& n, int& e, int& p0,
+                                        int& p1) {
+  if (L.direct) {
+    n = L.T * L.k;
+    e = min(max(L.ids_in[min(a, n - 1)], 0), L.E - 1);  // clamped like the plan's ids
+    p0 = a;
+    p1 = a + 1;
+    return;
+  }
+  n = L.plan.n_active[0];
+  e = L.plan.active[a];
+  p0 = L.plan.act_off[a];
+  p1 = L.plan.act_off[a + 1];
+}
+
+// Pair (token * k + slot) at plan position p.
+__device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
+  return L.direct ? p : L.plan.pairs[p];
+}
+
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
-  // all four plan reads at once (in bounds for any a < E); the slot is
-  // checked after they land, so the expert's first weight loads wait for one
-  // round trip, not two
-  const int na = L.plan.n_active[0];
-  const int e = L.plan.active[a];
-  const int p0 = L.plan.act_off[a];
-  const int p1 = L.plan.act_off[a + 1];
+  int na, e, p0, p1;
+  slot_of(L, a, na, e, p0, p1);
   if (a >= na) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -345,7 +364,7 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
     if (kq0 < kq1) load(ta, kq0);
     __syncthreads();
     stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) {
-      return L.x + size_t(min(L.plan.pairs[t0 + j] / L.k, L.T - 1)) * H;
+      return L.x + size_t(min(pair_at(L, t0 + j) / L.k, L.T - 1)) * H;
     });
     __syncthreads();
     const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
@@ -354,7 +373,6 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
               [&](const GuTiles& t, int kq) { mma_gu(t, xrow, kq, g, ag, au); });
     join_halves(ag, au, red);
     if (!(wave & 1) && c < mt) {
-      const int pair = L.plan.pairs[t0 + c];
       uint32_t hv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -362,7 +380,7 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
         split_bf16(silu(ag[i]) * au[i], hi, lo);
         hv[i] = uint32_t(hi) | (uint32_t(lo) << 16);
       }
-      *reinterpret_cast<u32x4*>(L.h + size_t(pair) * I + rg * 16 + 4 * g) =
+      *reinterpret_cast<u32x4*>(L.h + size_t(t0 + c) * I + rg * 16 + 4 * g) =
           u32x4{hv[0], hv[1], hv[2], hv[3]};
     }
   }
@@ -484,12 +502,11 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
     DnTiles bufs[kDownStages];
     const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;  // column c: token c / 2, hi / lo
     const int tok = c / 2;
-    const int pair = L.plan.pairs[t0 + (tok < mt ? tok : 0)];
+    const int pair = pair_at(L, t0 + (tok < mt ? tok : 0));
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     auto stage = [&]() {
       __syncthreads();
-      stage_h(hsm, hstride, mt, I, pad_k(I),
-              [&](int j) { return L.h + size_t(L.plan.pairs[t0 + j]) * I; });
+      stage_h(hsm, hstride, mt, I, pad_k(I), [&](int j) { return L.h + size_t(t0 + j) * I; });
       __syncthreads();
     };
     pipelineN<kDownStages>(0, nsteps, bufs, load, stage, [&](const DnTiles& t, int s) {
@@ -991,10 +1008,11 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   // coherent level for the ids it has just computed.
   const bool single = st.n_select == 1;
   __shared__ int own_ids[4 * 32];
+  __shared__ SelectScratch sc[kWaves];
   if (t < L.T) {
     int id;
     float w;
-    select_token(L.logits + size_t(t) * L.E, L.E, L.k, id, w);
+    select_token(L.logits + size_t(t) * L.E, L.E, L.k, id, w, sc[wave]);
     if (lane < L.k) {
       if (single) {
         L.ids_out[size_t(t) * L.k + lane] = id;
@@ -1007,6 +1025,10 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
     }
   }
   if (!st.plan_after_select) return;
+  if (L.direct) {  // no plan: only the combine's arrival counters need clearing
+    for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
+    return;
+  }
   if (single) {
     __syncthreads();
     build_plan([&](int p) { return own_ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt, L.n_tiles);
@@ -1019,10 +1041,8 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
 }
 
 __device__ void routed_down_role(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
-  const int n_active = L.plan.n_active[0];  // plan reads issued together (see routed_gateup)
-  const int e = L.plan.active[a];
-  const int p0 = L.plan.act_off[a];
-  const int p1 = L.plan.act_off[a + 1];
+  int n_active, e, p0, p1;
+  slot_of(L, a, n_active, e, p0, p1);
   if (a >= n_active) return;  // slot beyond this routing's experts
   routed_down(L, a, e, p0, p1, tile, hsm);
   if (arrive_last(&L.tile_cnt[tile], n_active)) combine_tile(L, tile);
@@ -1052,6 +1072,10 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   }
   if constexpr ((R & kRolePlan) != 0) {
     if (b < st.n_plan) {
+      if (L.direct) {
+        for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
+        return;
+      }
       const int32_t* ids = L.ids_in;
       build_plan([&](int p) { return ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt,
                  L.n_tiles);

@@ -67,7 +67,7 @@ __device__ __forceinline__ void router_logits_rows(const uint16_t* __restrict__ 
 // Orderable 32-bit image of a float: a > b as floats iff ord(a) > ord(b) as
 // unsigned (finite values and infinities); never 0 for a finite value.
 __device__ __forceinline__ uint32_t ord_f32(float l) {
-  const uint32_t u = __float_as_uint(l);
+  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 ties with +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -92,19 +92,59 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 
+// Candidate keys a wave keeps in LDS during one token's top-k.
+constexpr int kSelCap = 256;
+
+// Per-wave LDS of select_token.
+struct alignas(16) SelectScratch {
+  uint32_t lmax[kWave];      // each lane's largest key
+  uint64_t cand[kSelCap];    // candidate (value, index) keys
+  uint64_t top[32];          // the selected keys by rank
+};
+
+// Orders this wave's LDS stores before its later LDS loads (a wave's LDS
+// accesses are carried out in program order; this keeps the compiler from
+// moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Exclusive prefix sum over the lanes of a count 0 <= v < 32, and the
+// total, from one ballot per bit.
+__device__ __forceinline__ int wave_prefix_small(int v, int& total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1);
+    const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+    pre += below << bit;
+    tot += __popcll(m) << bit;
+  }
+  total = tot;
+  return pre;
+}
+
 // Top-k (k <= 32) of one token's E <= 1024 logits by one wave (all 64 lanes
 // active): lane j < k receives the j-th selected expert (score descending,
 // ties to the lower expert index) in id and w = sigmoid(l) / sum over the
 // selected.  Selecting on the fp32 logit is the same order as on the
 // sigmoid score, without its saturation ties.
 //
-// Fast path: every lane keeps its 4 best (value, index) candidates sorted;
-// each round takes the wave-wide best head (32-bit DPP max, ties resolved
-// by the lowest index) and pops it from its lane.  If some lane runs out of
-// candidates before the last round, its fifth key might belong to the top-k:
-// the token is then redone exactly by k rounds over all 16 keys per lane.
+// Each key is the pair (ordered logit, inverted index), unique per expert,
+// so "larger key" is exactly the selection order.  Lane l holds experts
+// l + 64 i.  The k-th largest of the 64 per-lane maxima is a lower bound M
+// on the k-th largest logit (k lanes hold a value >= M), so every selected
+// expert has a logit >= M.  The experts at or above M (a few more than k
+// for any spread-out logits) are gathered in LDS and each one's rank among
+// them -- which equals its rank among all experts, since any larger key is
+// also at or above M -- is counted directly; ranks below k are the
+// selection.  If more than kSelCap experts reach M (heavy ties), the token
+// is redone exactly by k rounds of a wave-wide maximum over all keys.
 __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int E, int k,
-                                             int& id, float& w) {
+                                             int& id, float& w, SelectScratch& sc) {
   const int lane = threadIdx.x % kWave;
   uint32_t val[16];
 #pragma unroll
@@ -112,54 +152,51 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int
     const int e = lane + kWave * i;
     val[i] = e < E ? ord_f32(lrow[e]) : 0u;
   }
-  // per-lane sorted top 4; indices rise with i, so strict > keeps ties in
-  // index order
-  uint32_t cv[4] = {0u, 0u, 0u, 0u};
-  int ci[4] = {1 << 20, 1 << 20, 1 << 20, 1 << 20};
+  uint32_t mx = 0u;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t v = val[i];
-    const int e = lane + kWave * i;
-    const bool b0 = v > cv[0], b1 = v > cv[1], b2 = v > cv[2], b3 = v > cv[3];
-    cv[3] = b2 ? cv[2] : (b3 ? v : cv[3]);
-    ci[3] = b2 ? ci[2] : (b3 ? e : ci[3]);
-    cv[2] = b1 ? cv[1] : (b2 ? v : cv[2]);
-    ci[2] = b1 ? ci[1] : (b2 ? e : ci[2]);
-    cv[1] = b0 ? cv[0] : (b1 ? v : cv[1]);
-    ci[1] = b0 ? ci[0] : (b1 ? e : ci[1]);
-    cv[0] = b0 ? v : cv[0];
-    ci[0] = b0 ? e : ci[0];
+  for (int i = 0; i < 16; ++i) mx = val[i] > mx ? val[i] : mx;
+  sc.lmax[lane] = mx;
+  wave_lds_sync();
+  // number of lanes whose maximum is >= this lane's; the threshold is the
+  // largest maximum that at least k lanes reach
+  int ge = 0;
+#pragma unroll
+  for (int j = 0; j < kWave; j += 4) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(&sc.lmax[j]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ge += q[t] >= mx ? 1 : 0;
   }
+  const uint32_t M = wave_max_u32(ge >= k ? mx : 0u);
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) cnt += (lane + kWave * i < E && val[i] >= M) ? 1 : 0;
+  int total;
+  int off = wave_prefix_small(cnt, total);
   int my_id = 0;
   uint32_t my_val = 0;
-  int used = 0;
-  bool overflow = false;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t m = wave_max_u32(cv[0]);
-    const uint64_t tied = __ballot(cv[0] == m);
-    int win_lane, win_id;
-    if (__popcll(tied) == 1) {
-      win_lane = __ffsll((unsigned long long)tied) - 1;
-      win_id = __builtin_amdgcn_readlane(ci[0], win_lane);
-    } else {  // equal logits in several lanes: the lowest expert index wins
-      const uint32_t inv = cv[0] == m ? ~uint32_t(ci[0]) : 0u;
-      win_id = int(~wave_max_u32(inv));
-      win_lane = win_id % kWave;
+  const bool overflow = total > kSelCap;
+  if (!overflow) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E && val[i] >= M)
+        sc.cand[off++] = (uint64_t(val[i]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
     }
-    if (lane == j) {
-      my_id = win_id;
-      my_val = m;
+    wave_lds_sync();
+    for (int c = lane; c < total; c += kWave) {
+      const uint64_t key = sc.cand[c];
+      int r = 0;
+      for (int t = 0; t < total; ++t) r += sc.cand[t] > key ? 1 : 0;
+      if (r < k) sc.top[r] = key;
     }
-    if (lane == win_lane) {
-      cv[0] = cv[1], ci[0] = ci[1];
-      cv[1] = cv[2], ci[1] = ci[2];
-      cv[2] = cv[3], ci[2] = ci[3];
-      cv[3] = 0u, ci[3] = 1 << 20;
-      ++used;
-      if (used == 4 && j < k - 1) overflow = true;
+    wave_lds_sync();
+    if (lane < k) {
+      const uint64_t key = sc.top[lane];
+      my_val = uint32_t(key >> 32);
+      my_id = int(0xFFFFFFFFu - uint32_t(key));
     }
   }
-  if (__ballot(overflow) != 0) {
+  if (overflow) {
     // exact slow path: k rounds over all keys, 64-bit (value, ~index) keys
     uint64_t key[16];
 #pragma unroll
