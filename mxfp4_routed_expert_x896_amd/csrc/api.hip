@@ -261,8 +261,7 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                   hipStream_t stream) {
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
   G.ids_out = ids;
-  G.ids_in = ids;  // read back by the routed launches in direct mode
-  G.direct = T == 1;
+  G.ids_in = ids;  // read back by the routed down launch in direct mode
   G.w_out = w;
   G.w = w;
   G.residual = residual;
@@ -271,6 +270,21 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   moe::Stage s1;
   s1.n_logits = n_logit_wgs(L);
   s1.n_sgu = S * (L->inter / 16);
+  if (T == 1) {
+    // one token: no top-k launch; the routed gate/up workgroups select
+    // (direct mode), the shared down runs beside them
+    G.direct = 1;
+    G.select_inline = 1;
+    int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
+    if (st) return st;
+    moe::Stage s3;
+    s3.n_rgu = ma * tiles_gu;
+    s3.n_sdn = S * n_shared_tiles(L);
+    if ((st = stage(moe::StageKind::RoutedGateUp, G, s3, stream))) return st;
+    moe::Stage s4;
+    s4.n_rdn = ma * n_tiles(L);
+    return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
+  }
   int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
   if (st) return st;
   moe::Stage s2;

@@ -32,6 +32,11 @@ struct GemvLayer {
   // Direct mode (one token): expert slot a is pair a, its expert ids_in[a];
   // no plan is built (the k experts of one token are distinct).
   int direct;
+  // With direct mode, the routing is not stored beforehand: every routed
+  // gate/up workgroup takes the top-k of the token's logits itself and the
+  // slot's first workgroup writes ids_out / w_out for the later launches;
+  // the logits launch clears the combine's counters.
+  int select_inline;
   int n_tiles;              // ceil(H / kDownRows) routed down tiles (set by the launcher)
   int n_stiles;             // ceil(H / 64) shared down tiles (set by the launcher)
   int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launcher)

@@ -331,6 +331,36 @@ __device__ __forceinline__ void slot_of(const GemvLayer& L, int a, int& n, int& 
   p1 = L.plan.act_off[a + 1];
 }
 
+// Direct mode with the selection done here (one token): wave 0 takes the
+// token's top-k from its logits and slot a is its a-th choice, shared with
+// the other waves through LDS; the slot's first workgroup (publish) stores
+// the routing for the down launch.
+__device__ __forceinline__ void select_slot(const GemvLayer& L, int a, bool publish, int& n,
+                                            int& e, int& p0, int& p1) {
+  __shared__ SelectScratch sc;
+  __shared__ int sel_e;
+  n = L.k;
+  p0 = a;
+  p1 = a + 1;
+  if (wave_id() == 0) {
+    int id;
+    float w;
+    select_token(L.logits, L.E, L.k, id, w, sc);
+    const int r = min(a, L.k - 1);
+    const int er = __builtin_amdgcn_readlane(id, r);
+    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), r));
+    if (threadIdx.x == 0) {
+      sel_e = er;
+      if (publish && a < n) {
+        L.ids_out[a] = er;
+        L.w_out[a] = wr;
+      }
+    }
+  }
+  __syncthreads();
+  e = __builtin_amdgcn_readfirstlane(sel_e);
+}
+
 // Pair (token * k + slot) at plan position p.
 __device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
   return L.direct ? p : L.plan.pairs[p];
@@ -338,7 +368,10 @@ __device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
 
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
   int na, e, p0, p1;
-  slot_of(L, a, na, e, p0, p1);
+  if (L.select_inline)
+    select_slot(L, a, tile == 0, na, e, p0, p1);
+  else
+    slot_of(L, a, na, e, p0, p1);
   if (a >= na) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -589,31 +622,45 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm)
 // All of a token's partial loads are issued before the first add, so the
 // tail costs one memory round trip, not k of them.
 __device__ void combine_tile(const GemvLayer& L, int tile) {
-  const int H = L.H;
+  const int H = L.H, k = L.k;
   const int n_out = L.T * kRowsD;
+  // Every load of a token's sum is issued unconditionally, with clamped
+  // indices and stand-in rows for absent operands, and their values are taken
+  // at one point: a load under a condition would be waited for on its own,
+  // one memory round trip each.
+  const float* ysh = L.S > 0 ? L.ysh : L.part;
+  const uint16_t* res = L.residual != nullptr ? L.residual : L.x;
   for (int idx = threadIdx.x; idx < n_out; idx += kThreads) {
     const int t = idx / kRowsD;
     const int n = tile * kRowsD + idx % kRowsD;
     if (n >= H) continue;
-    float pv[32], wv[32], sv[4];
+    float acc = 0.0f;
+    float sv[4];
+    uint16_t rv = 0;
+    for (int j0 = 0; j0 < k; j0 += 16) {
+      float pv[16], wv[16];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const size_t p = size_t(t) * L.k + j;
-      pv[j] = j < L.k ? load_coherent(&L.part[p * H + n]) : 0.0f;
-      wv[j] = j < L.k ? L.w[p] : 0.0f;
+      for (int j = 0; j < 16; ++j) {
+        const size_t p = size_t(t) * k + min(j0 + j, k - 1);
+        pv[j] = load_coherent(&L.part[p * H + n]);
+        wv[j] = L.w[p];
+      }
+      if (j0 == 0) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          sv[s] = ysh[(size_t(max(min(s, L.S - 1), 0)) * L.T + t) * H + n];
+        rv = res[size_t(t) * H + n];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(pv[j]), "+v"(wv[j]));
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < k) acc = fmaf(wv[j], pv[j], acc);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      sv[s] = s < L.S ? L.ysh[(size_t(s) * L.T + t) * H + n] : 0.0f;
-    const float r = L.residual != nullptr ? bf16_to_f32(L.residual[size_t(t) * H + n]) : 0.0f;
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < L.k) acc = fmaf(wv[j], pv[j], acc);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
       if (s < L.S) acc += sv[s];
-    if (L.residual != nullptr) acc += r;
+    if (L.residual != nullptr) acc += bf16_to_f32(rv);
     L.y[size_t(t) * H + n] = f32_to_bf16(acc);
   }
 }
@@ -1025,10 +1072,6 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
     }
   }
   if (!st.plan_after_select) return;
-  if (L.direct) {  // no plan: only the combine's arrival counters need clearing
-    for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
-    return;
-  }
   if (single) {
     __syncthreads();
     build_plan([&](int p) { return own_ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt, L.n_tiles);
@@ -1058,6 +1101,8 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     if (b < st.n_logits) {
       // the select workgroups of the next launch count their arrivals here
       if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
+      if (b == 0 && L.select_inline)
+        for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
       router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
       return;
     }

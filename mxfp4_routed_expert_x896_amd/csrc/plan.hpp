@@ -31,6 +31,25 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wtot) {
   return v + add;
 }
 
+// Eight routing ids per thread in flight at once (they may come from far
+// memory: one round trip per batch instead of per pair): e[j] = the expert
+// of pair p0 + j * kPlanThreads + tid, clamped to [0, E), or -1 past
+// n_pairs.  The loads are unconditional (clamped index) and taken together;
+// a load under a condition would be waited for on its own.
+constexpr int kBatch = 8;
+template <typename Ids>
+__device__ __forceinline__ void batch_ids(Ids ids, int p0, int n_pairs, int E, int (&e)[kBatch]) {
+  int v[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    v[j] = ids(min(p0 + j * kPlanThreads + int(threadIdx.x), n_pairs - 1));
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) asm volatile("" : "+v"(v[j]));
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j)
+    e[j] = p0 + j * kPlanThreads + int(threadIdx.x) < n_pairs ? min(max(v[j], 0), E - 1) : -1;
+}
+
 // Builds `plan` from the routing ids(p), p < n_pairs (E <= kPlanExperts),
 // including the list of token tiles (kPlanTileTokens pairs of one expert,
 // in slot order), and zeroes zero[0 .. n_zero).  ids(p) is a callback so the routing can be
@@ -47,16 +66,9 @@ __device__ void build_plan(Ids ids, int n_pairs, int E, Plan plan, int* zero, in
   for (int i = tid; i < n_zero; i += kPlanThreads) zero[i] = 0;
   for (int i = tid; i < kPlanExperts; i += kPlanThreads) cnt[i] = 0;
   __syncthreads();
-  // Eight loads in flight before their atomics: the ids may come from far
-  // memory, one round trip per batch instead of per pair.
-  constexpr int kBatch = 8;
   for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kPlanThreads) {
     int e[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + j * kPlanThreads + tid;
-      e[j] = p < n_pairs ? min(max(ids(p), 0), E - 1) : -1;
-    }
+    batch_ids(ids, p0, n_pairs, E, e);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
       if (e[j] >= 0) atomicAdd(&cnt[e[j]], 1);
@@ -95,11 +107,7 @@ __device__ void build_plan(Ids ids, int n_pairs, int E, Plan plan, int* zero, in
   __syncthreads();
   for (int p0 = 0; p0 < n_pairs; p0 += kBatch * kPlanThreads) {
     int e[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + j * kPlanThreads + tid;
-      e[j] = p < n_pairs ? min(max(ids(p), 0), E - 1) : -1;
-    }
+    batch_ids(ids, p0, n_pairs, E, e);
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
       if (e[j] >= 0) plan.pairs[atomicAdd(&cnt[e[j]], 1)] = p0 + j * kPlanThreads + tid;

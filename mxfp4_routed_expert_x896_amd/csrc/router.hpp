@@ -67,8 +67,9 @@ __device__ __forceinline__ void router_logits_rows(const uint16_t* __restrict__ 
 // Orderable 32-bit image of a float: a > b as floats iff ord(a) > ord(b) as
 // unsigned (finite values and infinities); never 0 for a finite value.
 __device__ __forceinline__ uint32_t ord_f32(float l) {
-  const uint32_t u = __float_as_uint(l == 0.0f ? 0.0f : l);  // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(l + 0.0f);  // -0 + 0 = +0: the zeros tie
+  // negative: all bits flipped; positive: sign bit set
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float unord_f32(uint32_t o) {
@@ -98,7 +99,8 @@ constexpr int kSelCap = 256;
 // Per-wave LDS of select_token.
 struct alignas(16) SelectScratch {
   uint32_t lmax[kWave];      // each lane's largest key
-  uint64_t cand[kSelCap];    // candidate (value, index) keys
+  uint64_t cand[kSelCap + kWave];  // candidate (value, index) keys; the last kWave
+                                   // entries take the other lanes' stores
   uint64_t top[32];          // the selected keys by rank
 };
 
@@ -147,11 +149,16 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int
                                              int& id, float& w, SelectScratch& sc) {
   const int lane = threadIdx.x % kWave;
   uint32_t val[16];
+  // unconditional loads (clamped address), so all sixteen are in flight at
+  // once; a load under a condition would be waited for on its own
+  float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + kWave * i;
-    val[i] = e < E ? ord_f32(lrow[e]) : 0u;
-  }
+  for (int i = 0; i < 16; ++i) lv[i] = lrow[min(lane + kWave * i, E - 1)];
+  // the values are taken here, so no load is moved under the condition below
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(lv[i]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) val[i] = lane + kWave * i < E ? ord_f32(lv[i]) : 0u;
   uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = val[i] > mx ? val[i] : mx;
@@ -176,17 +183,29 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int
   uint32_t my_val = 0;
   const bool overflow = total > kSelCap;
   if (!overflow) {
+    // every lane stores each of its keys: candidates to the next free slot,
+    // the others to the lane's own slot past the candidates (no branches)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + kWave * i;
-      if (e < E && val[i] >= M)
-        sc.cand[off++] = (uint64_t(val[i]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
+      const bool is_c = e < E && val[i] >= M;
+      sc.cand[is_c ? off : kSelCap + lane] =
+          (uint64_t(val[i]) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(e));
+      off += is_c ? 1 : 0;
     }
     wave_lds_sync();
     for (int c = lane; c < total; c += kWave) {
       const uint64_t key = sc.cand[c];
       int r = 0;
-      for (int t = 0; t < total; ++t) r += sc.cand[t] > key ? 1 : 0;
+      // eight keys per pass, loaded together (reads past total stay inside
+      // the array and are not counted)
+      for (int t0 = 0; t0 < total; t0 += 8) {
+        uint64_t q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = sc.cand[t0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += (t0 + u < total && q[u] > key) ? 1 : 0;
+      }
       if (r < k) sc.top[r] = key;
     }
     wave_lds_sync();
