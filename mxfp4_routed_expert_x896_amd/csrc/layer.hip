@@ -419,6 +419,10 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
   }
 }
 
+// Shared gate/up and down waves keep this many super-steps of weights in
+// flight (the shared launches have few workgroups per CU).
+constexpr int kSharedStages = 4;
+
 // Shared gate/up (bf16): 1 KiB tiles of 16 rows x 32 columns are the A
 // operand as loaded; four tiles per super-step, double-buffered.  A bf16
 // row is 3.8x the bytes of an MXFP4 row, so a workgroup takes one row group
@@ -450,14 +454,14 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, uint16_t* xs, 
   };
   for (int t0 = 0; t0 < L.T; t0 += L.mtp_gu) {
     const int mt = min(L.mtp_gu, L.T - t0);
-    Bf16Tiles ta, tb;
-    if (q0 < q1) load(ta, q0);
-    __syncthreads();
-    stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) { return L.x + size_t(t0 + j) * H; });
-    __syncthreads();
+    Bf16Tiles bufs[kSharedStages];
     const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
     f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
-    pipeline2(q0, q1, ta, tb, load, [&](const Bf16Tiles& t, int q) {
+    pipelineN<kSharedStages>(q0, q1, bufs, load, [&]() {
+      __syncthreads();
+      stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) { return L.x + size_t(t0 + j) * H; });
+      __syncthreads();
+    }, [&](const Bf16Tiles& t, int q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 bx = lds16(xrow + (4 * q + j) * 32 + 8 * g);
@@ -591,26 +595,26 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm)
   };
   for (int t0 = 0; t0 < L.T; t0 += L.mtp_d) {
     const int mt = min(L.mtp_d, L.T - t0);
-    Bf16Tile4 ta, tb;
-    if (live) load(ta, 0);
-    __syncthreads();
-    // interleaved rows: 2 j = hi, 2 j + 1 = lo of token j (see stage_h)
-    stage_rows(hsm, 2 * hstride, mt, I, pad_k(I),
-               [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
-    stage_rows(hsm + hstride, 2 * hstride, mt, I, pad_k(I),
-               [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
-    __syncthreads();
-    if (!live) continue;
+    Bf16Tile4 bufs[kSharedStages];
     const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    pipeline2(0, nq, ta, tb, load, [&](const Bf16Tile4& t, int q) {
+    // a dead wave (rows past H) loads nothing but joins the staging barriers
+    pipelineN<kSharedStages>(0, live ? nq : 0, bufs, load, [&]() {
+      __syncthreads();
+      // interleaved rows: 2 j = hi, 2 j + 1 = lo of token j (see stage_h)
+      stage_rows(hsm, 2 * hstride, mt, I, pad_k(I),
+                 [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
+      stage_rows(hsm + hstride, 2 * hstride, mt, I, pad_k(I),
+                 [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
+      __syncthreads();
+    }, [&](const Bf16Tile4& t, int q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma(t.w[j], lds16(bh + (4 * q + j) * 32 + 8 * g), acc);
     });
     float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
-    if ((c & 1) == 0 && c / 2 < mt) {
+    if (live && (c & 1) == 0 && c / 2 < mt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         L.ysh[(size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g + i] = y[i];
