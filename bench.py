@@ -35,8 +35,8 @@ REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
 SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 # kernels of one moe_layer call, in launch order (see moe_profile_events)
 KERNELS_GEMV = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
-# one token: the top-k is taken inside the routed gate/up launch, beside the shared down
-KERNELS_GEMV_T1 = ["router_shared_gateup", "shared_down_routed_gateup", "routed_down_combine"]
+# up to 4 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
+KERNELS_GEMV_SMALL = ["router_shared_gateup_topk", "shared_down_routed_gateup", "routed_down_combine"]
 KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4
@@ -87,13 +87,16 @@ def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
     x = T * H * 2
     if name == "router_shared_gateup":
         return E * H * 2 + x + T * E * 4 + S * 2 * SHARED_MAT_BYTES + S * T * I * 4
+    if name == "router_shared_gateup_topk":  # + logits read back, ids and weights written
+        return (E * H * 2 + x + 2 * T * E * 4 + T * k * 8
+                + S * 2 * SHARED_MAT_BYTES + S * T * I * 4)
     if name == "select_shared_down":
         return (T * E * 4 + T * k * 8 + T * k * 4 + E * 8
                 + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
     if name == "routed_gateup":
         return D * 2 * MAT_BYTES + x + T * k * I * 4
     if name == "shared_down_routed_gateup":
-        return (T * E * 4 + T * k * 8 + D * 2 * MAT_BYTES + x + T * k * I * 4
+        return (T * k * 4 + D * 2 * MAT_BYTES + x + T * k * I * 4
                 + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
     if name == "routed_down_combine":
         return D * MAT_BYTES + T * k * I * 4 + T * k * 4 + S * T * H * 4 + x
@@ -186,7 +189,7 @@ def main():
         args.warmup = cfgd.get("warmup", 20)
     mfma = cfgd.get("path") == "mfma"
     path = b.PATH_MFMA if mfma else b.PATH_GEMV
-    KERNELS = KERNELS_MFMA if mfma else (KERNELS_GEMV_T1 if T == 1 else KERNELS_GEMV)
+    KERNELS = KERNELS_MFMA if mfma else (KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
     replicas = args.replicas or cfgd["replicas"]
     c = synth.K3
     H, I, E, k, S = c["hidden"], c["inter"], c["n_experts"], c["top_k"], c["n_shared"]

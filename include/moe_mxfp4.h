@@ -209,9 +209,8 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
  * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
- * + combine -- for one token: router logits + shared gate/up, shared down +
- * routed gate/up (each workgroup takes its expert from the token's top-k),
- * routed down + combine.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
+ * + combine -- for up to 4 tokens: router logits + shared gate/up + top-k
+ * (and plan), shared down + routed gate/up, routed down + combine.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
  * to stop.  Timing
  * records only add event markers; no kernel is skipped or changed.
  */

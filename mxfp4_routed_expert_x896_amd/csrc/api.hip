@@ -1,6 +1,9 @@
 // C ABI of the MoE layer library: host-side validation, workspace carving
 // and launch sequencing on the caller's stream.  See include/moe_mxfp4.h.
+#include <unistd.h>
+
 #include <atomic>
+#include <chrono>
 #include <climits>
 #include <cstring>
 
@@ -105,9 +108,20 @@ int max_mtiles(const moe_layer_desc* L, int64_t T) {
 }
 int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
 
+int n_logit_wgs(const moe_layer_desc* L) { return (L->n_experts + 3) / 4; }
+
+// A value no earlier call stored in the logits flags: odd numbers from a
+// per-process start, so it is never 0 (the cleared state).
+unsigned long long next_epoch() {
+  static std::atomic<unsigned long long> ctr{
+      (uint64_t(std::chrono::steady_clock::now().time_since_epoch().count()) << 20) |
+      (uint64_t(getpid()) & 0xFFFFF)};
+  return ctr.fetch_add(2, std::memory_order_relaxed) | 1ull;
+}
+
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
+  uint64_t lflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
   uint64_t n_mtiles, mtiles, xq, xs, hq, hs8, total;
 };
 
@@ -121,6 +135,7 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
     off = align256(off + bytes);
     return at;
   };
+  c.lflags = take(uint64_t(n_logit_wgs(L) + 1) * 8);  // first: same place for every T
   c.logits = take(t * E * 4);
   c.n_active = take(4);
   c.active = take(E * 4);
@@ -174,6 +189,8 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.wr = L->router_w;
   G.rbias = L->router_bias;
   G.logits = at<float>(ws, c.logits);
+  G.lflags = at<unsigned long long>(ws, c.lflags);
+  G.epoch = next_epoch();
   G.sel_cnt = at<int>(ws, c.sel_cnt);
   G.experts = L->experts;
   G.stride = L->expert_stride;
@@ -201,7 +218,6 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
 }
 
 // Workgroup counts of the roles (see layer.hip).
-int n_logit_wgs(const moe_layer_desc* L) { return (L->n_experts + 3) / 4; }
 int n_select_wgs(int64_t T) { return int((T + 3) / 4); }
 int max_active(const moe_layer_desc* L, int64_t T) {
   const int64_t pairs = T * L->top_k;
@@ -270,11 +286,13 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   moe::Stage s1;
   s1.n_logits = n_logit_wgs(L);
   s1.n_sgu = S * (L->inter / 16);
-  if (T == 1) {
-    // one token: no top-k launch; the routed gate/up workgroups select
-    // (direct mode), the shared down runs beside them
-    G.direct = 1;
-    G.select_inline = 1;
+  if (n_select_wgs(T) == 1) {
+    // up to 4 tokens: the top-k (and for several tokens the plan) runs in
+    // the router launch, on one workgroup that waits for the logits; one
+    // token needs no plan (direct mode)
+    G.direct = T == 1;
+    s1.n_selw = 1;
+    s1.plan_after_select = 1;
     int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
     if (st) return st;
     moe::Stage s3;

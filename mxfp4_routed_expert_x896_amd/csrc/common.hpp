@@ -178,4 +178,17 @@ __device__ __forceinline__ int mxfp8_block_exp(float amax) {
   return max(-127, min(127, E));
 }
 
+// Results that cross workgroups of one launch (and XCDs, whose L2s are
+// private) are stored and re-read with device-scope atomic accesses, which
+// the compiler emits as write-through stores and L2-bypassing loads, instead
+// of fencing (a device-scope fence writes back and invalidates the whole L2).
+template <typename V>
+__device__ __forceinline__ void store_coherent(V* p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V load_coherent(const V* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace moe

@@ -32,11 +32,13 @@ struct GemvLayer {
   // Direct mode (one token): expert slot a is pair a, its expert ids_in[a];
   // no plan is built (the k experts of one token are distinct).
   int direct;
-  // With direct mode, the routing is not stored beforehand: every routed
-  // gate/up workgroup takes the top-k of the token's logits itself and the
-  // slot's first workgroup writes ids_out / w_out for the later launches;
-  // the logits launch clears the combine's counters.
-  int select_inline;
+  // Completion flags of the logits workgroups ([n_logits], at the start of
+  // the workspace): each stores `epoch` once its logits are stored, for a
+  // top-k workgroup of the same launch to wait on; that workgroup clears
+  // them.  epoch differs between calls; lflags[n_logits] is 1 if the wait
+  // gave up, else 0 (see select_waits in layer.hip).
+  unsigned long long* lflags;
+  unsigned long long epoch;
   int n_tiles;              // ceil(H / kDownRows) routed down tiles (set by the launcher)
   int n_stiles;             // ceil(H / 64) shared down tiles (set by the launcher)
   int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launcher)
@@ -63,6 +65,7 @@ struct GemvLayer {
 struct Stage {
   int n_logits = 0;           // ceil(E / 4)
   int n_select = 0;           // ceil(T / 4)
+  int n_selw = 0;             // 0 or 1: top-k (T <= 4) after waiting for this launch's logits
   int plan_after_select = 0;  // the last top-k workgroup builds the plan
   int n_plan = 0;             // 0 or 1
   int n_sgu = 0;              // S * I / 16
@@ -79,7 +82,7 @@ struct Stage {
 };
 
 enum class StageKind {
-  RouterSharedGateUp,  // roles: logits, shared gate/up
+  RouterSharedGateUp,  // roles: logits, shared gate/up, top-k waiting for the logits
   SelectSharedDown,    // roles: top-k (+ plan), shared down
   PlanSharedGateUp,    // roles: plan, shared gate/up
   RoutedGateUp,        // roles: shared down, routed gate/up

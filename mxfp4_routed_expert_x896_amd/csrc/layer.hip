@@ -76,19 +76,6 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
-// Partials cross workgroups (and XCDs, whose L2s are private): they are
-// stored and re-read with device-scope atomic accesses, which the compiler
-// emits as write-through stores and L2-bypassing loads, instead of fencing
-// (a device-scope fence writes back and invalidates the whole L2).
-template <typename V>
-__device__ __forceinline__ void store_coherent(V* p, V v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename V>
-__device__ __forceinline__ V load_coherent(const V* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Counts this workgroup's arrival on *cnt once all its global stores have
 // completed; true in every thread of the last of n arrivals.  With the
 // stores made through the coherent level (store_coherent), the last
@@ -331,36 +318,6 @@ __device__ __forceinline__ void slot_of(const GemvLayer& L, int a, int& n, int& 
   p1 = L.plan.act_off[a + 1];
 }
 
-// Direct mode with the selection done here (one token): wave 0 takes the
-// token's top-k from its logits and slot a is its a-th choice, shared with
-// the other waves through LDS; the slot's first workgroup (publish) stores
-// the routing for the down launch.
-__device__ __forceinline__ void select_slot(const GemvLayer& L, int a, bool publish, int& n,
-                                            int& e, int& p0, int& p1) {
-  __shared__ SelectScratch sc;
-  __shared__ int sel_e;
-  n = L.k;
-  p0 = a;
-  p1 = a + 1;
-  if (wave_id() == 0) {
-    int id;
-    float w;
-    select_token(L.logits, L.E, L.k, id, w, sc);
-    const int r = min(a, L.k - 1);
-    const int er = __builtin_amdgcn_readlane(id, r);
-    const float wr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), r));
-    if (threadIdx.x == 0) {
-      sel_e = er;
-      if (publish && a < n) {
-        L.ids_out[a] = er;
-        L.w_out[a] = wr;
-      }
-    }
-  }
-  __syncthreads();
-  e = __builtin_amdgcn_readfirstlane(sel_e);
-}
-
 // Pair (token * k + slot) at plan position p.
 __device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
   return L.direct ? p : L.plan.pairs[p];
@@ -368,10 +325,7 @@ __device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
 
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
   int na, e, p0, p1;
-  if (L.select_inline)
-    select_slot(L, a, tile == 0, na, e, p0, p1);
-  else
-    slot_of(L, a, na, e, p0, p1);
+  slot_of(L, a, na, e, p0, p1);
   if (a >= na) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -689,6 +643,7 @@ enum : unsigned {
   kRoleRouterMx = 2048u,  // prefill: router logits, (256 experts, 64 tokens)
   kRoleSharedGUMx = 4096u,    // prefill: shared gate/up, (expert, 128 rows, 64 tokens)
   kRoleSharedDownMx = 8192u,  // prefill: shared down, (expert, 256 rows, 64 tokens)
+  kRoleSelectWait = 16384u,   // top-k of T <= 4 tokens once this launch's logits are flagged
 };
 
 // XCD-aware order for a grid over (pair, token tile): block b runs on XCD
@@ -1050,6 +1005,27 @@ __device__ void combine_role(const GemvLayer& L, int t) {
   }
 }
 
+// The top-k workgroup of the router launch (T <= 4, the launch's last
+// block) waits until every logits workgroup has flagged its logits with this
+// call's epoch, then clears the flags for the next call.  Only this one
+// workgroup waits, on workgroups that wait on nothing, so the others always
+// get to run.  The wait is bounded: lflags[n] is set to 1 if it gave up (0
+// otherwise), and the selection then runs on what is there (wrong results,
+// no hang).
+constexpr long kSelectSpinLimit = 1l << 20;  // polls of ~0.3 us
+__device__ void select_waits(const GemvLayer& L, int n) {
+  bool done = false;
+  for (long it = 0; it < kSelectSpinLimit && !done; ++it) {
+    int ok = 1;
+    for (int i = threadIdx.x; i < n; i += kThreads) ok &= load_coherent(&L.lflags[i]) == L.epoch;
+    done = __syncthreads_and(ok) != 0;
+    if (!done) __builtin_amdgcn_s_sleep(8);
+  }
+  for (int i = threadIdx.x; i < n; i += kThreads) L.lflags[i] = 0;
+  if (threadIdx.x == 0) L.lflags[n] = done ? 0ull : 1ull;
+}
+
+template <bool kCoherent = false>
 __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -1057,13 +1033,13 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   // With one top-k workgroup (T <= 4) it builds the plan straight from its
   // own selections in LDS: no arrival count, and no round trips through the
   // coherent level for the ids it has just computed.
-  const bool single = st.n_select == 1;
+  const bool single = st.n_select + st.n_selw == 1;
   __shared__ int own_ids[4 * 32];
   __shared__ SelectScratch sc[kWaves];
   if (t < L.T) {
     int id;
     float w;
-    select_token(L.logits + size_t(t) * L.E, L.E, L.k, id, w, sc[wave]);
+    select_token<kCoherent>(L.logits + size_t(t) * L.E, L.E, L.k, id, w, sc[wave]);
     if (lane < L.k) {
       if (single) {
         L.ids_out[size_t(t) * L.k + lane] = id;
@@ -1076,6 +1052,10 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
     }
   }
   if (!st.plan_after_select) return;
+  if (L.direct) {  // no plan: only the combine's arrival counters need clearing
+    for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
+    return;
+  }
   if (single) {
     __syncthreads();
     build_plan([&](int p) { return own_ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt, L.n_tiles);
@@ -1105,9 +1085,12 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     if (b < st.n_logits) {
       // the select workgroups of the next launch count their arrivals here
       if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
-      if (b == 0 && L.select_inline)
-        for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
       router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
+      if (st.n_selw > 0) {  // logits stored (through the coherent level): flag them
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0) store_coherent(&L.lflags[b], L.epoch);
+      }
       return;
     }
     b -= st.n_logits;
@@ -1204,14 +1187,24 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     b -= st.n_rgu;
   }
   if constexpr ((R & kRoleRoutedDown) != 0) {
-    if (b < st.n_rdn) routed_down_role(L, b / L.n_tiles, b % L.n_tiles, lds16p);
+    if (b < st.n_rdn) {
+      routed_down_role(L, b / L.n_tiles, b % L.n_tiles, lds16p);
+      return;
+    }
+    b -= st.n_rdn;
+  }
+  if constexpr ((R & kRoleSelectWait) != 0) {  // last: it waits on the blocks before it
+    if (b < st.n_selw) {
+      select_waits(L, st.n_logits);
+      select_role<true>(L, st, 0);
+    }
   }
 }
 
 // The launches, named for what they run.
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void moe_router_shared_gateup(GemvLayer L, Stage st) {
-  stage_body<kRoleLogits | kRoleSharedGU, NCH>(L, st);
+  stage_body<kRoleLogits | kRoleSharedGU | kRoleSelectWait, NCH>(L, st);
 }
 __global__ __launch_bounds__(kThreads) void moe_select_shared_down(GemvLayer L, Stage st) {
   stage_body<kRoleSelect | kRoleSharedDown, 0>(L, st);
@@ -1265,7 +1258,7 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   if (st.n_sdmx > 0) lds = max(lds, size_t(4 * bf::kStageBytes));
   const int wgs = st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu +
                   st.n_rdn + st.n_xq + st.n_mgu + st.n_mdn + st.n_comb + st.n_rmx + st.n_sgmx +
-                  st.n_sdmx;
+                  st.n_sdmx + st.n_selw;
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs), block(kThreads);
   switch (kind) {

@@ -59,7 +59,9 @@ __device__ __forceinline__ void router_logits_rows(const uint16_t* __restrict__ 
         }
       }
       acc = wave_sum(acc);
-      if (live && lane == 0) logits[size_t(t0 + tt) * E + e] = acc + bv;
+      // through the coherent level: a top-k workgroup of the same launch may
+      // read them (see select_waits in layer.hip)
+      if (live && lane == 0) store_coherent(&logits[size_t(t0 + tt) * E + e], acc + bv);
     }
   }
 }
@@ -145,6 +147,8 @@ __device__ __forceinline__ int wave_prefix_small(int v, int& total) {
 // also at or above M -- is counted directly; ranks below k are the
 // selection.  If more than kSelCap experts reach M (heavy ties), the token
 // is redone exactly by k rounds of a wave-wide maximum over all keys.
+// kCoherent: the logits were written in the same launch (read past L2).
+template <bool kCoherent = false>
 __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int E, int k,
                                              int& id, float& w, SelectScratch& sc) {
   const int lane = threadIdx.x % kWave;
@@ -153,7 +157,10 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, int
   // once; a load under a condition would be waited for on its own
   float lv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lv[i] = lrow[min(lane + kWave * i, E - 1)];
+  for (int i = 0; i < 16; ++i) {
+    const float* p = lrow + min(lane + kWave * i, E - 1);
+    lv[i] = kCoherent ? load_coherent(p) : *p;
+  }
   // the values are taken here, so no load is moved under the condition below
 #pragma unroll
   for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(lv[i]));

@@ -182,7 +182,7 @@ def test_forward_tiny_given_oracle_routing(b, tiny, T):
 
 
 @pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY], ids=["tiny", "ragged", "wide", "many"])
-@pytest.mark.parametrize("T", [1, 7, 70])
+@pytest.mark.parametrize("T", [1, 4, 7, 70])
 def test_layer_matches_oracle(b, cfg, T):
     built = Built(cfg, seed=11)
     xh, xd = SD.upload_tokens(1100 + T, T, cfg["hidden"])
@@ -310,5 +310,33 @@ def test_consecutive_calls_with_changing_inputs(b):
         _, _, s = M.route(xh, built.oracle)
         ids_np = i_.cpu().numpy()
         check_routing(ids_np, w_.cpu().numpy(), s, 6)
+        ref = M.moe_forward(xh, built.oracle, ids_np, oracle_weights(s, ids_np))
+        check_parity(to_np_u16(y), ref)
+
+
+def test_alternating_batch_sizes_share_a_workspace(b):
+    """One workspace, token counts alternating over the three launch
+    structures (one token: no plan; 2-4 tokens: top-k and plan inside the
+    router launch; more: a top-k launch).  Every call matches the oracle,
+    and after each call the logits completion flags at the start of the
+    workspace are all clear (the top-k workgroup clears what it waited on,
+    and the give-up word is 0)."""
+    cfg = dict(hidden=512, inter=128, n_experts=64, top_k=6, n_shared=2)
+    built = Built(cfg, seed=11)
+    ws = built.lib.workspace(9)
+    n_flags = (64 + 3) // 4 + 1
+    for i, T in enumerate([1, 4, 9, 2, 1, 3, 9, 1]):
+        xh, xd = SD.upload_tokens(1900 + i, T, 512)
+        ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, 6), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, 512), dtype=torch.int16, device="cuda")
+        b.moe_layer(built.lib, xd, y, ids, w, ws, path=b.PATH_GEMV)
+        torch.cuda.synchronize()
+        if T <= 4:
+            flags = ws[: 8 * n_flags].cpu().numpy().view(np.uint64)
+            assert not flags.any(), (T, flags)
+        _, _, s = M.route(xh, built.oracle)
+        ids_np = ids.cpu().numpy()
+        check_routing(ids_np, w.cpu().numpy(), s, 6)
         ref = M.moe_forward(xh, built.oracle, ids_np, oracle_weights(s, ids_np))
         check_parity(to_np_u16(y), ref)
