@@ -9,7 +9,8 @@
 namespace moe {
 
 // Output rows per routed down workgroup (and per combine tile).
-constexpr int kDownRows = 256;
+constexpr int kDownRows = 128;
+static_assert(kDownRows % 16 == 0, "whole row groups");
 
 // Everything the layer kernels need (layer.hip).
 struct GemvLayer {

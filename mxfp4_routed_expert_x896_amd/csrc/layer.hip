@@ -49,7 +49,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRowsD = kDownRows;  // routed down rows per workgroup (4 row groups per wave)
+constexpr int kRowsD = kDownRows;  // routed down rows per workgroup (a multiple of 16)
 constexpr int kRowsSD = 64;        // shared down rows per workgroup (one row group per wave)
 constexpr int kCols = 16;         // B columns of one MFMA: at most 16 tokens per pass
 constexpr int kLdsBudget = 32768;  // bytes of staged activations per workgroup
@@ -160,8 +160,10 @@ __device__ __forceinline__ void pipeline2(int s0, int s1, Buf& a, Buf& b, Load l
   int s = s0;
   for (; s + 2 < s1; s += 2) {
     load(b, s + 1);
+    __builtin_amdgcn_sched_barrier(0);  // loads stay ahead of the wait (see pipelineN)
     comp(a, s);
     load(a, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
     comp(b, s + 1);
   }
   if (s + 1 < s1) {
@@ -190,6 +192,9 @@ __device__ __forceinline__ void pipelineN(int s0, int s1, Buf (&b)[D], Load load
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       load(b[(d + D - 1) % D], s + d + D - 1);
+      // keep the loads ahead of the wait for step s + d: scheduled after
+      // it, they would leave one step fewer in flight
+      __builtin_amdgcn_sched_barrier(0);
       comp(b[d], s + d);
     }
   }
@@ -454,12 +459,14 @@ struct DnTiles {
   uint32_t sc;
 };
 
-// Routed down waves stream 4 row groups x 3 super-steps of 4 KiB with about
-// 1.75 waves per SIMD; four stages keep 12 KiB per wave in flight.
-constexpr int kDownStages = 4;
+// Routed down: three stages (8 KiB per wave in flight) keep the kernel
+// under 128 VGPRs, so four waves share a SIMD; at the K3 shape (I = 1536)
+// a wave streams 2 row groups x 3 super-steps of 4 KiB, and more waves in
+// flight per SIMD beat deeper pipelines per wave (measured).
+constexpr int kDownStages = 3;
 
 // Routed down: workgroup = (expert, tile of kRowsD rows); wave w takes the
-// tile's row groups 4 w .. 4 w + 3 one after the other as one continuous
+// tile's row groups w, w + 4, w + 8, ... one after the other as one continuous
 // pipeline of (row group, super-step) steps, so its loads never drain
 // between row groups; a row group's partials are stored after its last
 // super-step.
@@ -471,9 +478,10 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   const int H = L.H, I = L.I;
   const PackedMx pgu(I, H), pd(H, I);
   const int nkq = pd.nkb4 / 4;
-  constexpr int kGroups = kRowsD / 16 / kWaves;  // row groups per wave
-  const int rg0 = tile * (kRowsD / 16) + wave * kGroups;
-  const int nrg = max(0, min(kGroups, H / 16 - rg0));  // live row groups (ragged last tile)
+  // the tile's row groups rg0 + wave + kWaves r, r = 0 .. nrg - 1
+  const int tile_rg = min(kRowsD / 16, H / 16 - tile * (kRowsD / 16));  // ragged last tile
+  const int rg0 = tile * (kRowsD / 16) + wave;
+  const int nrg = max(0, (tile_rg - wave + kWaves - 1) / kWaves);
   const int nsteps = nrg * nkq;
   const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
   const uint8_t* codes = base + size_t(rg0) * pd.nkb * 1024 + 16 * lane;
@@ -481,11 +489,11 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   const int hstride = pad_k(I) + 8;
   auto load = [&](DnTiles& t, int s) {
     const int r = s / nkq, kq = s - r * nkq;
-    const uint8_t* cr = codes + size_t(r) * pd.nkb * 1024;
+    const uint8_t* cr = codes + size_t(r) * kWaves * pd.nkb * 1024;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       t.w[j] = ld_nt(cr + size_t(min(4 * kq + j, pd.nkb - 1)) * 1024);
-    t.sc = *reinterpret_cast<const uint32_t*>(scl + size_t(r) * 64 * pd.nkb4 + 4 * kq);
+    t.sc = *reinterpret_cast<const uint32_t*>(scl + size_t(r) * kWaves * 64 * pd.nkb4 + 4 * kq);
   };
 
   for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
@@ -510,14 +518,14 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
         for (int q = 0; q < 4; ++q)
           acc = mfma(fp4x8_scaled(t.w[j][q], sd), lds16(bh + bi * 32 + 8 * q), acc);
       }
-      if (kq == nkq - 1) {  // row group rg0 + r complete
+      if (kq == nkq - 1) {  // row group rg0 + kWaves r complete
         float y[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
         if ((c & 1) == 0 && tok < mt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            store_coherent(&L.part[size_t(pair) * H + (rg0 + r) * 16 + 4 * g + i], y[i]);
+            store_coherent(&L.part[size_t(pair) * H + (rg0 + kWaves * r) * 16 + 4 * g + i], y[i]);
         }
         acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -1215,7 +1223,8 @@ __global__ __launch_bounds__(kThreads) void moe_plan_shared_gateup(GemvLayer L, 
 __global__ __launch_bounds__(kThreads) void moe_routed_gateup(GemvLayer L, Stage st) {
   stage_body<kRoleSharedDown | kRoleRoutedGU, 0>(L, st);
 }
-__global__ __launch_bounds__(kThreads) void moe_routed_down_combine(GemvLayer L, Stage st) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+moe_routed_down_combine(GemvLayer L, Stage st) {
   stage_body<kRoleRoutedDown, 0>(L, st);
 }
 __global__ __launch_bounds__(kThreads) void moe_plan_quant_shared_gateup(GemvLayer L, Stage st) {
