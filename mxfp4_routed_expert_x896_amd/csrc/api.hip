@@ -100,11 +100,11 @@ uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
 int n_tiles(const moe_layer_desc* L) { return (L->hidden + moe::kDownRows - 1) / moe::kDownRows; }
 uint64_t pad512(uint64_t v) { return (v + 511) / 512 * 512; }
-// Upper bound on the prefill token tiles (64 pairs of one expert each).
+// Upper bound on the prefill token tiles (kPlanTileTokens pairs of one expert each).
 int max_mtiles(const moe_layer_desc* L, int64_t T) {
   const int64_t pairs = T * L->top_k;
   const int64_t active = pairs < L->n_experts ? pairs : L->n_experts;
-  return int((pairs + 63 * active) / 64 + 1);
+  return int((pairs + (moe::kPlanTileTokens - 1) * active) / moe::kPlanTileTokens + 1);
 }
 int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
 
@@ -318,7 +318,6 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
 }
 
-int round8(int v) { return (v + 7) / 8 * 8; }
 int n_quant_wgs(const moe::GemvLayer& G, int64_t T) { return int((T * (G.Kq / 32) + 255) / 256); }
 int n_token_tiles(int64_t T) { return int((T + 63) / 64); }
 // Grid of an XCD-ordered role over (pairs, token tiles): see xcd_split.
@@ -331,12 +330,12 @@ int xcd_grid(int n_pairs, int64_t T) { return 8 * ((n_pairs + 7) / 8) * n_token_
 int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hipStream_t stream) {
   const int S = L->n_shared, mt = max_mtiles(L, T);
   moe::Stage s2;
-  s2.n_mgu = round8(mt * ((L->inter + 127) / 128));
+  s2.n_mgu = 8 * ((mt + 7) / 8) * ((L->inter + 127) / 128);  // XCD-grouped (see layer.hip)
   s2.n_sgmx = S > 0 ? xcd_grid(S * ((L->inter + 127) / 128), T) : 0;
   int st = stage(moe::StageKind::MxGateUp, G, s2, stream);
   if (st) return st;
   moe::Stage s3;
-  s3.n_mdn = round8(mt * ((L->hidden + 255) / 256));
+  s3.n_mdn = 8 * ((mt + 7) / 8) * ((L->hidden + 255) / 256);
   s3.n_sdmx = S > 0 ? xcd_grid(S * ((L->hidden + 255) / 256), T) : 0;
   if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
   moe::Stage s4;

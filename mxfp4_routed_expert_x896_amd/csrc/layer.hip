@@ -857,9 +857,12 @@ __device__ __forceinline__ bool mx_tile(const GemvLayer& L, int ti, MxTile& t) {
 // wave's 32 rows are exactly one block per token.
 __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int tiles_r = (L.I + 127) / 128;
+  // the row tiles of one token tile share an XCD (b % 8), so its staged
+  // activations come from that XCD's L2 after the first
   MxTile tt;
-  if (!mx_tile(L, b / tiles_r, tt)) return;
-  const int rt = b % tiles_r;
+  const int i = b / 8;
+  if (!mx_tile(L, b % 8 + 8 * (i / tiles_r), tt)) return;
+  const int rt = i % tiles_r;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -932,9 +935,10 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
 // groups 4 w .. 4 w + 3.  Writes fp32 partials per pair (combined later).
 __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int tiles_r = (L.H + 255) / 256;
-  MxTile tt;
-  if (!mx_tile(L, b / tiles_r, tt)) return;
-  const int rt = b % tiles_r;
+  MxTile tt;  // XCD-grouped like the gate/up
+  const int i = b / 8;
+  if (!mx_tile(L, b % 8 + 8 * (i / tiles_r), tt)) return;
+  const int rt = i % tiles_r;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -978,34 +982,49 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
 __device__ void combine_role(const GemvLayer& L, int t) {
   if (t >= L.T) return;
   const int H = L.H, k = L.k;
-  float wv[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) wv[j] = j < k ? L.w[size_t(t) * k + j] : 0.0f;
+  // Every load is unconditional (clamped index, stand-in rows for absent
+  // operands) and the values of a group are taken together: a load under a
+  // condition would be waited for on its own, one round trip each.
+  const float* ysh = L.S > 0 ? L.ysh : L.part;
+  const uint16_t* res = L.residual != nullptr ? L.residual : L.x;
   for (int n = 4 * threadIdx.x; n < H; n += 4 * kThreads) {
-    mx::f32x4 pv[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < k)
-        pv[j] = __builtin_nontemporal_load(
-            reinterpret_cast<const mx::f32x4*>(L.part + (size_t(t) * k + j) * H + n));
     mx::f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    mx::f32x4 sv[4];
+    u32x2 rv = {0u, 0u};
+    for (int j0 = 0; j0 < k; j0 += 16) {
+      mx::f32x4 pv[16];
+      float wv[16];
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      if (j < k)
+      for (int j = 0; j < 16; ++j) {
+        const size_t p = size_t(t) * k + min(j0 + j, k - 1);
+        pv[j] = __builtin_nontemporal_load(reinterpret_cast<const mx::f32x4*>(L.part + p * H + n));
+        wv[j] = L.w[p];
+      }
+      if (j0 == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wv[j], pv[j][i], acc[i]);
-    for (int sx = 0; sx < L.S; ++sx) {
-      const mx::f32x4 sv =
-          *reinterpret_cast<const mx::f32x4*>(L.ysh + (size_t(sx) * L.T + t) * H + n);
+        for (int sx = 0; sx < 4; ++sx)
+          sv[sx] = *reinterpret_cast<const mx::f32x4*>(
+              ysh + (size_t(max(min(sx, L.S - 1), 0)) * L.T + t) * H + n);
+        rv = *reinterpret_cast<const u32x2*>(res + size_t(t) * H + n);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += sv[i];
+      for (int j = 0; j < 16; ++j) asm volatile("" : "+v"(pv[j]), "+v"(wv[j]));
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(wv[j], pv[j][i], acc[i]);
     }
+#pragma unroll
+    for (int sx = 0; sx < 4; ++sx)
+      if (sx < L.S)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += sv[sx][i];
     if (L.residual != nullptr) {
-      const u32x2 r = *reinterpret_cast<const u32x2*>(L.residual + size_t(t) * H + n);
-      acc[0] += bf16_lo(r[0]);
-      acc[1] += bf16_hi(r[0]);
-      acc[2] += bf16_lo(r[1]);
-      acc[3] += bf16_hi(r[1]);
+      acc[0] += bf16_lo(rv[0]);
+      acc[1] += bf16_hi(rv[0]);
+      acc[2] += bf16_lo(rv[1]);
+      acc[3] += bf16_hi(rv[1]);
     }
     *reinterpret_cast<u32x2*>(L.y + size_t(t) * H + n) =
         u32x2{uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16),
