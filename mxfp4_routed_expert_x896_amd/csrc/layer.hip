@@ -379,15 +379,21 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
 }
 
 // Shared gate/up and down waves keep this many super-steps of weights in
-// flight (the shared launches have few workgroups per CU).
+// flight (the shared launches have few workgroups per CU); the shared down
+// shares its launch with the routed gate/up, whose occupancy (three waves
+// per SIMD) its registers must not lower.
 constexpr int kSharedStages = 4;
+constexpr int kSharedDownStages = 3;
 
 // Shared gate/up (bf16): 1 KiB tiles of 16 rows x 32 columns are the A
-// operand as loaded; four tiles per super-step, double-buffered.  A bf16
+// operand as loaded; four tiles per super-step, three in flight.  A bf16
 // row is 3.8x the bytes of an MXFP4 row, so a workgroup takes one row group
 // and its four waves split the contraction in quarters (more waves in
-// flight for the same bytes).
-__device__ void shared_gateup(const GemvLayer& L, int sx, int rg, uint16_t* xs, float* red) {
+// flight for the same bytes).  The B operand (16 tokens per pass) is read
+// straight from the token rows, which every workgroup shares through L2:
+// per tile it is as many bytes as the weights, so no LDS staging (and no
+// cap on tokens per pass from the LDS size) is needed.
+__device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -398,34 +404,32 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, uint16_t* xs, 
   const int q0 = min(wave * qq, nq), q1 = min(q0 + qq, nq);
   const uint16_t* gt = L.sgate + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
   const uint16_t* ut = L.sup + sx * (size_t(I) * H) + size_t(rg) * nu * 512;
-  const int xstride = pad_k(H) + 8;
   const size_t plane = size_t(L.S) * L.T * I;
-  struct Bf16Tiles {
-    u32x4 g[4], u[4];
+  struct Tiles {
+    u32x4 g[4], u[4], x[4];
   };
-  auto load = [&](Bf16Tiles& t, int q) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = min(4 * q + j, nu - 1);  // past the end: multiplied by zeros
-      t.g[j] = ld_nt(gt + size_t(u) * 512 + 8 * lane);
-      t.u[j] = ld_nt(ut + size_t(u) * 512 + 8 * lane);
-    }
-  };
-  for (int t0 = 0; t0 < L.T; t0 += L.mtp_gu) {
-    const int mt = min(L.mtp_gu, L.T - t0);
-    Bf16Tiles bufs[kSharedStages];
-    const uint16_t* xrow = xs + (c < mt ? c : 0) * xstride;
-    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
-    pipelineN<kSharedStages>(q0, q1, bufs, load, [&]() {
-      __syncthreads();
-      stage_rows(xs, xstride, mt, H, pad_k(H), [&](int j) { return L.x + size_t(t0 + j) * H; });
-      __syncthreads();
-    }, [&](const Bf16Tiles& t, int q) {
+  for (int t0 = 0; t0 < L.T; t0 += kCols) {
+    const int mt = min(kCols, L.T - t0);
+    // B straight from the token rows (L2-resident): lane (c, g) reads token
+    // c's 8 columns of each 32-column tile (a clamped token past mt)
+    const uint16_t* xrow = L.x + size_t(t0 + min(c, mt - 1)) * H + 8 * g;
+    auto load = [&](Tiles& t, int q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x4 bx = lds16(xrow + (4 * q + j) * 32 + 8 * g);
-        ag = mfma(t.g[j], bx, ag);
-        au = mfma(t.u[j], bx, au);
+        const int u = min(4 * q + j, nu - 1);  // past the end: skipped below
+        t.g[j] = ld_nt(gt + size_t(u) * 512 + 8 * lane);
+        t.u[j] = ld_nt(ut + size_t(u) * 512 + 8 * lane);
+        t.x[j] = ld16(xrow + u * 32);
+      }
+    };
+    Tiles bufs[3];
+    f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
+    pipelineN<3>(q0, q1, bufs, load, [&]() {}, [&](const Tiles& t, int q) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * q + j >= nu) break;  // uniform
+        ag = mfma(t.g[j], t.x[j], ag);
+        au = mfma(t.u[j], t.x[j], au);
       }
     });
     join_quarters(ag, au, red);
@@ -444,8 +448,9 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, uint16_t* xs, 
 
 // ------------------------------------------------------------------------
 // Down projections and the combine.  Workgroups are (expert, tile of kRowsD
-// output rows, 16 per wave); h enters as bf16 hi + lo, staged in LDS, two
-// MFMAs per step.  The shared experts' down runs in an earlier launch and
+// output rows, 16 per wave); h enters as bf16 hi + lo, staged in LDS (the
+// shared down reads it straight from L2, 8 tokens per pass, hi and lo as
+// adjacent B columns).  The shared experts' down runs in an earlier launch and
 // leaves fp32 outputs in ysh.  Each routed workgroup writes fp32 partials
 // for its rows and tokens; the last one to finish a tile (device-scope
 // counter, zeroed by the plan builder of the same call) sums the tile's
@@ -533,7 +538,7 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   }
 }
 
-__device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm) {
+__device__ void shared_down(const GemvLayer& L, int sx, int tile) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -543,35 +548,32 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile, uint16_t* hsm)
   const int nu = I / 32;
   const int nq = (nu + 3) / 4;
   const uint16_t* dt = L.sdown + sx * (size_t(H) * I) + size_t(live ? rg : 0) * nu * 512;
-  const int hstride = pad_k(I) + 8;
   const size_t plane = size_t(L.S) * L.T * I;
-  struct Bf16Tile4 {
-    u32x4 w[4];
+  struct Tiles {
+    u32x4 w[4], h[4];
   };
-  auto load = [&](Bf16Tile4& t, int q) {
+  for (int t0 = 0; t0 < L.T; t0 += kCols / 2) {
+    const int mt = min(kCols / 2, L.T - t0);
+    // B straight from h (L2-resident): column c is token c / 2's hi (c even)
+    // or lo (c odd) part; lane (c, g) reads 8 columns of each 32-column tile
+    const int tok = t0 + min(c / 2, mt - 1);
+    const uint16_t* hrow = L.hs + (c & 1) * plane + (size_t(sx) * L.T + tok) * I + 8 * g;
+    auto load = [&](Tiles& t, int q) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = 4 * q + j;
-      t.w[j] = ld_nt(dt + size_t(min(u, nu - 1)) * 512 + 8 * lane);
-    }
-  };
-  for (int t0 = 0; t0 < L.T; t0 += L.mtp_d) {
-    const int mt = min(L.mtp_d, L.T - t0);
-    Bf16Tile4 bufs[kSharedStages];
-    const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;
+      for (int j = 0; j < 4; ++j) {
+        const int u = min(4 * q + j, nu - 1);  // past the end: skipped below
+        t.w[j] = ld_nt(dt + size_t(u) * 512 + 8 * lane);
+        t.h[j] = ld16(hrow + u * 32);
+      }
+    };
+    Tiles bufs[kSharedDownStages];
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // a dead wave (rows past H) loads nothing but joins the staging barriers
-    pipelineN<kSharedStages>(0, live ? nq : 0, bufs, load, [&]() {
-      __syncthreads();
-      // interleaved rows: 2 j = hi, 2 j + 1 = lo of token j (see stage_h)
-      stage_rows(hsm, 2 * hstride, mt, I, pad_k(I),
-                 [&](int j) { return L.hs + (size_t(sx) * L.T + t0 + j) * I; });
-      stage_rows(hsm + hstride, 2 * hstride, mt, I, pad_k(I),
-                 [&](int j) { return L.hs + plane + (size_t(sx) * L.T + t0 + j) * I; });
-      __syncthreads();
-    }, [&](const Bf16Tile4& t, int q) {
+    pipelineN<kSharedDownStages>(0, live ? nq : 0, bufs, load, [&]() {}, [&](const Tiles& t, int q) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma(t.w[j], lds16(bh + (4 * q + j) * 32 + 8 * g), acc);
+      for (int j = 0; j < 4; ++j) {
+        if (4 * q + j >= nu) break;  // uniform
+        acc = mfma(t.w[j], t.h[j], acc);
+      }
     });
     float y[4];
 #pragma unroll
@@ -1194,14 +1196,14 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   const int gu_tiles = L.I / 32;
   if constexpr ((R & kRoleSharedGU) != 0) {
     if (b < st.n_sgu) {
-      shared_gateup(L, b / (L.I / 16), b % (L.I / 16), lds16p, red);
+      shared_gateup(L, b / (L.I / 16), b % (L.I / 16), red);
       return;
     }
     b -= st.n_sgu;
   }
   if constexpr ((R & kRoleSharedDown) != 0) {
     if (b < st.n_sdn) {
-      shared_down(L, b / L.n_stiles, b % L.n_stiles, lds16p);
+      shared_down(L, b / L.n_stiles, b % L.n_stiles);
       return;
     }
     b -= st.n_sdn;
@@ -1279,8 +1281,8 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   L.mtp_d = min(tokens_per_pass(L.T, hrow * 4), kCols / 2);  // hi + lo: two B columns per token
   size_t lds = 0;
   if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
-  if (st.n_sgu > 0 || st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
-  if (st.n_sdn > 0 || st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
+  if (st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
+  if (st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
   if (st.n_mgu > 0 || st.n_mdn > 0) lds = max(lds, size_t(2 * mx::kStageBytes));
   if (st.n_rmx > 0 || st.n_sgmx > 0) lds = max(lds, size_t(2 * bf::kStageBytes));
   if (st.n_sdmx > 0) lds = max(lds, size_t(4 * bf::kStageBytes));
