@@ -40,6 +40,7 @@ KERNELS_GEMV_SMALL = ["router_shared_gateup_topk", "shared_down_routed_gateup", 
 KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
@@ -50,6 +51,10 @@ CONFIGS = {
                 desc="K3 MoE layer batched decode, 64 tokens"),
     "stack12": dict(tokens=8, layers=12, replicas=1,
                     desc="12 stacked K3 MoE layers (RMSNorm -> MoE -> residual), batch 8"),
+    "prefill128": dict(tokens=4096, layers=1, replicas=1, bias=True, favor=128, path="mfma",
+                       steps=20, warmup=3,
+                       desc="compute-bound diagnostic of the prefill kernels: 4096 tokens routed to "
+                            "128 experts (512 tokens each) by +20 on their logit bias"),
     "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
                     desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
                          "MXFP8 activations on block-scaled MFMA"),
@@ -144,6 +149,9 @@ def cpu_baseline(cfg_name, n_tokens):
     cfg = CONFIGS[cfg_name]
     mx = cfg.get("path") == "mfma"
     bias = synth.router_bias(0, 0, c["n_experts"]) if cfg.get("bias") else None
+    if bias is not None and cfg.get("favor"):
+        bias = bias.copy()
+        bias[:cfg["favor"]] += 20.0
     layer = M.Layer(H, I, c["n_experts"], c["top_k"], synth.router_weight(0, 0, c["n_experts"], H),
                     expert_record=lambda e: synth.expert_record(0, 0, e, H, I),
                     shared=[synth.shared_expert(0, 0, s, H, I) for s in range(c["n_shared"])],
@@ -202,6 +210,8 @@ def main():
     n_distinct = n_layers
     for l in range(n_distinct):
         d = SD.upload_layer(c, seed=0, layer=l, bias=bool(cfgd.get("bias")))
+        if cfgd.get("favor"):  # diagnostic: every token's top-16 among the favoured experts
+            d["router_bias"][: cfgd["favor"]] += 20.0
         L = b.Layer.from_canonical(H, I, E, k, d["router_w"], d["experts"], d["shared_gate"],
                                    d["shared_up"], d["shared_down"], d["router_bias"])
         del d  # canonical copies are not needed once packed
@@ -283,15 +293,22 @@ def main():
     b.profile_events(None, 0)
     kern_us = {n: float(np.mean(v)) for n, v in per_kernel.items() if v}
     dom = max(kern_us, key=kern_us.get)
+    D0 = D[:prof_steps, 0]
+    dom_bytes = float(np.mean([kernel_bytes(dom, T, k, d, S) for d in D0]))
     mfma_info = None
     if mfma:
         f8, f16 = mfma_flops(dom, T, k, S)
-        mfma_info = {"kernel": dom, "fp4xfp8_tflops": round(f8 / (kern_us[dom] * 1e-6) / 1e12, 1),
-                     "frac_of_fp8_peak": round(f8 / (kern_us[dom] * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
-                     "frac_of_fp4_peak": round(f8 / (kern_us[dom] * 1e-6) / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4),
-                     "bf16_tflops_same_launch": round(f16 / (kern_us[dom] * 1e-6) / 1e12, 1)}
-    D0 = D[:prof_steps, 0]
-    dom_bytes = float(np.mean([kernel_bytes(dom, T, k, d, S) for d in D0]))
+        t_dom = kern_us[dom] * 1e-6
+        # the launch's bounding roof: its bytes at the HBM peak or its MFMA work
+        # at the dense peaks (routed at the MXFP8 rate, shared at bf16), whichever is longer
+        t_bound = max(dom_bytes / (HBM_PEAK_GBS * 1e9),
+                      f8 / (FP8_MFMA_PEAK_TFLOPS * 1e12) + f16 / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        mfma_info = {"kernel": dom, "fp4xfp8_tflops": round(f8 / t_dom / 1e12, 1),
+                     "frac_of_fp8_peak": round(f8 / t_dom / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                     "frac_of_fp4_peak": round(f8 / t_dom / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4),
+                     "bf16_tflops_same_launch": round(f16 / t_dom / 1e12, 1),
+                     "bounding_roof_us": round(t_bound * 1e6, 1),
+                     "frac_of_bounding_roof": round(t_bound / t_dom, 4)}
     achieved = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
 
     traffic = None
@@ -300,6 +317,20 @@ def main():
         pmc = json.load(open(pmc_path))
         if pmc.get("source_hash") == source_hash():
             traffic = pmc.get("bytes_per_launch")
+
+    # the box's practical HBM ceiling: a plain 1 GiB device-to-device copy
+    # (read + write bytes over its time), outside the timed region
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = round(5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
+    del src, dst
 
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -322,7 +353,9 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp4*mxfp8->f32" if mfma else "mxfp4*bf16->f32",
         "data": "synthetic (seeded; codes uniform, E8M0 118..126, N(0,0.02) bf16 router/shared, N(0,1) tokens"
-                + (", logit bias N(0,0.5))" if cfgd.get("bias") else ")"),
+                + ((", logit bias N(0,0.5)" + (f", +20 on experts 0..{cfgd['favor'] - 1}"
+                                                  if cfgd.get("favor") else "") + ")")
+                   if cfgd.get("bias") else ")"),
         "config": {"workload": cfgd["desc"], "tokens_per_step": T, "layers": n_layers,
                    "resident_copies": len(layers), "path": "mfma" if mfma else "gemv"},
         "expert_weight_gbs": round(float(exp_gbs), 1),
@@ -330,6 +363,10 @@ def main():
         "distinct_experts_mean": round(float(D.mean()), 2),
         "kernel_us": {n: round(v, 2) for n, v in kern_us.items()},
         "layer_span_us_events": round(float(np.mean(span)), 2),
+        "layer_span_us_median": round(float(np.median(span)), 2),
+        "layer_span_us_iqr": [round(float(np.percentile(span, 25)), 2),
+                              round(float(np.percentile(span, 75)), 2)],
+        "hbm_copy_gbs": copy_gbs,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": round(dom_bytes)},
