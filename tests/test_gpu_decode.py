@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 RAGGED = dict(hidden=288, inter=96, n_experts=40, top_k=5, n_shared=2)
 WIDE = dict(hidden=8192, inter=64, n_experts=24, top_k=3, n_shared=1)
 MANY = dict(hidden=128, inter=32, n_experts=1024, top_k=32, n_shared=0)
+# every expert selected by every token (k = E), and a wide intermediate
+ALL = dict(hidden=256, inter=128, n_experts=8, top_k=8, n_shared=1)
+WIDE_I = dict(hidden=256, inter=2048, n_experts=16, top_k=4, n_shared=1)
 
 
 @pytest.fixture(scope="module")
@@ -181,7 +184,8 @@ def test_forward_tiny_given_oracle_routing(b, tiny, T):
     check_parity(y, ref)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY], ids=["tiny", "ragged", "wide", "many"])
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY, ALL, WIDE_I],
+                         ids=["tiny", "ragged", "wide", "many", "all", "wide_i"])
 @pytest.mark.parametrize("T", [1, 4, 7, 70])
 def test_layer_matches_oracle(b, cfg, T):
     built = Built(cfg, seed=11)

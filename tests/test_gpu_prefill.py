@@ -26,6 +26,7 @@ RAGGED = dict(hidden=288, inter=96, n_experts=40, top_k=5, n_shared=2)
 WIDE = dict(hidden=8192, inter=64, n_experts=24, top_k=3, n_shared=1)
 MANY = dict(hidden=128, inter=32, n_experts=1024, top_k=32, n_shared=0)
 MID = dict(hidden=1024, inter=512, n_experts=16, top_k=4, n_shared=1)
+ALL = dict(hidden=256, inter=128, n_experts=8, top_k=8, n_shared=1)  # k = E
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +46,8 @@ def _forward(b, built, x_dev, ids_np, w_np, residual=None):
     return to_np_u16(y)
 
 
-@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY, MID],
-                         ids=["tiny", "ragged", "wide", "many", "mid"])
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED, WIDE, MANY, MID, ALL],
+                         ids=["tiny", "ragged", "wide", "many", "mid", "all"])
 @pytest.mark.parametrize("T", [1, 7, 70, 200])
 def test_mfma_forward_matches_oracle_mxfp8(b, cfg, T):
     built = Built(cfg, seed=21)
