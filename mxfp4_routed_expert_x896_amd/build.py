@@ -34,6 +34,10 @@ CFLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register
+    # allocator rotates the prefill GEMM's accumulators through copies inside
+    # its main loop and the kernel drops to one wave per SIMD
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -327,15 +327,23 @@ int xcd_grid(int n_pairs, int64_t T) { return 8 * ((n_pairs + 7) / 8) * n_token_
 // (scaled MFMA) + shared gate/up (bf16 MFMA); routed down -> per-pair
 // partials + shared down; combine.  Segments before an XCD-ordered role are
 // padded to multiples of 8 so its block index keeps the XCD of blockIdx.
+// Blocks of a prefill GEMM launch over mt token tiles and tiles_r row tiles:
+// the XCD-grouped order of the launch (kMxGroup token tiles per XCD visit)
+// needs whole rounds of 8 groups.
+int mx_blocks(int mt, int tiles_r) {
+  const int round = 8 * moe::kMxGroup;
+  return round * ((mt + round - 1) / round) * tiles_r;
+}
+
 int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hipStream_t stream) {
   const int S = L->n_shared, mt = max_mtiles(L, T);
   moe::Stage s2;
-  s2.n_mgu = 8 * ((mt + 7) / 8) * ((L->inter + 127) / 128);  // XCD-grouped (see layer.hip)
+  s2.n_mgu = mx_blocks(mt, (L->inter + 127) / 128);
   s2.n_sgmx = S > 0 ? xcd_grid(S * ((L->inter + 127) / 128), T) : 0;
   int st = stage(moe::StageKind::MxGateUp, G, s2, stream);
   if (st) return st;
   moe::Stage s3;
-  s3.n_mdn = 8 * ((mt + 7) / 8) * ((L->hidden + 255) / 256);
+  s3.n_mdn = mx_blocks(mt, (L->hidden + 255) / 256);
   s3.n_sdmx = S > 0 ? xcd_grid(S * ((L->hidden + 255) / 256), T) : 0;
   if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
   moe::Stage s4;

@@ -11,6 +11,8 @@ namespace moe {
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
+// Consecutive prefill token tiles that one XCD runs side by side.
+constexpr int kMxGroup = 4;
 
 // Everything the layer kernels need (layer.hip).
 struct GemvLayer {

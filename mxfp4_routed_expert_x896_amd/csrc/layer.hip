@@ -853,18 +853,30 @@ __device__ __forceinline__ bool mx_tile(const GemvLayer& L, int ti, MxTile& t) {
   return true;
 }
 
+// Block b of a prefill GEMM launch -> (token tile, row tile rt of tiles_r).
+// Blocks are dealt to the 8 XCDs round-robin (XCD b % 8), so each XCD takes
+// groups of kMxGroup consecutive token tiles and runs every row tile of the
+// group, the group's tiles side by side: the row tiles of a token tile read
+// its activations from one L2, and consecutive token tiles of one expert
+// (one in three experts has several at 4096 tokens) read each weight row
+// tile within a few blocks of each other, so all but the first come from L2.
+// The launch has 8 kMxGroup ceil(tiles / (8 kMxGroup)) tiles_r blocks.
+__device__ __forceinline__ bool mx_unit(const GemvLayer& L, int b, int tiles_r, MxTile& t,
+                                        int& rt) {
+  const int i = b / 8, rem = i % (kMxGroup * tiles_r);
+  rt = rem / kMxGroup;
+  return mx_tile(L, kMxGroup * (b % 8 + 8 * (i / (kMxGroup * tiles_r))) + rem % kMxGroup, t);
+}
+
 // Prefill gate/up: workgroup = (token tile, 128 rows of I); wave w takes row
 // groups 2 w, 2 w + 1 of gate and up (4 A streams) against the tile's 64
 // tokens.  Epilogue: h = SiLU(g) * u in fp32, then MXFP8 along I -- the
 // wave's 32 rows are exactly one block per token.
 __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int tiles_r = (L.I + 127) / 128;
-  // the row tiles of one token tile share an XCD (b % 8), so its staged
-  // activations come from that XCD's L2 after the first
   MxTile tt;
-  const int i = b / 8;
-  if (!mx_tile(L, b % 8 + 8 * (i / tiles_r), tt)) return;
-  const int rt = i % tiles_r;
+  int rt;
+  if (!mx_unit(L, b, tiles_r, tt, rt)) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -877,28 +889,31 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
                             L.experts + size_t(e) * L.stride + pm.bytes};
   mx::AStreams st;
   st.nkb = pm.nkb;
+  st.lane_code = 16 * lane;
+  st.lane_scl = lane * pm.nkb4;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
     const int rg = min(rg0 + (s & 1), ngroups - 1);
-    st.codes[s] = base[s >> 1] + size_t(rg) * pm.nkb * 1024 + 16 * lane;
-    st.scl[s] = base[s >> 1] + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+    st.codes[s] = base[s >> 1] + size_t(rg) * pm.nkb * 1024;
+    st.scl[s] = base[s >> 1] + pm.code_bytes + size_t(rg) * 64 * pm.nkb4;
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
   auto tok = [&](int j) { return pairs[j] / L.k; };
   mx::f32x4 acc[mx::kNS][mx::kSub];
   mx::gemm_tile(
-      acc, st, pm.nkb4 / 4, lds, [&](int j) { return L.xq + size_t(tok(j)) * L.Kq; },
-      [&](int j) { return L.xs + size_t(tok(j)) * (L.Kq / 32); });
+      acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs,
+      [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq); },
+      [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq / 32); });
   if (rt == tiles_r - 1 && L.Iq > I) {
     // h columns I .. Iq are read by the down GEMM against clamped weight
     // tiles: zero codes with a finite exponent make them contribute 0
     const int pad16 = (L.Iq - I) / 16, pad_blocks = (L.Iq - I) / 32;
     for (int i = threadIdx.x; i < tt.mt * pad16; i += kThreads)
-      *reinterpret_cast<u32x4*>(L.hq + size_t(pairs[i / pad16]) * L.Iq + I + 16 * (i % pad16)) =
+      *reinterpret_cast<u32x4*>(L.hq + size_t(tt.p0 + i / pad16) * L.Iq + I + 16 * (i % pad16)) =
           u32x4{0, 0, 0, 0};
     for (int i = threadIdx.x; i < tt.mt * pad_blocks; i += kThreads)
-      L.hs8[size_t(pairs[i / pad_blocks]) * (L.Iq / 32) +
+      L.hs8[size_t(tt.p0 + i / pad_blocks) * (L.Iq / 32) +
             mx::scale_pos(I / 32 + i % pad_blocks)] = 127;
   }
   if (rg0 >= ngroups) return;  // no rows for this wave (I not a multiple of 128)
@@ -919,8 +934,8 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
     const int E = mxfp8_block_exp(amax);
     const int j = 16 * u + c;
     if (j < tt.mt) {
-      const int pair = pairs[j];
-      uint8_t* hrow = L.hq + size_t(pair) * L.Iq + rt * 128 + 32 * wave;
+      const int pos = tt.p0 + j;  // h rows in plan order: a tile's rows are contiguous
+      uint8_t* hrow = L.hq + size_t(pos) * L.Iq + rt * 128 + 32 * wave;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         uint32_t word = 0;
@@ -928,7 +943,7 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
         for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(__builtin_ldexpf(h[r][i], -E)) << (8 * i);
         *reinterpret_cast<uint32_t*>(hrow + 16 * r + 4 * g) = word;
       }
-      if (g == 0) L.hs8[size_t(pair) * (L.Iq / 32) + mx::scale_pos(blk)] = uint8_t(E + 127);
+      if (g == 0) L.hs8[size_t(pos) * (L.Iq / 32) + mx::scale_pos(blk)] = uint8_t(E + 127);
     }
   }
 }
@@ -937,10 +952,9 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
 // groups 4 w .. 4 w + 3.  Writes fp32 partials per pair (combined later).
 __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int tiles_r = (L.H + 255) / 256;
-  MxTile tt;  // XCD-grouped like the gate/up
-  const int i = b / 8;
-  if (!mx_tile(L, b % 8 + 8 * (i / tiles_r), tt)) return;
-  const int rt = i % tiles_r;
+  MxTile tt;
+  int rt;
+  if (!mx_unit(L, b, tiles_r, tt, rt)) return;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -952,18 +966,22 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
   mx::AStreams st;
   st.nkb = pd.nkb;
+  st.lane_code = 16 * lane;
+  st.lane_scl = lane * pd.nkb4;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
     const int rg = min(rg0 + s, ngroups - 1);
-    st.codes[s] = base + size_t(rg) * pd.nkb * 1024 + 16 * lane;
-    st.scl[s] = base + pd.code_bytes + (size_t(rg) * 64 + lane) * pd.nkb4;
+    st.codes[s] = base + size_t(rg) * pd.nkb * 1024;
+    st.scl[s] = base + pd.code_bytes + size_t(rg) * 64 * pd.nkb4;
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
   mx::f32x4 acc[mx::kNS][mx::kSub];
   mx::gemm_tile(
-      acc, st, pd.nkb4 / 4, lds, [&](int j) { return L.hq + size_t(pairs[j]) * L.Iq; },
-      [&](int j) { return L.hs8 + size_t(pairs[j]) * (L.Iq / 32); });
+      acc, st, pd.nkb4 / 4, lds, tt.mt, L.hq + size_t(tt.p0) * L.Iq,
+      L.hs8 + size_t(tt.p0) * (L.Iq / 32),
+      [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq); },
+      [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq / 32); });
 #pragma unroll
   for (int u = 0; u < mx::kSub; ++u) {
     const int j = 16 * u + c;

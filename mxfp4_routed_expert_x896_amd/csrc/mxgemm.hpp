@@ -35,14 +35,17 @@ namespace mx {
 constexpr int kTok = kPlanTileTokens;  // tokens (B columns) per tile, 4 MFMA column groups
 constexpr int kSub = kTok / 16;
 constexpr int kStep = 512;             // contraction columns per super-step (4 tiles)
-constexpr int kRowB = kStep + 16;      // staged bytes per token and step: codes + 16 scale bytes
-constexpr int kStageBytes = kTok * kRowB;  // 33 KiB: 33 wave-wide 1 KiB loads
+constexpr int kStageBytes = kTok * kStep;  // 32 KiB of activation codes per staging buffer
 constexpr int kNS = 4;                 // A streams (16-row groups x matrices) per wave
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
+
+// s_waitcnt vmcnt(16) with expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kVmcnt16 = (1 << 14) | (7 << 4) | (15 << 8);
 
 // Position of the scale byte of block b (along the contraction) in the
 // MFMA-ordered scale row (see the header comment).
@@ -64,11 +67,14 @@ struct ATiles {
   uint32_t s[kNS];
 };
 
-// Streams of a wave: code tiles of a 16-row group (base + 16 lane) and the
-// lane's exponent bytes (nkb4 per lane, tile kb at byte kb).
+// Streams of a wave: code tiles of a 16-row group and the lane's exponent
+// bytes (nkb4 per lane, tile kb at byte kb).  The stream bases are uniform
+// across the wave; the lane's part is a 32-bit offset shared by all streams
+// (16 lane into a code tile, lane nkb4 into the exponents).
 struct AStreams {
   const uint8_t* codes[kNS];
   const uint8_t* scl[kNS];
+  uint32_t lane_code, lane_scl;
   int nkb;
 };
 
@@ -77,92 +83,188 @@ __device__ __forceinline__ void load_a(ATiles& t, const AStreams& st, int kq) {
   for (int s = 0; s < kNS; ++s) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      t.w[s][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          st.codes[s] + size_t(min(4 * kq + j, st.nkb - 1)) * 1024));
-    t.s[s] = *reinterpret_cast<const uint32_t*>(st.scl[s] + 4 * kq);
+      t.w[s][j] = *(reinterpret_cast<const u32x4*>(
+          st.codes[s] + size_t(min(4 * kq + j, st.nkb - 1)) * 1024 + st.lane_code));
+    t.s[s] = *reinterpret_cast<const uint32_t*>(st.scl[s] + 4 * kq + st.lane_scl);
   }
 }
 
-// Issues the wave's share of one super-step of activations straight into
-// LDS (no registers): 33 wave-wide 16-byte-per-lane loads fill kTok token
-// rows of kRowB bytes; wave w issues loads w, w + 4, ...  row(j) gives
-// token j's code row (kStep bytes of this step at +kq * kStep) and srow(j)
-// its MFMA-ordered scale row (16 bytes of this step at +kq * 16).
-template <typename Row, typename SRow>
-__device__ __forceinline__ void stage_b(uint8_t* lds, int kq, Row row, SRow srow) {
+// Staged activations: token j's kStep code bytes of a super-step as 32
+// 16-byte chunks, chunk q at slot q ^ (j % 16) of the token's 512-byte LDS
+// row.  The 16 lanes that read the same chunk of 16 consecutive tokens then
+// hit 16 different bank groups, and a wave-wide staging load still fills
+// 1 KiB of LDS contiguously (two token rows).
+//
+// Per lane, as 32-bit byte offsets from the wave-uniform bases: the global
+// chunk each of the wave's 2 NSub staging loads fetches at super-step 0
+// (wave w issues loads w, w + 4, ..., covering the first 16 NSub tokens),
+// and the B exponent dword of each of its token groups.
+template <int NSub>
+struct BStage {
+  const uint8_t* cbase;
+  const uint8_t* sbase;
+  uint32_t src[2 * NSub];
+  uint32_t scl[NSub];
+};
+
+// row(j): token j's code row as a byte offset from cbase; srow(j): its
+// MFMA-ordered exponent row as a byte offset from sbase.
+template <int NSub, typename Row, typename SRow>
+__device__ __forceinline__ void prepare_b(BStage<NSub>& bs, const uint8_t* cbase,
+                                          const uint8_t* sbase, Row row, SRow srow) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
-  for (int n = wave; n < kStageBytes / 1024; n += 4) {
-    const int chunk = n * 64 + lane;  // 16-byte chunk of the staged block
-    const int j = chunk / (kRowB / 16), q = chunk % (kRowB / 16);
-    const uint8_t* src = q < kStep / 16 ? row(j) + size_t(kq) * kStep + 16 * q
-                                        : srow(j) + size_t(kq) * 16;
-    __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(lds + n * 1024), 16, 0, 0);
+  const int g = lane / 16, c = lane % 16;
+  bs.cbase = cbase;
+  bs.sbase = sbase;
+#pragma unroll
+  for (int i = 0; i < 2 * NSub; ++i) {
+    const int j = 2 * (wave + 4 * i) + lane / 32;  // token of this lane's LDS chunk
+    bs.src[i] = row(j) + 16 * ((lane % 32) ^ (j % 16));
   }
+#pragma unroll
+  for (int u = 0; u < NSub; ++u) bs.scl[u] = srow(16 * u + c) + 4 * g;
 }
 
-// acc[s][u] += A stream s (this step's 4 tiles) x B columns 16 u .. 16 u + 15.
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[kNS][kSub], const ATiles& a,
-                                         const uint8_t* lds) {
+// One wave-wide 16-byte-per-lane load from global memory (base + lane's
+// off) straight into LDS (lane l's bytes land at lds_addr + 16 l).  Issued
+// as inline assembly so that the compiler's wait-count bookkeeping, which
+// cannot order such loads against ordinary loads and would then wait for
+// every load before the next MFMA, does not see it: the caller waits for it
+// explicitly.  s_nop: one wait state between writing M0 and a load that
+// reads it.
+__device__ __forceinline__ void load_to_lds16(const uint8_t* base, uint32_t off,
+                                              uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+template <int NSub>
+__device__ __forceinline__ void stage_b(uint8_t* lds, int kq, const BStage<NSub>& bs) {
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const uint8_t* base = bs.cbase + size_t(kq) * kStep;
+  const uint32_t l0 = uint32_t(reinterpret_cast<uintptr_t>((lvoid*)lds));
+#pragma unroll
+  for (int i = 0; i < 2 * NSub; ++i)
+    load_to_lds16(base, bs.src[i], __builtin_amdgcn_readfirstlane(l0 + (wave + 4 * i) * 1024));
+}
+
+// B operand of tile J for token group u: token 16 u + c, bytes K = 16 g ..
+// 16 g + 15 (chunk 8 J + g) and K = 64 + 16 g .. (chunk 8 J + 4 + g).
+__device__ __forceinline__ i32x8 read_b(const uint8_t* buf, int u, int J) {
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
-#pragma unroll
-  for (int u = 0; u < kSub; ++u) {
-    const uint8_t* r = lds + (16 * u + c) * kRowB;
-    const uint32_t sb = *reinterpret_cast<const uint32_t*>(r + kStep + 4 * g);
-#define MX_TILE(J)                                                                        \
-  {                                                                                      \
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + 128 * J + 16 * g);             \
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 128 * J + 64 + 16 * g);        \
-    const i32x8 b = {int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),                     \
-                     int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};                    \
-    _Pragma("unroll") for (int s = 0; s < kNS; ++s) acc[s][u] =                          \
-        mma<J>(a.w[s][J], b, acc[s][u], a.s[s], sb);                                     \
-  }
-    MX_TILE(0)
-    MX_TILE(1)
-    MX_TILE(2)
-    MX_TILE(3)
-#undef MX_TILE
-  }
+  const uint8_t* r = buf + (16 * u + c) * kStep;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + g) ^ c));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + 4 + g) ^ c));
+  return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+               int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
 }
 
-// The contraction of one tile: nkq super-steps, A double-buffered in
-// registers, B double-buffered in LDS (two kStageBytes buffers at lds).
-// All threads of the workgroup must call it.
-template <typename Row, typename SRow>
-__device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], const AStreams& st, int nkq,
-                                          uint8_t* lds, Row row, SRow srow) {
+// The contraction of one tile over nkq super-steps, for the first NSub
+// 16-token groups.  B (activation codes) is double-buffered in LDS; A
+// (weights) is single-buffered in registers and reloaded tile by tile: tile
+// J of step kq + 1 is requested as soon as the MFMAs of tile J of step kq
+// have read it, so each weight load has a whole step to arrive while only
+// one step's weights occupy registers; the exponent dwords of A and B (a
+// few registers) are double-buffered and requested at the start of the step
+// before the one that uses them.  B operands are read from LDS two (tile, token
+// group) pairs ahead of the MFMAs that use them.  Every wave issues the same loads in the same
+// order, so one counted wait per step covers the staging.
+template <int NSub, typename Row, typename SRow>
+__device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStreams& st, int nkq,
+                                            uint8_t* lds, const uint8_t* cbase,
+                                            const uint8_t* sbase, Row row, SRow srow) {
 #pragma unroll
   for (int s = 0; s < kNS; ++s)
 #pragma unroll
     for (int u = 0; u < kSub; ++u) acc[s][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  ATiles ta, tb;
-  stage_b(lds, 0, row, srow);
-  load_a(ta, st, 0);
+  BStage<NSub> bs;
+  prepare_b(bs, cbase, sbase, row, srow);
+  ATiles a;
+  uint32_t sb[NSub];
+  stage_b(lds, 0, bs);
+  load_a(a, st, 0);
+#pragma unroll
+  for (int u = 0; u < NSub; ++u) sb[u] = *reinterpret_cast<const uint32_t*>(bs.sbase + bs.scl[u]);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  auto step = [&](ATiles& cur, ATiles& nxt, int kq) {
-    // loads of step kq + 1: activations into the other LDS buffer, weights
-    // into the other registers; both in flight while step kq computes
-    uint8_t* cur_l = lds + (kq & 1) * kStageBytes;
-    uint8_t* nxt_l = lds + ((kq + 1) & 1) * kStageBytes;
-    stage_b(nxt_l, kq + 1, row, srow);
-    load_a(nxt, st, kq + 1);
-    mma_step(acc, cur, cur_l);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  auto step = [&](int kq, auto reload) {
+    constexpr bool kReload = decltype(reload)::value;
+    constexpr int kGroups = 4 * NSub;  // (tile J, token group u) pairs, J major
+    const uint8_t* cur = lds + (kq & 1) * kStageBytes;
+    const int kn = kq + 1;
+    uint32_t as_n[kNS], sb_n[NSub];  // exponent dwords of step kq + 1
+    if constexpr (kReload) {
+      stage_b(lds + (kn & 1) * kStageBytes, kn, bs);
+#pragma unroll
+      for (int s = 0; s < kNS; ++s)
+        as_n[s] = *reinterpret_cast<const uint32_t*>(st.scl[s] + 4 * kn + st.lane_scl);
+#pragma unroll
+      for (int u = 0; u < NSub; ++u)
+        sb_n[u] = *reinterpret_cast<const uint32_t*>(bs.sbase + 16 * kn + bs.scl[u]);
+    }
+    i32x8 b[3];  // B operands of groups gi, gi + 1, gi + 2
+    b[0] = read_b(cur, 0, 0);
+    if (kGroups > 1) b[1] = read_b(cur, 1 % NSub, 1 / NSub);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      const int J = gi / NSub, u = gi % NSub;
+      if (gi + 2 < kGroups) b[(gi + 2) % 3] = read_b(cur, (gi + 2) % NSub, (gi + 2) / NSub);
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) {
+        switch (J) {  // opsel J is an immediate
+          case 0: acc[s][u] = mma<0>(a.w[s][0], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          case 1: acc[s][u] = mma<1>(a.w[s][1], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          case 2: acc[s][u] = mma<2>(a.w[s][2], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          default: acc[s][u] = mma<3>(a.w[s][3], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+        }
+      }
+      if constexpr (kReload) {
+        if (u == NSub - 1) {
+#pragma unroll
+          for (int s = 0; s < kNS; ++s)
+            a.w[s][J] = *(reinterpret_cast<const u32x4*>(
+                st.codes[s] + size_t(min(4 * kn + J, st.nkb - 1)) * 1024 + st.lane_code));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kReload) {
+#pragma unroll
+      for (int s = 0; s < kNS; ++s) a.s[s] = as_n[s];
+#pragma unroll
+      for (int u = 0; u < NSub; ++u) sb[u] = sb_n[u];
+      // The staging loads for kq + 1 were issued before this step's 20 + NSub
+      // exponent and weight loads; vector loads complete in order, so at most
+      // 16 outstanding means every staging load has landed in LDS.  A fenced
+      // barrier would wait for all loads: the memory model orders the
+      // staging's LDS writes with vmcnt(0).
+      __builtin_amdgcn_s_waitcnt(kVmcnt16);
+      asm volatile("s_barrier" ::: "memory");
+    }
   };
   int kq = 0;
-  for (; kq + 2 < nkq; kq += 2) {
-    step(ta, tb, kq);
-    step(tb, ta, kq + 1);
-  }
-  if (kq + 1 < nkq) {
-    step(ta, tb, kq);
-    mma_step(acc, tb, lds + ((kq + 1) & 1) * kStageBytes);
-  } else {
-    mma_step(acc, ta, lds + (kq & 1) * kStageBytes);
+  for (; kq + 1 < nkq; ++kq) step(kq, std::true_type{});
+  step(kq, std::false_type{});
+}
+
+// Only the 16-token column groups that hold tokens are staged and multiplied
+// (ntok = the tile's token count, 1 .. kTok); the other groups keep acc = 0.
+// All threads of the workgroup must call it.
+template <typename Row, typename SRow>
+__device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], const AStreams& st, int nkq,
+                                          uint8_t* lds, int ntok, const uint8_t* cbase,
+                                          const uint8_t* sbase, Row row, SRow srow) {
+  static_assert(kSub == 4, "one instantiation per group count");
+  switch (__builtin_amdgcn_readfirstlane((ntok + 15) / 16)) {
+    case 1: gemm_tile_n<1>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    case 2: gemm_tile_n<2>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    case 3: gemm_tile_n<3>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    default: gemm_tile_n<4>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
   }
 }
 
