@@ -64,6 +64,11 @@ __device__ __forceinline__ u32x4 ld_nt(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+template <bool kReuse>
+__device__ __forceinline__ u32x4 ld_w(const void* p) {
+  if constexpr (kReuse) return ld16(p);
+  else return ld_nt(p);
+}
 
 __device__ __forceinline__ f32x4_t mfma(const u32x4& a, const u32x4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -393,6 +398,10 @@ constexpr int kSharedDownStages = 3;
 // straight from the token rows, which every workgroup shares through L2:
 // per tile it is as many bytes as the weights, so no LDS staging (and no
 // cap on tokens per pass from the LDS size) is needed.
+// kReuse: more than one pass of tokens, so the weights are loaded with the
+// default cache policy and later passes find them in the caches; a single
+// pass streams them past the caches.
+template <bool kReuse>
 __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -417,8 +426,8 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int u = min(4 * q + j, nu - 1);  // past the end: skipped below
-        t.g[j] = ld_nt(gt + size_t(u) * 512 + 8 * lane);
-        t.u[j] = ld_nt(ut + size_t(u) * 512 + 8 * lane);
+        t.g[j] = ld_w<kReuse>(gt + size_t(u) * 512 + 8 * lane);
+        t.u[j] = ld_w<kReuse>(ut + size_t(u) * 512 + 8 * lane);
         t.x[j] = ld16(xrow + u * 32);
       }
     };
@@ -538,6 +547,7 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   }
 }
 
+template <bool kReuse>  // as for shared_gateup
 __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -562,7 +572,7 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int u = min(4 * q + j, nu - 1);  // past the end: skipped below
-        t.w[j] = ld_nt(dt + size_t(u) * 512 + 8 * lane);
+        t.w[j] = ld_w<kReuse>(dt + size_t(u) * 512 + 8 * lane);
         t.h[j] = ld16(hrow + u * 32);
       }
     };
@@ -1214,14 +1224,16 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   const int gu_tiles = L.I / 32;
   if constexpr ((R & kRoleSharedGU) != 0) {
     if (b < st.n_sgu) {
-      shared_gateup(L, b / (L.I / 16), b % (L.I / 16), red);
+      if (L.T > kCols) shared_gateup<true>(L, b / (L.I / 16), b % (L.I / 16), red);
+      else shared_gateup<false>(L, b / (L.I / 16), b % (L.I / 16), red);
       return;
     }
     b -= st.n_sgu;
   }
   if constexpr ((R & kRoleSharedDown) != 0) {
     if (b < st.n_sdn) {
-      shared_down(L, b / L.n_stiles, b % L.n_stiles);
+      if (L.T > kCols / 2) shared_down<true>(L, b / L.n_stiles, b % L.n_stiles);
+      else shared_down<false>(L, b / L.n_stiles, b % L.n_stiles);
       return;
     }
     b -= st.n_sdn;
