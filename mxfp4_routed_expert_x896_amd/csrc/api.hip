@@ -109,6 +109,11 @@ int max_mtiles(const moe_layer_desc* L, int64_t T) {
 int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
 
 int n_logit_wgs(const moe_layer_desc* L) { return (L->n_experts + 3) / 4; }
+// Router workgroups of the GEMV path for T tokens (see lsplit).
+int router_split(int64_t T) { return T >= moe::kRouterSplitMin ? moe::kRouterSplit : 1; }
+int n_router_wgs(const moe_layer_desc* L, int64_t T) {
+  return router_split(T) > 1 ? (L->n_experts + 15) / 16 * moe::kRouterSplit : n_logit_wgs(L);
+}
 
 // A value no earlier call stored in the logits flags: odd numbers from a
 // per-process start, so it is never 0 (the cleared state).
@@ -136,7 +141,7 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
     return at;
   };
   c.lflags = take(uint64_t(n_logit_wgs(L) + 1) * 8);  // first: same place for every T
-  c.logits = take(t * E * 4);
+  c.logits = take(t * E * 4 * (T >= moe::kRouterSplitMin ? moe::kRouterSplit : 1));
   c.n_active = take(4);
   c.active = take(E * 4);
   c.act_off = take((E + 1) * 4);
@@ -191,6 +196,7 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.logits = at<float>(ws, c.logits);
   G.lflags = at<unsigned long long>(ws, c.lflags);
   G.epoch = next_epoch();
+  G.lsplit = 1;
   G.sel_cnt = at<int>(ws, c.sel_cnt);
   G.experts = L->experts;
   G.stride = L->expert_stride;
@@ -235,8 +241,9 @@ int do_route(const moe_layer_desc* L, const uint16_t* x, int64_t T, int32_t* ids
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
   G.ids_out = ids;
   G.w_out = w;
+  G.lsplit = router_split(T);
   moe::Stage s1;
-  s1.n_logits = n_logit_wgs(L);
+  s1.n_logits = n_router_wgs(L, T);
   int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);
   if (st) return st;
   moe::Stage s2;
@@ -282,9 +289,10 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.w = w;
   G.residual = residual;
   G.y = y;
+  G.lsplit = router_split(T);
   const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
   moe::Stage s1;
-  s1.n_logits = n_logit_wgs(L);
+  s1.n_logits = n_router_wgs(L, T);
   s1.n_sgu = S * (L->inter / 16);
   if (n_select_wgs(T) == 1) {
     // up to 4 tokens: the top-k (and for several tokens the plan) runs in

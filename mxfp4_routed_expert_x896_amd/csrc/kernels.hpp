@@ -11,6 +11,11 @@ namespace moe {
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
+// Router logits of kRouterSplitMin or more tokens (GEMV path): bf16 MFMA
+// over kRouterSplit quarters of the contraction, one workgroup per (16
+// experts, quarter).
+constexpr int kRouterSplit = 4;
+constexpr int kRouterSplitMin = 16;
 // Consecutive prefill token tiles that one XCD runs side by side.
 constexpr int kMxGroup = 4;
 
@@ -42,6 +47,10 @@ struct GemvLayer {
   // gave up, else 0 (see select_waits in layer.hip).
   unsigned long long* lflags;
   unsigned long long epoch;
+  // 1: logits[t][e] complete; kRouterSplit: logits holds kRouterSplit partial
+  // sums [q][t][e] over quarters of the contraction (bias in quarter 0),
+  // which the top-k adds in order
+  int lsplit;
   int n_tiles;              // ceil(H / kDownRows) routed down tiles (set by the launcher)
   int n_stiles;             // ceil(H / 64) shared down tiles (set by the launcher)
   int mtp_gu, mtp_d;        // tokens staged per LDS pass (set by the launcher)

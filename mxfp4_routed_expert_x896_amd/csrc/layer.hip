@@ -455,6 +455,59 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
   }
 }
 
+// Router logits of kRouterSplitMin or more tokens: bf16 MFMA with 16 experts'
+// router rows as A, straight from their row-major storage (lane (c, g) reads
+// row c at columns 32 u + 8 g .. + 7, the packed-tile layout), and 16 tokens
+// of x as B from L2.  Workgroup b takes experts 16 (b / kRouterSplit) .. + 15
+// and quarter q = b % kRouterSplit of the contraction; wave w takes slice
+// 4 q + w of 16 slices of the 32-column tiles and keeps its slice of the rows
+// in registers for every token group.  The waves' sums are added in wave
+// order and the quarter's partial logits stored (quarter 0 adds the bias);
+// the top-k adds the quarters in order.  The token rows, not the router
+// rows, are what repeats per token group, and they are L2-resident.
+constexpr int kRsTiles = 16;  // tiles per slice: H <= 8192 = 16 slices x 16 tiles x 32
+__device__ void router_split_role(const GemvLayer& L, int b, float* red) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int H = L.H, E = L.E, T = L.T;
+  const int e0 = (b / kRouterSplit) * 16, q = b % kRouterSplit;
+  const int nt = H / 32;
+  const int sl = q * kWaves + wave;
+  const int t_beg = sl * nt / 16, n_i = (sl + 1) * nt / 16 - t_beg;  // uniform, <= kRsTiles
+  const uint16_t* arow = L.wr + size_t(min(e0 + c, E - 1)) * H + 8 * g;
+  u32x4 a[kRsTiles];
+#pragma unroll
+  for (int i = 0; i < kRsTiles; ++i) a[i] = ld_nt(arow + 32 * min(t_beg + i, nt - 1));
+  float* part = L.logits + size_t(q) * T * E;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const uint16_t* xrow = L.x + size_t(min(t0 + c, T - 1)) * H + 8 * g;
+    u32x4 bx[kRsTiles];
+#pragma unroll
+    for (int i = 0; i < kRsTiles; ++i) bx[i] = ld16(xrow + 32 * min(t_beg + i, nt - 1));
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kRsTiles; ++i)
+      if (i < n_i) acc = mfma(a[i], bx[i], acc);  // uniform
+    __syncthreads();  // red is free
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * kWave + lane) * 4 + r] = acc[r];
+    __syncthreads();
+    if (wave == 0 && t0 + c < T) {
+      // lane (c, g) holds experts e0 + 4 g .. + 3 of token t0 + c
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 4 * g + r;
+        float v = red[lane * 4 + r];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) v += red[(ww * kWave + lane) * 4 + r];
+        if (q == 0 && L.rbias != nullptr && e < E) v += L.rbias[e];
+        if (e < E) part[size_t(t0 + c) * E + e] = v;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------
 // Down projections and the combine.  Workgroups are (expert, tile of kRowsD
 // output rows, 16 per wave); h enters as bf16 hi + lo, staged in LDS (the
@@ -1096,7 +1149,11 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   if (t < L.T) {
     int id;
     float w;
-    select_token<kCoherent>(L.logits + size_t(t) * L.E, L.E, L.k, id, w, sc[wave]);
+    if (L.lsplit == kRouterSplit)
+      select_token<kCoherent, kRouterSplit>(L.logits + size_t(t) * L.E, size_t(L.T) * L.E, L.E,
+                                            L.k, id, w, sc[wave]);
+    else
+      select_token<kCoherent>(L.logits + size_t(t) * L.E, 0, L.E, L.k, id, w, sc[wave]);
     if (lane < L.k) {
       if (single) {
         L.ids_out[size_t(t) * L.k + lane] = id;
@@ -1142,7 +1199,10 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     if (b < st.n_logits) {
       // the select workgroups of the next launch count their arrivals here
       if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
-      router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
+      if (L.lsplit == kRouterSplit)
+        router_split_role(L, b, red);
+      else
+        router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
       if (st.n_selw > 0) {  // logits stored (through the coherent level): flag them
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();

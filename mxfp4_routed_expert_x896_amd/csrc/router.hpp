@@ -148,24 +148,35 @@ __device__ __forceinline__ int wave_prefix_small(int v, int& total) {
 // selection.  If more than kSelCap experts reach M (heavy ties), the token
 // is redone exactly by k rounds of a wave-wide maximum over all keys.
 // kCoherent: the logits were written in the same launch (read past L2).
-template <bool kCoherent = false>
-__device__ __forceinline__ void select_token(const float* __restrict__ lrow, int E, int k,
-                                             int& id, float& w, SelectScratch& sc) {
+// kSplit > 1: lrow is the first of kSplit partial rows pstride floats apart,
+// summed in order.
+template <bool kCoherent = false, int kSplit = 1>
+__device__ __forceinline__ void select_token(const float* __restrict__ lrow, size_t pstride,
+                                             int E, int k, int& id, float& w,
+                                             SelectScratch& sc) {
   const int lane = threadIdx.x % kWave;
   uint32_t val[16];
-  // unconditional loads (clamped address), so all sixteen are in flight at
+  // unconditional loads (clamped address), so all of them are in flight at
   // once; a load under a condition would be waited for on its own
-  float lv[16];
+  float lv[kSplit][16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float* p = lrow + min(lane + kWave * i, E - 1);
-    lv[i] = kCoherent ? load_coherent(p) : *p;
-  }
+  for (int q = 0; q < kSplit; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float* p = lrow + q * pstride + min(lane + kWave * i, E - 1);
+      lv[q][i] = kCoherent ? load_coherent(p) : *p;
+    }
   // the values are taken here, so no load is moved under the condition below
 #pragma unroll
-  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(lv[i]));
+  for (int q = 0; q < kSplit; ++q)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) val[i] = lane + kWave * i < E ? ord_f32(lv[i]) : 0u;
+    for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(lv[q][i]));
+#pragma unroll
+  for (int q = 1; q < kSplit; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lv[0][i] += lv[q][i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) val[i] = lane + kWave * i < E ? ord_f32(lv[0][i]) : 0u;
   uint32_t mx = 0u;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = val[i] > mx ? val[i] : mx;
