@@ -11,11 +11,11 @@ namespace moe {
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
-// Router logits of kRouterSplitMin or more tokens (GEMV path): bf16 MFMA
-// over kRouterSplit quarters of the contraction, one workgroup per (16
-// experts, quarter).
+// Router logits of kRouterSplitMin or more tokens (GEMV path: the batches
+// whose top-k has a launch of its own): bf16 MFMA over kRouterSplit quarters
+// of the contraction, one workgroup per (16 experts, quarter).
 constexpr int kRouterSplit = 4;
-constexpr int kRouterSplitMin = 16;
+constexpr int kRouterSplitMin = 5;
 // Consecutive prefill token tiles that one XCD runs side by side.
 constexpr int kMxGroup = 4;
 
