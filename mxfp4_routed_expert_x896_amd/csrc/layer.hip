@@ -53,6 +53,10 @@ constexpr int kRowsD = kDownRows;  // routed down rows per workgroup (a multiple
 constexpr int kRowsSD = 64;        // shared down rows per workgroup (one row group per wave)
 constexpr int kCols = 16;         // B columns of one MFMA: at most 16 tokens per pass
 constexpr int kLdsBudget = 32768;  // bytes of staged activations per workgroup
+// Routed gate/up: its token rows are H bf16 each (14 KiB at K3); three
+// workgroups per CU (its register limit) leave 53 KiB of LDS each, three K3
+// tokens, so an expert with up to three tokens streams its weights once.
+constexpr int kLdsBudgetGU = 53248;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -1354,8 +1358,8 @@ __global__ __launch_bounds__(kThreads) void moe_combine(GemvLayer L, Stage st) {
   stage_body<kRoleCombine, 0>(L, st);
 }
 
-int tokens_per_pass(int T, int row_bytes) {
-  const int t = kLdsBudget / row_bytes;
+int tokens_per_pass(int T, int row_bytes, int budget) {
+  const int t = budget / row_bytes;
   return max(1, min(min(t, kCols), T));
 }
 
@@ -1367,8 +1371,8 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   L.n_tiles = (L.H + kRowsD - 1) / kRowsD;
   L.n_stiles = (L.H + kRowsSD - 1) / kRowsSD;
   const int xrow = pad_k(L.H) + 8, hrow = pad_k(L.I) + 8;  // staged row lengths
-  L.mtp_gu = tokens_per_pass(L.T, xrow * 2);
-  L.mtp_d = min(tokens_per_pass(L.T, hrow * 4), kCols / 2);  // hi + lo: two B columns per token
+  L.mtp_gu = tokens_per_pass(L.T, xrow * 2, kLdsBudgetGU);
+  L.mtp_d = min(tokens_per_pass(L.T, hrow * 4, kLdsBudget), kCols / 2);  // hi + lo: two B columns per token
   size_t lds = 0;
   if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
   if (st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
