@@ -114,6 +114,8 @@ def test_workspace_grows_with_tokens_and_token_limits(lib):
     s2, b2 = _ws(lib, d, 64)
     assert s1 == 0 and s2 == 0 and b2 > b1
     assert _ws(lib, d, 0)[0] == -1
+    assert _ws(lib, d, 1 << 16)[0] == 0   # the largest batch one call takes
+    assert _ws(lib, d, (1 << 16) + 1)[0] == -3
     assert _ws(lib, d, 1 << 17)[0] == -3
 
 

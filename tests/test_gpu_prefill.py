@@ -17,8 +17,8 @@ import synth
 import synth.device as SD
 from oracle import moe as M
 
-from tests._gpu import (Built, check_mxfp8_parity, check_routing, mxfp8_h_flip_allowance,
-                        oracle_weights, rel_l2_per_token, to_np_u16)
+from tests._gpu import (Built, check_mxfp8_parity, check_parity, check_routing,
+                        mxfp8_h_flip_allowance, oracle_weights, rel_l2_per_token, to_np_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,36 @@ def test_mfma_residual_and_layer_entry(b):
     wref = oracle_weights(s, ids_np)
     ref = M.moe_forward(xh, built.oracle, ids_np, wref, act_mxfp8=True, residual_bits=rh)
     check_mxfp8_parity(to_np_u16(y), ref, mxfp8_h_flip_allowance(xh, built.oracle, ids_np, wref))
+
+
+@pytest.mark.parametrize("path", ["mfma", "gemv"])
+def test_layer_at_the_token_limit(b, path):
+    # 65,536 tokens, the most one call takes (about 128 64-token tiles per
+    # expert at the tiny shape), on either path; routing and output checked
+    # on a sample of tokens spread over the batch, the first and last included
+    cfg = synth.TINY
+    built = Built(cfg, seed=25, bias=True)
+    T = 1 << 16
+    xh, xd = SD.upload_tokens(1480, T, cfg["hidden"])
+    k = cfg["top_k"]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, cfg["hidden"]), dtype=torch.int16, device="cuda")
+    b.moe_layer(built.lib, xd, y, ids, w, built.lib.workspace(T),
+                path=b.PATH_MFMA if path == "mfma" else b.PATH_GEMV)
+    torch.cuda.synchronize()
+    sample = np.unique(np.concatenate([np.arange(0, T, 251), [T - 1]]))
+    ids_np, w_np = ids.cpu().numpy()[sample], w.cpu().numpy()[sample]
+    xs = np.ascontiguousarray(xh[sample])
+    _, _, s = M.route(xs, built.oracle)
+    check_routing(ids_np, w_np, s, k)
+    wref = oracle_weights(s, ids_np)
+    if path == "mfma":
+        ref = M.moe_forward(xs, built.oracle, ids_np, wref, act_mxfp8=True)
+        check_mxfp8_parity(to_np_u16(y)[sample], ref,
+                           mxfp8_h_flip_allowance(xs, built.oracle, ids_np, wref))
+    else:
+        check_parity(to_np_u16(y)[sample], M.moe_forward(xs, built.oracle, ids_np, wref))
 
 
 def test_mfma_and_gemv_paths_agree_closely(b):
