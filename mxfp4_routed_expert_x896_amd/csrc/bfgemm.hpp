@@ -42,6 +42,19 @@ struct ATiles {
   u32x4 w[kNS][4];
 };
 
+// One wave-wide 16-byte-per-lane load from global memory straight into LDS
+// (lane l's bytes land at lds_addr + 16 l), issued as inline assembly so the
+// compiler's wait-count bookkeeping, which cannot order such loads against
+// ordinary loads and would wait for all of them before the next product,
+// does not see it; the caller waits for it explicitly.  s_nop: one wait
+// state between writing M0 and a load that reads it.
+__device__ __forceinline__ void load_to_lds16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Stages super-step kq of NB token sources (rows of K bf16) into NB LDS
 // buffers of kStageBytes: 17 wave-wide loads each, wave w issuing w, w + 4..
 // Chunks past K are loaded from the row's last chunk (valid memory) and
@@ -51,14 +64,15 @@ __device__ __forceinline__ void stage_b(uint8_t* lds, int kq, int K, Row row) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
   const int last = K / 8 - 1;  // last 16-byte chunk of a row
+  const uint32_t l0 = uint32_t(reinterpret_cast<uintptr_t>((lvoid*)lds));
   for (int n = wave; n < kStageBytes / 1024; n += 4) {
     const int chunk = n * 64 + lane;
     const int j = chunk / kChunks, q = chunk % kChunks;
     const int col_chunk = q < 16 ? min(kq * 16 + q, last) : kq * 16;
 #pragma unroll
     for (int s = 0; s < NB; ++s)
-      __builtin_amdgcn_global_load_lds((gvoid*)(row(s, j) + 8 * min(col_chunk, last)),
-                                       (lvoid*)(lds + s * kStageBytes + n * 1024), 16, 0, 0);
+      load_to_lds16(row(s, j) + 8 * min(col_chunk, last),
+                    __builtin_amdgcn_readfirstlane(l0 + s * kStageBytes + n * 1024));
   }
 }
 
@@ -88,32 +102,24 @@ __device__ __forceinline__ void load_a(ATiles& t, AAddr a, int kq) {
       t.w[s][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a(s, 4 * kq + j)));
 }
 
-template <int NB>
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[kNS][kSub], const ATiles& a,
-                                         const uint8_t* lds) {
-  const int lane = threadIdx.x % kWave;
-  const int g = lane / 16, c = lane % 16;
-#pragma unroll
-  for (int u = 0; u < kSub; ++u) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int s2 = 0; s2 < NB; ++s2) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(lds + s2 * kStageBytes +
-                                                        (16 * u + c) * kRowB + 64 * j + 16 * g);
-#pragma unroll
-        for (int s = 0; s < kNS; ++s) acc[s][u] = mma(a.w[s][j], b, acc[s][u]);
-      }
-    }
-  }
-}
+// s_waitcnt vmcnt(16) with expcnt and lgkmcnt left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kVmcnt16 = (1 << 14) | (7 << 4) | (15 << 8);
 
 // acc[s][u] = sum over the K columns of A stream s x (sum over the NB token
 // sources) for token columns 16 u .. 16 u + 15.  lds: NB x 2 stage buffers.
+// B (tokens) is double-buffered in LDS; A (weights) is single-buffered in
+// registers and reloaded k-tile by k-tile: k-tile j of step kq + 1 is
+// requested as soon as the products of k-tile j of step kq have read it, so
+// each weight load has a whole step to arrive.  The staging loads of step
+// kq + 1 precede the step's 16 weight loads, and vector loads complete in
+// order, so one counted wait (at most 16 outstanding) per step covers them.
 // All threads of the workgroup must call it.
 template <int NB, typename AAddr, typename Row>
 __device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], AAddr a, int K, uint8_t* lds,
                                           Row row) {
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
 #pragma unroll
   for (int s = 0; s < kNS; ++s)
 #pragma unroll
@@ -121,39 +127,57 @@ __device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], AAddr a, int 
   const int nkq = (K + kStepK - 1) / kStepK;
   constexpr int kBuf = NB * kStageBytes;
   const bool tail = K % kStepK != 0;  // the last step has columns past K
-  ATiles ta, tb;
+  ATiles at;
   stage_b<NB>(lds, 0, K, row);
-  load_a(ta, a, 0);
+  load_a(at, a, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tail && nkq == 1) {
     zero_tail<NB>(lds, 0, K);
     __syncthreads();
   }
-  auto step = [&](ATiles& cur, ATiles& nxt, int kq) {
-    uint8_t* cur_l = lds + (kq & 1) * kBuf;
-    uint8_t* nxt_l = lds + ((kq + 1) & 1) * kBuf;
-    stage_b<NB>(nxt_l, kq + 1, K, row);
-    load_a(nxt, a, kq + 1);
-    mma_step<NB>(acc, cur, cur_l);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tail && kq + 2 == nkq) {
-      zero_tail<NB>(nxt_l, kq + 1, K);
-      __syncthreads();
+  // the last step has nothing to reload; a runtime condition around the
+  // loads would make the compiler wait for all of them at the next step
+  auto step = [&](int kq, auto reload) {
+    constexpr bool kReload = decltype(reload)::value;
+    const uint8_t* cur = lds + (kq & 1) * kBuf;
+    uint8_t* nxt = lds + ((kq + 1) & 1) * kBuf;
+    if constexpr (kReload) stage_b<NB>(nxt, kq + 1, K, row);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+#pragma unroll
+        for (int s2 = 0; s2 < NB; ++s2) {
+          const u32x4 b = *reinterpret_cast<const u32x4*>(cur + s2 * kStageBytes +
+                                                          (16 * u + c) * kRowB + 64 * j + 16 * g);
+#pragma unroll
+          for (int s = 0; s < kNS; ++s) acc[s][u] = mma(at.w[s][j], b, acc[s][u]);
+        }
+      }
+      if constexpr (kReload) {
+#pragma unroll
+        for (int s = 0; s < kNS; ++s)
+          at.w[s][j] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(a(s, 4 * (kq + 1) + j)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kReload) {
+      // a fenced barrier would wait for every load (the memory model orders
+      // the staging's LDS writes with vmcnt(0))
+      __builtin_amdgcn_s_waitcnt(kVmcnt16);
+      asm volatile("s_barrier" ::: "memory");
+      if (tail && kq + 2 == nkq) {
+        zero_tail<NB>(nxt, kq + 1, K);
+        __syncthreads();
+      }
     }
   };
   int kq = 0;
-  for (; kq + 2 < nkq; kq += 2) {
-    step(ta, tb, kq);
-    step(tb, ta, kq + 1);
-  }
-  if (kq + 1 < nkq) {
-    step(ta, tb, kq);
-    mma_step<NB>(acc, tb, lds + ((kq + 1) & 1) * kBuf);
-  } else {
-    mma_step<NB>(acc, ta, lds + (kq & 1) * kBuf);
-  }
+  for (; kq + 1 < nkq; ++kq) step(kq, std::true_type{});
+  step(kq, std::false_type{});
 }
 
 }  // namespace bf
