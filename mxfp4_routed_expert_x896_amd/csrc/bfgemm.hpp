@@ -105,6 +105,7 @@ __device__ __forceinline__ void load_a(ATiles& t, AAddr a, int kq) {
 // s_waitcnt vmcnt(16) with expcnt and lgkmcnt left alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kVmcnt16 = (1 << 14) | (7 << 4) | (15 << 8);
+static_assert(kNS * 4 >= 16, "a step issues at least 16 ordinary loads after its staging");
 
 // acc[s][u] = sum over the K columns of A stream s x (sum over the NB token
 // sources) for token columns 16 u .. 16 u + 15.  lds: NB x 2 stage buffers.

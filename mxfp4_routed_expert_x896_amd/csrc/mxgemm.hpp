@@ -46,6 +46,7 @@ typedef __attribute__((address_space(3))) void lvoid;
 // s_waitcnt vmcnt(16) with expcnt and lgkmcnt left alone (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kVmcnt16 = (1 << 14) | (7 << 4) | (15 << 8);
+static_assert(kNS * 4 >= 16, "a step issues at least 16 ordinary loads after its staging");
 
 // Position of the scale byte of block b (along the contraction) in the
 // MFMA-ordered scale row (see the header comment).
