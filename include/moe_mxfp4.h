@@ -210,9 +210,12 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
  * + combine -- for up to 4 tokens: router logits + shared gate/up + top-k
- * (and plan), shared down + routed gate/up, routed down + combine.  The caller creates and owns the hipEvent_t handles; pass NULL / 0
- * to stop.  Timing
- * records only add event markers; no kernel is skipped or changed.
+ * (and plan), shared down + routed gate/up, routed down + combine;
+ * moe_layer (MFMA path): x to MXFP8 + router logits, top-k + plan, routed +
+ * shared gate/up, routed + shared down, combine; moe_forward (MFMA path):
+ * plan + x to MXFP8, then the same last three.  The caller creates and owns the hipEvent_t
+ * handles; pass NULL / 0 to stop.  Timing records only add event markers;
+ * no kernel is skipped or changed.
  */
 int moe_profile_events(hipEvent_t* events, int32_t n_events);
 int moe_profile_count(void);

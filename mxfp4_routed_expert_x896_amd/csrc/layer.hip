@@ -706,13 +706,13 @@ __device__ void combine_tile(const GemvLayer& L, int tile) {
 // the role segments present in it (Stage counts, 0 = absent).
 
 enum : unsigned {
-  kRoleLogits = 1u,       // router logits, 4 experts per workgroup
+  kRoleLogits = 1u,       // router logits, 4 experts per workgroup (split: 16 x a quarter)
   kRoleSelect = 2u,       // top-k, 4 tokens per workgroup (+ plan by the last)
   kRolePlan = 4u,         // plan from a given routing (one workgroup)
-  kRoleSharedGU = 8u,     // shared gate/up, (expert, 32 rows) per workgroup
+  kRoleSharedGU = 8u,     // shared gate/up, (expert, 16 rows) per workgroup
   kRoleSharedDown = 16u,  // shared down, (expert, 64 rows) per workgroup
   kRoleRoutedGU = 32u,    // routed gate/up, (active slot, 32 rows)
-  kRoleRoutedDown = 64u,  // routed down, (active slot, 256 rows) + combine
+  kRoleRoutedDown = 64u,  // routed down, (active slot, kRowsD rows) + combine
   kRoleQuantX = 128u,     // prefill: x -> MXFP8 (256 blocks per workgroup)
   kRoleMxGateUp = 256u,   // prefill: routed gate/up, (token tile, 128 rows)
   kRoleMxDown = 512u,     // prefill: routed down, (token tile, 256 rows)
