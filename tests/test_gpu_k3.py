@@ -92,6 +92,31 @@ def test_k3_eight_tokens_with_residual(b, k3):
     assert rel_l2_per_token(y[sample], ref).max() <= REL_TOL
 
 
+@pytest.mark.parametrize("top_k,T", [(8, 1), (8, 8), (4, 64)])
+def test_k3_reduced_top_k(b, k3, top_k, T):
+    """The pages' experimental switch that lowers the number of routed experts
+    per token (K3_MOE_TOP_K): the same K3 weights with top-8 and top-4, on the
+    launch paths of 1, 8 and 64 tokens."""
+    lay = b.Layer(7168, 1536, 896, top_k, k3.lib.router_w, k3.lib.experts, k3.lib.shared_gate,
+                  k3.lib.shared_up, k3.lib.shared_down)
+    orc = M.Layer(7168, 1536, 896, top_k, k3.oracle.router_w, k3.oracle.expert_record,
+                  shared=k3.oracle.shared)
+    xh, xd = SD.upload_tokens(5000 + T, T, 7168)
+    ids = torch.empty((T, top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, 7168), dtype=torch.int16, device="cuda")
+    b.moe_layer(lay, xd, y, ids, w, lay.workspace(T), path=b.PATH_GEMV)
+    torch.cuda.synchronize()
+    ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
+    _, _, s = M.route(xh, orc)
+    check_routing(ids, w, s, top_k)
+    sample = sorted({0, T // 2, T - 1})
+    ref = M.moe_forward(xh, orc, ids, oracle_weights(s, ids), tokens=sample)
+    err = rel_l2_per_token(y[sample], ref)
+    print(f"K3 top-{top_k} T={T}: rel L2 {err.max():.3e}")
+    assert err.max() <= REL_TOL
+
+
 def test_k3_prefill_4096_with_bias(b, k3):
     """K3 prefill (4096 tokens, per-expert logit bias N(0, 0.5)) on the MFMA
     path: routing for every token, output on sampled tokens against the
