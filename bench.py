@@ -1,6 +1,7 @@
 """Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b1|b8|b64|stack12]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--config b1|b8|b64|stack12|prefill|prefill128|b1_stream]
 
 A step is one full pass of the layer (router GEMV + top-k, token->expert
 plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
@@ -10,6 +11,11 @@ experts streamed change from step to step.  For batch 1 the layer is held in
 several replicas at different addresses, used round-robin, so that no step
 finds the previous step's weights in the 256 MB Infinity Cache (in a model
 the other layers run in between).
+
+b1_stream is the decode step with the experts NOT resident: their records sit
+in pinned host memory and an HBM pool of 256 slots is filled on demand
+(moe_pool_fetch) between the router and the expert kernels, so each step
+includes the host-to-device copies of the experts it misses.
 
 Printed: one JSON line with tokens/s (value), ms per step, the expert-weight
 HBM rate, the dominant kernel's roofline (HIP events around each kernel of
@@ -41,6 +47,7 @@ KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+PCIE_PEAK_GBS = 64.0            # PCIe 5.0 x16, one direction
 
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
@@ -55,6 +62,9 @@ CONFIGS = {
                        steps=20, warmup=3,
                        desc="compute-bound diagnostic of the prefill kernels: 4096 tokens routed to "
                             "128 experts (512 tokens each) by +20 on their logit bias"),
+    "b1_stream": dict(tokens=1, layers=1, replicas=1, pool_slots=256, steps=100, warmup=10,
+                      desc="K3 MoE layer decode, batch 1, experts streamed from pinned host memory "
+                           "into a 256-slot HBM pool (least recently used eviction)"),
     "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
                     desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
                          "MXFP8 activations on block-scaled MFMA"),
@@ -235,12 +245,26 @@ def main():
     y = torch.empty((n_layers + 1, T, H), dtype=torch.int16, device=dev)
     normed = torch.empty((T, H), dtype=torch.int16, device=dev)
     ws = layers[0].workspace(T)
+    pool = pooled = None
+    if cfgd.get("pool_slots"):
+        L0 = layers[0]
+        host = torch.empty(L0.experts.shape, dtype=torch.uint8, pin_memory=True)
+        host.copy_(L0.experts)
+        pool = b.ExpertPool(host, cfgd["pool_slots"], device=dev)
+        pooled = b.Layer(H, I, E, k, L0.router_w, pool.slots, L0.shared_gate, L0.shared_up,
+                         L0.shared_down, L0.router_bias, pool=pool)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.time() - t_setup:.0f} s; {len(layers)} resident layer copies",
           file=sys.stderr, flush=True)
 
     def step(i):
-        if n_layers == 1:
+        if pooled is not None:
+            # the router picks the experts, the pool makes them resident
+            # (a host round trip for the ids), then the expert kernels run
+            b.route(pooled, xs[i], ids[i, 0], wts[i, 0], ws)
+            pool.fetch(ids[i, 0].cpu().numpy())
+            b.forward(pooled, xs[i], ids[i, 0], wts[i, 0], y[0], ws, path=path)
+        elif n_layers == 1:
             L = layers[i % len(layers)]
             b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=path)
         else:
@@ -254,6 +278,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    pool_before = pool.stats() if pool is not None else None
     t0 = time.perf_counter()
     for i in range(args.warmup, n_steps):
         step(i)
@@ -373,6 +398,18 @@ def main():
     }
     if mfma_info is not None:
         out["mfma"] = mfma_info
+    if pool is not None:
+        copied, resident = (a - c for a, c in zip(pool.stats(), pool_before))
+        h2d = copied * REC_BYTES / args.steps
+        out["stream"] = {
+            "pool_slots": cfgd["pool_slots"],
+            "records_copied_per_step": round(copied / args.steps, 2),
+            "hit_rate": round(resident / max(copied + resident, 1), 4),
+            "h2d_bytes_per_step": round(h2d),
+            "h2d_gbs": round(h2d / (ms_per_step * 1e-3) / 1e9, 2),
+            "pcie_peak_gbs": PCIE_PEAK_GBS,
+            "note": "value includes the host-to-device copies; kernel_us and roofline are the "
+                    "same kernels timed on the resident layer"}
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_tokens)

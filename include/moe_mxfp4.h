@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION ((1u << 16) | 0u)
+#define MOE_ABI_VERSION ((2u << 16) | 0u)
 
 /* status codes */
 #define MOE_OK 0
@@ -99,6 +99,13 @@ extern "C" {
  *   shared_gate, shared_up: S packed bf16 [I][H] matrices, back to back;
  *   shared_down: S packed bf16 [H][I] matrices (moe_pack_bf16); NULL when
  *                n_shared == 0
+ *   expert_slot: NULL (expert e's record is record e of `experts`), or an
+ *                expert pool: device int32 [E], expert e's record is record
+ *                expert_slot[e] of `experts`, which then holds n_slots
+ *                records (values outside 0 .. n_slots - 1 are clamped).
+ *                moe_pool_fetch (below) keeps such a pool filled from host
+ *                memory; a call must only route to experts whose records
+ *                are resident.  n_slots is 0 when expert_slot is NULL.
  */
 typedef struct moe_layer_desc {
   int32_t hidden;
@@ -114,6 +121,9 @@ typedef struct moe_layer_desc {
   const uint16_t* shared_gate;
   const uint16_t* shared_up;
   const uint16_t* shared_down;
+  const int32_t* expert_slot;
+  int32_t n_slots;
+  int32_t reserved1; /* must be 0 */
 } moe_layer_desc;
 
 /* major << 16 | minor of the library; bindings refuse a different major. */
@@ -201,6 +211,44 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
                 int32_t hidden, uint16_t* out, hipStream_t stream);
 
 /*
+ * Expert pool: the experts are not all resident in HBM.
+ *
+ * Deltafin README, I/O and streaming, and the Deltafin explainer, section
+ * 6.1: the model does not fit the machine, so each token's selected experts
+ * are read from storage into memory as whole contiguous records (17.5 MB at
+ * the K3 shape), and records the previous tokens used are kept.  Here the
+ * records live in host memory (pinned, so the copies are DMA), and a pool of
+ * n_slots records in HBM holds the resident ones; a layer descriptor with
+ * expert_slot = the pool's slot map and experts = the pool runs on them.
+ *
+ * moe_pool_create: host_records (host, pinned for asynchronous copies): E
+ *   PACKED records, stride bytes apart; slots (device): n_slots records,
+ *   stride bytes apart; slot_map (device int32 [E]): written by the pool,
+ *   every entry 0 until its expert is fetched.  1 <= n_slots <= E; stride a
+ *   multiple of 16.  The caller owns all three buffers and keeps them alive
+ *   until moe_pool_destroy; the pool holds host-side bookkeeping only.
+ *   Enqueues the slot map's initialisation on stream.
+ * moe_pool_fetch: makes the n_ids experts in ids (host int32, repeats
+ *   allowed, each in 0 .. E-1) resident: a record not in the pool is copied
+ *   host -> device on stream into a free slot, else into the slot used
+ *   longest ago by an expert not in ids, and the slot map is updated on
+ *   stream.  More distinct experts than n_slots: MOE_ESHAPE, nothing done.
+ *   *copied (may be NULL) receives the number of records copied.  Work is
+ *   ordered on stream, so kernels enqueued before it that read the pool
+ *   finish before a slot is overwritten, and layer calls enqueued after it
+ *   see the records.  Calls on one pool must not run concurrently.
+ * moe_pool_stats: records fetched so far (copied) and found resident.
+ */
+typedef struct moe_expert_pool moe_expert_pool;
+int moe_pool_create(const uint8_t* host_records, uint64_t stride, int32_t n_experts,
+                    uint8_t* slots, int32_t n_slots, int32_t* slot_map, hipStream_t stream,
+                    moe_expert_pool** out_pool);
+int moe_pool_fetch(moe_expert_pool* pool, const int32_t* ids, int64_t n_ids, hipStream_t stream,
+                   int32_t* copied);
+int moe_pool_stats(const moe_expert_pool* pool, int64_t* copied, int64_t* resident);
+int moe_pool_destroy(moe_expert_pool* pool);
+
+/*
  * Optional per-kernel timing for benchmarks.  While an event array is set
  * (per host thread), every call that launches kernels records events[0] on
  * its stream before its first kernel and events[i] right after its i-th
@@ -223,8 +271,9 @@ int moe_profile_count(void);
 /*
  * Test export: the fp32 weights of one matrix of one (packed) expert,
  * decoded by the same device conversion the expert kernels use and written
- * in canonical order.  matrix: 0 gate [I][H], 1 up [I][H], 2 down [H][I];
- * out: fp32 of that shape.
+ * in canonical order.  expert: the record's index in layer->experts (for
+ * a pool, its slot: 0 .. n_slots-1).  matrix: 0 gate [I][H], 1 up [I][H],
+ * 2 down [H][I]; out: fp32 of that shape.
  */
 int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matrix, float* out,
                        hipStream_t stream);

@@ -15,7 +15,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library links against)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 
-ABI_MAJOR = 1
+ABI_MAJOR = 2
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE",
@@ -51,6 +51,9 @@ class LayerDesc(ctypes.Structure):
         ("shared_gate", ctypes.c_void_p),
         ("shared_up", ctypes.c_void_p),
         ("shared_down", ctypes.c_void_p),
+        ("expert_slot", ctypes.c_void_p),
+        ("n_slots", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -80,6 +83,10 @@ _SIGNATURES = {
     "moe_pack_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
     "moe_profile_events": (ctypes.c_int, [_P, _I32]),
     "moe_profile_count": (ctypes.c_int, []),
+    "moe_pool_create": (ctypes.c_int, [_P, _U64, _I32, _P, _I32, _P, _P, ctypes.POINTER(_P)]),
+    "moe_pool_fetch": (ctypes.c_int, [_P, _P, _I64, _P, ctypes.POINTER(_I32)]),
+    "moe_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "moe_pool_destroy": (ctypes.c_int, [_P]),
 }
 
 
@@ -168,7 +175,7 @@ class Layer:
 
     def __init__(self, hidden, inter, n_experts, top_k, router_w, experts,
                  shared_gate=None, shared_up=None, shared_down=None, router_bias=None,
-                 expert_stride=None):
+                 expert_stride=None, pool=None):
         self.hidden, self.inter = int(hidden), int(inter)
         self.n_experts, self.top_k = int(n_experts), int(top_k)
         self.router_w = router_w
@@ -185,7 +192,10 @@ class Layer:
             experts.data_ptr(), self.expert_stride,
             None if shared_gate is None else shared_gate.data_ptr(),
             None if shared_up is None else shared_up.data_ptr(),
-            None if shared_down is None else shared_down.data_ptr())
+            None if shared_down is None else shared_down.data_ptr(),
+            None if pool is None else pool.slot_map.data_ptr(),
+            0 if pool is None else pool.n_slots, 0)
+        self.pool = pool
 
     @property
     def desc(self):
@@ -210,6 +220,48 @@ class Layer:
     def workspace(self, n_tokens, device=None):
         dev = device if device is not None else self.router_w.device
         return torch.empty(self.workspace_bytes(n_tokens), dtype=torch.uint8, device=dev)
+
+
+class ExpertPool:
+    """HBM slots for n_slots of the E packed records, filled on demand from
+    host memory (moe_pool_*).  host_records: packed uint8 [E, stride] in
+    host memory (pinned for asynchronous copies); the slots and the slot map
+    are allocated here on `device`.  Layer(..., experts=pool.slots,
+    pool=pool) runs on the resident records."""
+
+    def __init__(self, host_records, n_slots, device="cuda", stream=None):
+        self.host = host_records
+        self.n_experts, self.stride = int(host_records.shape[0]), int(host_records.shape[1])
+        self.n_slots = int(n_slots)
+        self.slots = torch.empty((self.n_slots, self.stride), dtype=torch.uint8, device=device)
+        self.slot_map = torch.empty(self.n_experts, dtype=torch.int32, device=device)
+        h = _P()
+        _check(_lib().moe_pool_create(host_records.data_ptr(), self.stride, self.n_experts,
+                                      self.slots.data_ptr(), self.n_slots,
+                                      self.slot_map.data_ptr(), _stream(stream), ctypes.byref(h)),
+               "moe_pool_create")
+        self._h = h
+
+    def fetch(self, ids, stream=None):
+        """Makes the experts in ids (host int32 array-like) resident; returns
+        how many records were copied."""
+        import numpy as np
+        a = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).ravel())
+        n = _I32()
+        _check(_lib().moe_pool_fetch(self._h, a.ctypes.data, a.size, _stream(stream),
+                                     ctypes.byref(n)), "moe_pool_fetch")
+        return n.value
+
+    def stats(self):
+        c, r = _I64(), _I64()
+        _check(_lib().moe_pool_stats(self._h, ctypes.byref(c), ctypes.byref(r)), "moe_pool_stats")
+        return c.value, r.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _LIB is not None:
+            _LIB.moe_pool_destroy(h)
+            self._h = None
 
 
 def route(layer, x, topk_ids, topk_w, ws, stream=None):

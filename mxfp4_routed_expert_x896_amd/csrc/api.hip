@@ -74,7 +74,9 @@ int check_layer(const moe_layer_desc* L) {
   if (L == nullptr) return MOE_EINVAL;
   if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0 || L->n_shared < 0)
     return MOE_EINVAL;
-  if (L->reserved0 != 0) return MOE_EINVAL;
+  if (L->reserved0 != 0 || L->reserved1 != 0) return MOE_EINVAL;
+  if (L->expert_slot == nullptr ? L->n_slots != 0 : L->n_slots <= 0) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(L->expert_slot) & 3u) return MOE_EALIGN;
   if (L->hidden % 32 || L->inter % 32 || L->hidden > 8192 || L->inter > 8192) return MOE_ESHAPE;
   if (L->n_experts > 1024 || L->top_k > 32 || L->top_k > L->n_experts || L->n_shared > 4)
     return MOE_ESHAPE;
@@ -200,6 +202,8 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.sel_cnt = at<int>(ws, c.sel_cnt);
   G.experts = L->experts;
   G.stride = L->expert_stride;
+  G.eslot = L->expert_slot;
+  G.n_slots = L->n_slots;
   G.sgate = L->shared_gate;
   G.sup = L->shared_up;
   G.sdown = L->shared_down;
@@ -572,7 +576,8 @@ MOE_API int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int3
                                float* out, hipStream_t stream) {
   int st = check_layer(layer);
   if (st) return st;
-  if (out == nullptr || expert < 0 || expert >= layer->n_experts || matrix < 0 || matrix > 2)
+  const int32_t n_rec = layer->expert_slot != nullptr ? layer->n_slots : layer->n_experts;
+  if (out == nullptr || expert < 0 || expert >= n_rec || matrix < 0 || matrix > 2)
     return MOE_EINVAL;
   if (!aligned16(out)) return MOE_EALIGN;
   if ((st = check_device())) return st;

@@ -31,7 +31,9 @@ struct GemvLayer {
   int32_t* ids_out;         // int32 [T][k] routing written by the top-k role
   float* w_out;             // fp32 [T][k] weights written by the top-k role
   int* sel_cnt;             // [1] arrivals of top-k workgroups (zeroed by the logits launch)
-  const uint8_t* experts;   // E packed records (MFMA-tiled, see pack.hip)
+  const uint8_t* experts;   // E packed records (MFMA-tiled, see pack.hip), or a pool
+  const int32_t* eslot;     // pool: expert -> record index (clamped to n_slots), else NULL
+  int n_slots;
   uint64_t stride;          // bytes between records
   const uint16_t* sgate;    // bf16 [S] packed [I][H]
   const uint16_t* sup;      // bf16 [S] packed [I][H]

@@ -337,6 +337,13 @@ __device__ __forceinline__ int pair_at(const GemvLayer& L, int p) {
   return L.direct ? p : L.plan.pairs[p];
 }
 
+// Packed record of expert e: record e, or with an expert pool the record
+// its slot map names (clamped to the pool).
+__device__ __forceinline__ const uint8_t* record_of(const GemvLayer& L, int e) {
+  const int r = L.eslot != nullptr ? min(max(L.eslot[e], 0), L.n_slots - 1) : e;
+  return L.experts + size_t(r) * L.stride;
+}
+
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
   int na, e, p0, p1;
   slot_of(L, a, na, e, p0, p1);
@@ -350,7 +357,7 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
   const int kqh = (nkq + 1) / 2;
   const int kq0 = (wave & 1) * kqh, kq1 = min(kq0 + kqh, nkq);
   const int rg = tile * 2 + wave / 2;
-  const uint8_t* gbase = L.experts + size_t(e) * L.stride;
+  const uint8_t* gbase = record_of(L, e);
   const uint8_t* ubase = gbase + pm.bytes;
   const uint8_t* gcodes = gbase + size_t(rg) * pm.nkb * 1024;
   const uint8_t* ucodes = ubase + size_t(rg) * pm.nkb * 1024;
@@ -554,7 +561,7 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   const int rg0 = tile * (kRowsD / 16) + wave;
   const int nrg = max(0, (tile_rg - wave + kWaves - 1) / kWaves);
   const int nsteps = nrg * nkq;
-  const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
+  const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
   const uint8_t* codes = base + size_t(rg0) * pd.nkb * 1024 + 16 * lane;
   const uint8_t* scl = base + pd.code_bytes + (size_t(rg0) * 64 + lane) * pd.nkb4;
   const int hstride = pad_k(I) + 8;
@@ -952,8 +959,8 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   const PackedMx pm(I, H);
   const int ngroups = I / 16;
   const int rg0 = rt * 8 + 2 * wave;
-  const uint8_t* base[2] = {L.experts + size_t(e) * L.stride,
-                            L.experts + size_t(e) * L.stride + pm.bytes};
+  const uint8_t* rec = record_of(L, e);
+  const uint8_t* base[2] = {rec, rec + pm.bytes};
   mx::AStreams st;
   st.nkb = pm.nkb;
   st.lane_code = 16 * lane;
@@ -1030,7 +1037,7 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   const PackedMx pgu(I, H), pd(H, I);
   const int ngroups = H / 16;
   const int rg0 = rt * 16 + 4 * wave;
-  const uint8_t* base = L.experts + size_t(e) * L.stride + 2 * pgu.bytes;
+  const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
   mx::AStreams st;
   st.nkb = pd.nkb;
   st.lane_code = 16 * lane;

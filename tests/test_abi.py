@@ -100,6 +100,11 @@ def _ws(lib, desc, t):
     (dict(expert_stride=PACKED_TINY + 8), -2),
     (dict(expert_stride=PACKED_TINY - 16), -3),
     (dict(reserved0=1), -1),
+    (dict(reserved1=1), -1),
+    (dict(expert_slot=0x20000, n_slots=3), 0),     # an expert pool of 3 records
+    (dict(expert_slot=0x20000, n_slots=0), -1),
+    (dict(expert_slot=None, n_slots=2), -1),
+    (dict(expert_slot=0x20002, n_slots=3), -2),
 ])
 def test_descriptor_validation(lib, kw, status):
     st, nbytes = _ws(lib, _desc(lib, **kw), 4)
@@ -143,6 +148,27 @@ def test_calls_reject_bad_arguments_before_launch(lib):
     assert L.moe_mxfp8_quantize(x, 2, 48, y, w, None) == -3
     for code in (0, -1, -2, -3, -4, -5, -6, -7, 99):
         assert L.moe_status_string(code)
+
+
+def test_pool_calls_reject_bad_arguments(lib):
+    L = lib.lib()
+    P = ctypes.c_void_p
+    host, slots, smap = P(0x100000), P(0x200000), P(0x300000)
+    out = P()
+    o = ctypes.byref(out)
+    assert L.moe_pool_create(host, PACKED_TINY, 32, slots, 8, smap, None, None) == -1
+    assert L.moe_pool_create(None, PACKED_TINY, 32, slots, 8, smap, None, o) == -1
+    assert L.moe_pool_create(host, PACKED_TINY, 32, None, 8, smap, None, o) == -1
+    assert L.moe_pool_create(host, PACKED_TINY, 32, slots, 0, smap, None, o) == -1
+    assert L.moe_pool_create(host, PACKED_TINY, 32, slots, 33, smap, None, o) == -3
+    assert L.moe_pool_create(host, PACKED_TINY + 8, 32, slots, 8, smap, None, o) == -2
+    assert L.moe_pool_create(host, PACKED_TINY, 32, P(0x200008), 8, smap, None, o) == -2
+    assert L.moe_pool_create(host, PACKED_TINY, 32, slots, 8, P(0x300002), None, o) == -2
+    assert out.value is None
+    ids = (ctypes.c_int32 * 2)(1, 2)
+    assert L.moe_pool_fetch(None, ids, 2, None, None) == -1
+    assert L.moe_pool_stats(None, None, None) == -1
+    assert L.moe_pool_destroy(None) == -1
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU refusal")

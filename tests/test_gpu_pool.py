@@ -1,0 +1,129 @@
+"""GPU tests of the expert pool (experts not resident: records in host memory,
+a few HBM slots filled on demand; Deltafin README, I/O and streaming).
+
+The pooled layer runs the same kernels on the same packed records, only
+found through the slot map, so its output must equal the resident layer's
+bit for bit; the resident layer itself is pinned to the oracle by the other
+GPU tests.  The fetch bookkeeping (copies, hits, least-recently-used
+eviction among the experts a call does not need) is checked by counts.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import synth.device as SD
+from tests._gpu import Built, to_np_u16
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = dict(hidden=288, inter=96, n_experts=40, top_k=5, n_shared=2)
+
+
+@pytest.fixture(scope="module")
+def b():
+    from mxfp4_routed_expert_x896_amd import binding
+    return binding
+
+
+def _pooled(b, built, n_slots, pinned=True):
+    host = built.lib.experts.cpu()
+    if pinned:
+        host = host.pin_memory()
+    pool = b.ExpertPool(host, n_slots)
+    c = built.cfg
+    lay = b.Layer(c["hidden"], c["inter"], c["n_experts"], c["top_k"], built.lib.router_w,
+                  pool.slots, built.lib.shared_gate, built.lib.shared_up, built.lib.shared_down,
+                  built.lib.router_bias, pool=pool)
+    return pool, lay
+
+
+def _route(b, built, xd):
+    T, k = xd.shape[0], built.cfg["top_k"]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    b.route(built.lib, xd, ids, w, built.lib.workspace(T))
+    return ids, w
+
+
+def _forward(b, lay, xd, ids, w, path):
+    y = torch.empty((xd.shape[0], lay.hidden), dtype=torch.int16, device="cuda")
+    b.forward(lay, xd, ids, w, y, lay.workspace(xd.shape[0]), path=path)
+    torch.cuda.synchronize()
+    return to_np_u16(y)
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED], ids=["tiny", "ragged"])
+@pytest.mark.parametrize("T", [1, 3, 6])
+def test_pooled_layer_equals_resident_gemv(b, cfg, T):
+    built = Built(cfg, seed=31)
+    calls = []
+    for call in range(6):  # new tokens each call
+        xh, xd = SD.upload_tokens(3100 + 10 * T + call, T, cfg["hidden"])
+        calls.append((xd, *_route(b, built, xd)))
+    # as many slots as the largest call needs: later calls must evict
+    n_slots = max(np.unique(ids.cpu().numpy()).size for _, ids, _ in calls)
+    pool, lay = _pooled(b, built, n_slots)
+    copied_total = 0
+    for xd, ids, w in calls:
+        copied_total += pool.fetch(ids.cpu().numpy())
+        np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_GEMV),
+                                      _forward(b, built.lib, xd, ids, w, b.PATH_GEMV))
+    assert copied_total > n_slots  # some records were evicted and refilled
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY, RAGGED], ids=["tiny", "ragged"])
+@pytest.mark.parametrize("T", [70, 300])
+def test_pooled_layer_equals_resident_mfma(b, cfg, T):
+    # a batch this large reaches nearly every expert, so the pool holds all
+    # of them, in a shuffled slot order: the slot map is a real permutation
+    built = Built(cfg, seed=35, bias=True)
+    E = cfg["n_experts"]
+    pool, lay = _pooled(b, built, E)
+    order = np.random.default_rng(7).permutation(E)
+    assert pool.fetch(order) == E
+    smap = pool.slot_map.cpu().numpy()
+    np.testing.assert_array_equal(smap[order], np.arange(E))
+    xh, xd = SD.upload_tokens(3300 + T, T, cfg["hidden"])
+    ids, w = _route(b, built, xd)
+    assert pool.fetch(ids.cpu().numpy()) == 0
+    np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_MFMA),
+                                  _forward(b, built.lib, xd, ids, w, b.PATH_MFMA))
+
+
+def test_fetch_counts_and_lru_eviction(b):
+    built = Built(synth.TINY, seed=32)
+    pool, lay = _pooled(b, built, 4)
+    assert pool.fetch([0, 1, 2, 3]) == 4
+    assert pool.fetch([3, 2, 3]) == 0           # repeats and residents copy nothing
+    assert pool.fetch([4, 5]) == 2              # evicts 0 and 1: used longest ago
+    assert pool.fetch([2, 3]) == 0              # 2 and 3 were kept
+    assert pool.fetch([0, 1, 2, 3]) == 2        # 0 and 1 come back in 4's and 5's slots
+    copied, resident = pool.stats()
+    assert copied == 8 and resident == 2 + 2 + 2
+    # the slot map the kernels read names the slot holding each expert
+    smap = pool.slot_map.cpu().numpy()
+    slots = pool.slots.cpu()
+    for e in (0, 1, 2, 3):
+        assert torch.equal(slots[smap[e]], built.lib.experts[e].cpu())
+
+
+def test_more_distinct_experts_than_slots_is_refused(b):
+    built = Built(synth.TINY, seed=33)
+    pool, _ = _pooled(b, built, 3)
+    with pytest.raises(b.MoeError, match="MOE_ESHAPE"):
+        pool.fetch([0, 1, 2, 3])
+    with pytest.raises(b.MoeError, match="MOE_EINVAL"):
+        pool.fetch([0, 32])                     # not an expert of this layer
+    assert pool.stats() == (0, 0)               # nothing was done
+
+
+def test_pageable_host_records(b):
+    built = Built(synth.TINY, seed=34)
+    pool, lay = _pooled(b, built, 8, pinned=False)
+    xh, xd = SD.upload_tokens(3200, 2, 256)
+    ids, w = _route(b, built, xd)
+    pool.fetch(ids.cpu().numpy())
+    np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_GEMV),
+                                  _forward(b, built.lib, xd, ids, w, b.PATH_GEMV))
