@@ -11,6 +11,11 @@ router's formula or the expert's activation; the readings used here:
     to the logits before the sigmoid;
   * the k largest scores are selected, exact ties going to the lower expert
     index; combine weights are the selected scores divided by their sum;
+  * two router variants the pages leave open, as the DeepSeek-V3 report
+    defines its gate (section 2.1.2, auxiliary-loss-free balancing):
+    bias_mode "select" adds the bias to the sigmoid scores for the choice
+    only (key = s + b) and takes the weights from the unbiased s; and a
+    routed scaling factor multiplies the combine weights (1 by default);
   * an expert is a SwiGLU FFN: y = Wd (SiLU(Wg x) * (Wu x));
   * shared experts are bf16 SwiGLU FFNs of the same shape, added with
     weight 1;
@@ -30,13 +35,17 @@ class Layer:
     """Plain description of one MoE layer for the oracle.
 
     router_w:      uint16 bf16 bits [E, H]
-    router_bias:   float32 [E] or None (added to the logits)
+    router_bias:   float32 [E] or None
+    bias_mode:     "logits" (bias added to the logits, for the choice and the
+                   weights) or "select" (added to the scores for the choice)
+    routed_scale:  factor on the combine weights
     expert_record: callable e -> uint8 record bytes of expert e
     shared:        list of (gate [I,H], up [I,H], down [H,I]) bf16 bit arrays
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, router_w,
-                 expert_record, shared=(), router_bias=None):
+                 expert_record, shared=(), router_bias=None, bias_mode="logits",
+                 routed_scale=1.0):
         self.hidden = int(hidden)
         self.inter = int(inter)
         self.n_experts = int(n_experts)
@@ -45,6 +54,10 @@ class Layer:
         self.router_bias = None if router_bias is None else np.asarray(router_bias, dtype=np.float32)
         self.expert_record = expert_record
         self.shared = list(shared)
+        if bias_mode not in ("logits", "select"):
+            raise ValueError("bias_mode is 'logits' or 'select'")
+        self.bias_mode = bias_mode
+        self.routed_scale = float(routed_scale)
         if self.router_w.shape != (self.n_experts, self.hidden):
             raise ValueError("router weight must be [E, H]")
         if not 1 <= self.top_k <= self.n_experts:
@@ -84,14 +97,30 @@ def select_topk(scores, k):
     return order[..., :k]
 
 
+def router_scores(x_bits, layer):
+    """(s, key) [T,E]: s weighs the chosen experts, key chooses them."""
+    if layer.bias_mode == "logits":
+        s = sigmoid(router_logits(x_bits, layer.router_w, layer.router_bias))
+        return s, s
+    s = sigmoid(router_logits(x_bits, layer.router_w))
+    if layer.router_bias is None:
+        return s, s
+    return s, s + np.asarray(layer.router_bias, dtype=np.float32).astype(np.float64)[None, :]
+
+
+def combine_weights(s, ids, routed_scale=1.0):
+    """routed_scale * s[ids] / sum(s[ids]) per token, for any chosen ids."""
+    sel = np.take_along_axis(np.asarray(s, dtype=np.float64), np.asarray(ids, dtype=np.int64),
+                             axis=-1)
+    return routed_scale * sel / np.sum(sel, axis=-1, keepdims=True)
+
+
 def route(x_bits, layer):
-    """Router: (topk ids int64 [T,k], weights float64 [T,k], scores [T,E])."""
-    logits = router_logits(x_bits, layer.router_w, layer.router_bias)
-    s = sigmoid(logits)
-    ids = select_topk(s, layer.top_k)
-    sel = np.take_along_axis(s, ids, axis=-1)
-    w = sel / np.sum(sel, axis=-1, keepdims=True)
-    return ids, w, s
+    """Router: (topk ids int64 [T,k], weights float64 [T,k], selection keys
+    [T,E]; the keys are the scores s unless bias_mode is "select")."""
+    s, key = router_scores(x_bits, layer)
+    ids = select_topk(key, layer.top_k)
+    return ids, combine_weights(s, ids, layer.routed_scale), key
 
 
 def expert_ffn(xv, wg, wu, wd, act_mxfp8=False):

@@ -102,3 +102,100 @@ def test_weights_renormalise_over_selected():
     for t in range(x.shape[0]):
         rest = np.setdiff1d(np.arange(layer.n_experts), ids[t])
         assert s[t, ids[t]].min() >= s[t, rest].max()
+
+
+# ---- router variants: bias on the scores for the choice only, routed scale
+
+def _one_hot(h, bits=0x3F80, hidden=256):
+    x = np.zeros((1, hidden), dtype=np.uint16)
+    x[0, h] = bits
+    return x
+
+
+def _select_layer(bias, k=4, routed_scale=1.0, router=None):
+    c = synth.TINY
+    wr = synth.router_weight(0, 0, c["n_experts"], c["hidden"]) if router is None else router
+    return M.Layer(c["hidden"], c["inter"], c["n_experts"], k, wr,
+                   expert_record=lambda e: synth.expert_record(0, 0, e, c["hidden"], c["inter"]),
+                   router_bias=bias, bias_mode="select", routed_scale=routed_scale)
+
+
+def test_select_mode_choice_is_brute_force_over_biased_scores():
+    """One-hot x = 4 e_h: logits 4 Wr[:, h] in closed form.  The chosen
+    subset maximises sum(s + b); the weights are the UNBIASED s renormalised."""
+    c = synth.TINY
+    for seed in range(4):
+        bias = synth.router_bias(seed, 0, c["n_experts"]).astype(np.float32)
+        layer = _select_layer(bias)
+        h = 11 + 7 * seed
+        ids, w, key = M.route(_one_hot(h, 0x4080), layer)  # bf16 4.0
+        col = F.bf16_decode(layer.router_w[:, h])
+        s = np.array([1.0 / (1.0 + math.exp(-4.0 * v)) for v in col])
+        kk = s + bias.astype(np.float64)
+        np.testing.assert_allclose(key[0], kk, rtol=1e-15, atol=0)
+        best, best_sum = None, -np.inf
+        for sub in itertools.combinations(range(c["n_experts"]), 4):
+            tot = sum(kk[e] for e in sub)
+            if tot > best_sum:
+                best, best_sum = sub, tot
+        assert sorted(ids[0].tolist()) == list(best)
+        assert np.all(np.diff(kk[ids[0]]) <= 0)
+        sel = s[ids[0]]
+        np.testing.assert_allclose(w[0], sel / sel.sum(), rtol=1e-15, atol=0)
+
+
+def test_select_mode_bias_decides_a_choice_the_logits_mode_does_not():
+    """A bias of +1 on the expert with the lowest score: on the scores
+    (each below 1) it must win; on the logits it need not.  Its weight
+    still comes from its own small unbiased score."""
+    c = synth.TINY
+    h = 3
+    x = _one_hot(h, 0x4220)  # bf16 40.0: logits from about -12 to +27
+    col = F.bf16_decode(synth.router_weight(0, 0, c["n_experts"], c["hidden"])[:, h])
+    s = np.array([1.0 / (1.0 + math.exp(-40.0 * v)) for v in col])
+    low = int(np.argmin(s))
+    bias = np.zeros(c["n_experts"], dtype=np.float32)
+    bias[low] = 1.0
+    ids, w, _ = M.route(x, _select_layer(bias))
+    assert ids[0, 0] == low
+    rest = [e for e in np.argsort(-s, kind="stable") if e != low][:3]
+    assert ids[0, 1:].tolist() == rest
+    sel = s[[low] + rest]
+    np.testing.assert_allclose(w[0], sel / sel.sum(), rtol=1e-15, atol=0)
+    assert w[0, 0] < w[0, 1]  # the biased winner carries its small score
+    ids_l, _, _ = M.route(x, _tiny_layer(bias=bias))
+    assert low not in ids_l[0].tolist()  # +1 on a logit of about -12 is not enough
+
+
+def test_select_mode_ignores_a_constant_bias_and_equals_logits_mode_at_zero():
+    c = synth.TINY
+    x = synth.activations(1010, 6, c["hidden"])
+    bias = synth.router_bias(3, 0, c["n_experts"]).astype(np.float32)
+    ids, w, _ = M.route(x, _select_layer(bias))
+    ids2, w2, _ = M.route(x, _select_layer(bias + np.float32(0.25)))
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_array_equal(w, w2)  # weights never see the bias
+    ids0, w0, s0 = M.route(x, _select_layer(np.zeros(c["n_experts"], np.float32)))
+    idsn, wn, sn = M.route(x, _tiny_layer())
+    assert np.array_equal(ids0, idsn)
+    np.testing.assert_array_equal(w0, wn)
+
+
+def test_routed_scale_multiplies_the_routed_part_only():
+    """Weights sum to the scale; y(2) - y(1) equals the routed part y(1) - shared."""
+    c = synth.TINY
+    shared = [synth.shared_expert(0, 0, 0, c["hidden"], c["inter"])]
+    mk = lambda scale: M.Layer(c["hidden"], c["inter"], c["n_experts"], c["top_k"],
+                               synth.router_weight(0, 0, c["n_experts"], c["hidden"]),
+                               expert_record=lambda e: synth.expert_record(0, 0, e, c["hidden"],
+                                                                          c["inter"]),
+                               shared=shared, routed_scale=scale)
+    x = synth.activations(1011, 3, c["hidden"])
+    y1, ids1, w1 = M.moe_layer(x, mk(1.0))
+    y2, ids2, w2 = M.moe_layer(x, mk(2.0))
+    assert np.array_equal(ids1, ids2)
+    np.testing.assert_allclose(w2.sum(axis=1), 2.0, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(w2, 2.0 * w1)
+    sh = M.shared_sum(x, mk(1.0))
+    np.testing.assert_allclose(y2 - y1, y1 - sh, rtol=0, atol=1e-12 * np.abs(y1).max())
+    assert np.abs(y1 - sh).max() > 1e-3  # the routed part is not empty
