@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION ((2u << 16) | 0u)
+#define MOE_ABI_VERSION ((2u << 16) | 1u)
 
 /* status codes */
 #define MOE_OK 0
@@ -83,6 +83,10 @@ extern "C" {
 #define MOE_ELAUNCH -6     /* a kernel launch failed; see moe_last_hip_error() */
 #define MOE_EUNSUPPORTED -7 /* valid request this build does not implement */
 
+/* moe_layer_desc.router_mode */
+#define MOE_ROUTER_BIAS_LOGITS 0
+#define MOE_ROUTER_BIAS_SELECT 1
+
 /* moe_forward path selection */
 #define MOE_PATH_AUTO 0  /* GEMV path for small T, MXFP8 MFMA path for large T */
 #define MOE_PATH_GEMV 1  /* bf16 activations, dequant-fused GEMV (decode) */
@@ -93,7 +97,18 @@ extern "C" {
  *   hidden (H) and inter (I): multiples of 32, H <= 8192, I <= 8192.
  *   n_experts (E) <= 1024; 1 <= top_k <= min(E, 32); 0 <= n_shared <= 4.
  *   router_w:    bf16 [E][H]
- *   router_bias: fp32 [E] added to the logits before the sigmoid, or NULL
+ *   router_bias: fp32 [E], or NULL; where it enters is router_mode's choice
+ *   router_mode: MOE_ROUTER_BIAS_LOGITS: the bias is added to the logits
+ *                before the sigmoid, for the choice and the weights (the
+ *                reading of the pages' per-expert logit bias);
+ *                MOE_ROUTER_BIAS_SELECT: the bias is added to the sigmoid
+ *                scores for the choice only, and the weights come from the
+ *                unbiased scores (the DeepSeek-V3 report's gate, section
+ *                2.1.2); other values: MOE_EINVAL
+ *   routed_scale: factor on the routed combine weights (the weights
+ *                moe_route returns and moe_layer applies); 0 is read as 1,
+ *                so a zeroed descriptor keeps plain weights summing to 1;
+ *                negative, infinite or NaN: MOE_EINVAL
  *   experts:     E PACKED records (moe_pack_experts), expert_stride bytes
  *                apart (stride >= moe_packed_record_bytes, multiple of 16)
  *   shared_gate, shared_up: S packed bf16 [I][H] matrices, back to back;
@@ -113,7 +128,7 @@ typedef struct moe_layer_desc {
   int32_t n_experts;
   int32_t top_k;
   int32_t n_shared;
-  int32_t reserved0; /* must be 0 */
+  int32_t router_mode;
   const uint16_t* router_w;
   const float* router_bias;
   const uint8_t* experts;
@@ -123,7 +138,7 @@ typedef struct moe_layer_desc {
   const uint16_t* shared_down;
   const int32_t* expert_slot;
   int32_t n_slots;
-  int32_t reserved1; /* must be 0 */
+  float routed_scale;
 } moe_layer_desc;
 
 /* major << 16 | minor of the library; bindings refuse a different major. */

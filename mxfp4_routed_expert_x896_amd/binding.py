@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE
                 -7: "MOE_EUNSUPPORTED"}
 
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+ROUTER_BIAS_LOGITS, ROUTER_BIAS_SELECT = 0, 1
 GATE, UP, DOWN = 0, 1, 2
 
 
@@ -43,7 +44,7 @@ class LayerDesc(ctypes.Structure):
         ("n_experts", ctypes.c_int32),
         ("top_k", ctypes.c_int32),
         ("n_shared", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("router_mode", ctypes.c_int32),
         ("router_w", ctypes.c_void_p),
         ("router_bias", ctypes.c_void_p),
         ("experts", ctypes.c_void_p),
@@ -53,7 +54,7 @@ class LayerDesc(ctypes.Structure):
         ("shared_down", ctypes.c_void_p),
         ("expert_slot", ctypes.c_void_p),
         ("n_slots", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("routed_scale", ctypes.c_float),
     ]
 
 
@@ -170,12 +171,14 @@ class Layer:
 
     router_w: bf16/uint16-viewable [E, H]; experts: PACKED uint8 records
     [E, stride] (pack_experts); shared_*: PACKED bf16 [S, I, H] / [S, H, I]
-    (pack_bf16) or None; router_bias: fp32 [E] or None.
+    (pack_bf16) or None; router_bias: fp32 [E] or None; router_mode:
+    ROUTER_BIAS_LOGITS or ROUTER_BIAS_SELECT (where the bias enters);
+    routed_scale: factor on the combine weights.
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, router_w, experts,
                  shared_gate=None, shared_up=None, shared_down=None, router_bias=None,
-                 expert_stride=None, pool=None):
+                 expert_stride=None, pool=None, router_mode=0, routed_scale=1.0):
         self.hidden, self.inter = int(hidden), int(inter)
         self.n_experts, self.top_k = int(n_experts), int(top_k)
         self.router_w = router_w
@@ -186,7 +189,7 @@ class Layer:
         stride = expert_stride if expert_stride is not None else packed_record_bytes(hidden, inter)
         self.expert_stride = int(stride)
         self._desc = LayerDesc(
-            self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, 0,
+            self.hidden, self.inter, self.n_experts, self.top_k, self.n_shared, int(router_mode),
             router_w.data_ptr(),
             None if router_bias is None else router_bias.data_ptr(),
             experts.data_ptr(), self.expert_stride,
@@ -194,7 +197,7 @@ class Layer:
             None if shared_up is None else shared_up.data_ptr(),
             None if shared_down is None else shared_down.data_ptr(),
             None if pool is None else pool.slot_map.data_ptr(),
-            0 if pool is None else pool.n_slots, 0)
+            0 if pool is None else pool.n_slots, float(routed_scale))
         self.pool = pool
 
     @property
@@ -209,13 +212,14 @@ class Layer:
 
     @classmethod
     def from_canonical(cls, hidden, inter, n_experts, top_k, router_w, experts,
-                       shared_gate=None, shared_up=None, shared_down=None, router_bias=None):
+                       shared_gate=None, shared_up=None, shared_down=None, router_bias=None,
+                       **kw):
         """Packs canonical expert records and row-major shared matrices first."""
         packed = pack_experts(experts, n_experts, hidden, inter)
         sg = None if shared_gate is None else pack_bf16(shared_gate)
         su = None if shared_up is None else pack_bf16(shared_up)
         sd = None if shared_down is None else pack_bf16(shared_down)
-        return cls(hidden, inter, n_experts, top_k, router_w, packed, sg, su, sd, router_bias)
+        return cls(hidden, inter, n_experts, top_k, router_w, packed, sg, su, sd, router_bias, **kw)
 
     def workspace(self, n_tokens, device=None):
         dev = device if device is not None else self.router_w.device

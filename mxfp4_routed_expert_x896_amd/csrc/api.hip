@@ -74,7 +74,9 @@ int check_layer(const moe_layer_desc* L) {
   if (L == nullptr) return MOE_EINVAL;
   if (L->hidden <= 0 || L->inter <= 0 || L->n_experts <= 0 || L->top_k <= 0 || L->n_shared < 0)
     return MOE_EINVAL;
-  if (L->reserved0 != 0 || L->reserved1 != 0) return MOE_EINVAL;
+  if (L->router_mode != MOE_ROUTER_BIAS_LOGITS && L->router_mode != MOE_ROUTER_BIAS_SELECT)
+    return MOE_EINVAL;
+  if (!(L->routed_scale >= 0.0f && L->routed_scale <= 3.0e38f)) return MOE_EINVAL;  // NaN, inf
   if (L->expert_slot == nullptr ? L->n_slots != 0 : L->n_slots <= 0) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(L->expert_slot) & 3u) return MOE_EALIGN;
   if (L->hidden % 32 || L->inter % 32 || L->hidden > 8192 || L->inter > 8192) return MOE_ESHAPE;
@@ -194,7 +196,9 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.S = L->n_shared;
   G.x = x;
   G.wr = L->router_w;
-  G.rbias = L->router_bias;
+  G.rbias = L->router_mode == MOE_ROUTER_BIAS_LOGITS ? L->router_bias : nullptr;
+  G.sbias = L->router_mode == MOE_ROUTER_BIAS_SELECT ? L->router_bias : nullptr;
+  G.rscale = L->routed_scale == 0.0f ? 1.0f : L->routed_scale;
   G.logits = at<float>(ws, c.logits);
   G.lflags = at<unsigned long long>(ws, c.lflags);
   G.epoch = next_epoch();

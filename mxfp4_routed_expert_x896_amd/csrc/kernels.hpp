@@ -24,7 +24,9 @@ struct GemvLayer {
   int T, H, I, E, k, S;
   const uint16_t* x;        // bf16 [T][H]
   const uint16_t* wr;       // bf16 [E][H] router weights
-  const float* rbias;       // fp32 [E] router bias or null
+  const float* rbias;       // fp32 [E] bias added to the logits, or null
+  const float* sbias;       // fp32 [E] bias added to the scores for the choice only, or null
+  float rscale;             // factor on the combine weights
   float* logits;            // fp32 [T][E]
   const int32_t* ids_in;    // int32 [T][k] routing given by the caller (plan role), or
                             // written by the top-k role of an earlier launch (direct mode)

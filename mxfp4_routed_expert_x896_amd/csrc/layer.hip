@@ -1160,11 +1160,20 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   if (t < L.T) {
     int id;
     float w;
-    if (L.lsplit == kRouterSplit)
-      select_token<kCoherent, kRouterSplit>(L.logits + size_t(t) * L.E, size_t(L.T) * L.E, L.E,
-                                            L.k, id, w, sc[wave]);
-    else
-      select_token<kCoherent>(L.logits + size_t(t) * L.E, 0, L.E, L.k, id, w, sc[wave]);
+    const float* lrow = L.logits + size_t(t) * L.E;
+    const size_t ps = size_t(L.T) * L.E;
+    if (L.sbias != nullptr) {
+      if (L.lsplit == kRouterSplit)
+        select_token<kCoherent, kRouterSplit, true>(lrow, ps, L.E, L.k, id, w, sc[wave], L.sbias,
+                                                    L.rscale);
+      else
+        select_token<kCoherent, 1, true>(lrow, 0, L.E, L.k, id, w, sc[wave], L.sbias, L.rscale);
+    } else if (L.lsplit == kRouterSplit) {
+      select_token<kCoherent, kRouterSplit>(lrow, ps, L.E, L.k, id, w, sc[wave], nullptr,
+                                            L.rscale);
+    } else {
+      select_token<kCoherent>(lrow, 0, L.E, L.k, id, w, sc[wave], nullptr, L.rscale);
+    }
     if (lane < L.k) {
       if (single) {
         L.ids_out[size_t(t) * L.k + lane] = id;

@@ -150,10 +150,16 @@ __device__ __forceinline__ int wave_prefix_small(int v, int& total) {
 // kCoherent: the logits were written in the same launch (read past L2).
 // kSplit > 1: lrow is the first of kSplit partial rows pstride floats apart,
 // summed in order.
-template <bool kCoherent = false, int kSplit = 1>
+// kSelBias: the bias takes part in the choice only (DeepSeek-V3 report,
+// section 2.1.2): the key is sigmoid(l) + sbias[e] instead of l, and the
+// weights still come from the unbiased sigmoid(l), recomputed for the
+// chosen experts from the same logits.  scale multiplies every weight.
+template <bool kCoherent = false, int kSplit = 1, bool kSelBias = false>
 __device__ __forceinline__ void select_token(const float* __restrict__ lrow, size_t pstride,
                                              int E, int k, int& id, float& w,
-                                             SelectScratch& sc) {
+                                             SelectScratch& sc,
+                                             const float* __restrict__ sbias = nullptr,
+                                             float scale = 1.0f) {
   const int lane = threadIdx.x % kWave;
   uint32_t val[16];
   // unconditional loads (clamped address), so all of them are in flight at
@@ -175,6 +181,13 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, siz
   for (int q = 1; q < kSplit; ++q)
 #pragma unroll
     for (int i = 0; i < 16; ++i) lv[0][i] += lv[q][i];
+  if constexpr (kSelBias) {
+    float bv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bv[i] = sbias[min(lane + kWave * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lv[0][i] = 1.0f / (1.0f + expf(-lv[0][i])) + bv[i];
+  }
 #pragma unroll
   for (int i = 0; i < 16; ++i) val[i] = lane + kWave * i < E ? ord_f32(lv[0][i]) : 0u;
   uint32_t mx = 0u;
@@ -259,10 +272,20 @@ __device__ __forceinline__ void select_token(const float* __restrict__ lrow, siz
       }
     }
   }
-  const float s = lane < k ? 1.0f / (1.0f + expf(-unord_f32(my_val))) : 0.0f;
+  float l = unord_f32(my_val);
+  if constexpr (kSelBias) {
+    // the chosen expert's logit, summed in the same order as above
+    l = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kSplit; ++q) {
+      const float* p = lrow + q * pstride + my_id;
+      l += kCoherent ? load_coherent(p) : *p;
+    }
+  }
+  const float s = lane < k ? 1.0f / (1.0f + expf(-l)) : 0.0f;
   const float tot = wave_sum(s);
   id = my_id;
-  w = s / tot;
+  w = s / tot * scale;
 }
 
 }  // namespace moe

@@ -31,23 +31,27 @@ class Built:
     dev["experts"] or the shared matrices.
     """
 
-    def __init__(self, cfg, seed=0, layer=0, bias=False):
+    def __init__(self, cfg, seed=0, layer=0, bias=False, bias_mode="logits", routed_scale=1.0):
         self.cfg = cfg
         self.seed, self.layer_idx = seed, layer
+        self.bias_mode, self.routed_scale = bias_mode, routed_scale
         d = SD.upload_layer(cfg, seed, layer, bias=bias)
         self.dev = d
         self.repack()
         H, I = cfg["hidden"], cfg["inter"]
         self.oracle = M.Layer(H, I, cfg["n_experts"], cfg["top_k"], d["host_router_w"],
                               expert_record=lambda e: synth.expert_record(seed, layer, e, H, I),
-                              shared=d["host_shared"], router_bias=d["host_bias"])
+                              shared=d["host_shared"], router_bias=d["host_bias"],
+                              bias_mode=bias_mode, routed_scale=routed_scale)
 
     def repack(self):
         from mxfp4_routed_expert_x896_amd import binding
         c, d = self.cfg, self.dev
+        mode = binding.ROUTER_BIAS_SELECT if self.bias_mode == "select" else binding.ROUTER_BIAS_LOGITS
         self.lib = binding.Layer.from_canonical(
             c["hidden"], c["inter"], c["n_experts"], c["top_k"], d["router_w"], d["experts"],
-            d["shared_gate"], d["shared_up"], d["shared_down"], d["router_bias"])
+            d["shared_gate"], d["shared_up"], d["shared_down"], d["router_bias"],
+            router_mode=mode, routed_scale=self.routed_scale)
         torch.cuda.synchronize()
 
 
@@ -89,15 +93,21 @@ def mxfp8_h_flip_allowance(x_bits, layer, ids, w, rel=5e-5, tokens=None):
     float64 oracle because of h quantisation decisions.
 
     The kernel decides each h code (and each block exponent) from its fp32
-    h; the oracle from its fp64 h.  Where the fp64 value lies within `rel`
-    (relative) of an E4M3 rounding midpoint, or a block maximum within `rel`
-    of a power of two, both decisions are correct.  rel = 5e-5 covers fp32
-    accumulation over a long contraction with cancellation (~800 ulp).  For such elements the
-    bound adds the largest change of y_t that taking the other decision can
-    make: w_j * ||Wd[:, i]||_2 * |step| per element (step = the neighbouring
-    code's distance), and for an ambiguous block exponent the whole block's
-    quantised contribution.  Elements far from any boundary add nothing, so
-    for most tokens the allowance is 0.
+    h; the oracle from its fp64 h.  Where the fp64 value lies within the
+    fp32 result's error of an E4M3 rounding midpoint, or a block maximum
+    within it of a power of two, both decisions are correct.  That error is
+    taken per element as max(rel, 4 sqrt(K) 2^-24 (c_g kappa_g + kappa_u)):
+    kappa = sum|x_k w_k| / |sum x_k w_k| is the condition number of the gate
+    or up contraction (the fp32 sum's error grows with it, and like sqrt(K)
+    for independent roundings: 4 such standard deviations), c_g =
+    |1 + g (1 - sigmoid(g))| carries the gate's error through SiLU, and
+    rel = 5e-5 (~800 ulp) is the floor for well-conditioned elements; a
+    block exponent takes the window of the block's largest element.  For
+    such elements the bound adds the largest change of y_t that taking the
+    other decision can make: w_j * ||Wd[:, i]||_2 * |step| per element
+    (step = the neighbouring code's distance), and for an ambiguous block
+    exponent the whole block's quantised contribution.  Elements far from
+    any boundary add nothing, so for most tokens the allowance is 0.
     """
     from oracle import formats as F
     from oracle.record import dequant_expert
@@ -115,6 +125,13 @@ def mxfp8_h_flip_allowance(x_bits, layer, ids, w, rel=5e-5, tokens=None):
         g = xin[t_idx] @ wg.T
         u = xin[t_idx] @ wu.T
         h = M.silu(g) * u
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+            kap_g = (np.abs(xin[t_idx]) @ np.abs(wg).T) / np.abs(g)
+            kap_u = (np.abs(xin[t_idx]) @ np.abs(wu).T) / np.abs(u)
+            c_g = np.abs(1.0 + g * (1.0 - M.sigmoid(g)))
+            rel_el = np.maximum(rel, 4.0 * np.sqrt(layer.hidden) * 2.0 ** -24
+                                * (c_g * kap_g + kap_u))
+        rel_el = np.where(np.isfinite(rel_el), rel_el, np.inf)
         codes, scales = F.mxfp8_quantize(h)
         E = scales.astype(np.int64) - 127
         scale = np.repeat(np.ldexp(1.0, E), 32, axis=-1)
@@ -127,14 +144,18 @@ def mxfp8_h_flip_allowance(x_bits, layer, ids, w, rel=5e-5, tokens=None):
         ulp = np.where(mag >= 2.0 ** -6, np.ldexp(1.0, (p - 3).astype(np.int64)), 2.0 ** -9)
         # distance from the nearest midpoint between two codes
         frac = np.abs(v - q) / ulp          # 0 at a code, 0.5 at a midpoint
-        near_mid = (0.5 - frac) * ulp <= rel * mag + 1e-300
+        near_mid = (0.5 - frac) * ulp <= rel_el * mag + 1e-300
         amb = near_mid & (mag > 0) & (mag <= 448.0)  # above 448 every value saturates to 448
         contrib = np.where(amb, col_norm[None, :] * ulp * scale, 0.0).sum(axis=1)
         # ambiguous block exponent: the block's whole quantised contribution
         blocks = np.abs(h).reshape(h.shape[0], -1, 32).max(axis=-1)
         with np.errstate(divide="ignore"):
             lg = np.log2(np.maximum(blocks, 1e-300))
-        amb_blk = (np.abs(lg - np.round(lg)) <= rel) & (blocks > 0)
+        # the exponent follows the block's largest element: its error decides
+        hb = np.abs(h).reshape(h.shape[0], -1, 32)
+        rel_blk = np.take_along_axis(rel_el.reshape(hb.shape), hb.argmax(axis=-1)[..., None],
+                                     axis=-1)[..., 0]
+        amb_blk = (np.abs(lg - np.round(lg)) <= rel_blk) & (blocks > 0)
         if amb_blk.any():
             hq = q * scale
             per_blk = np.linalg.norm(hq.reshape(h.shape[0], -1, 32), axis=-1)

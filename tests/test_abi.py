@@ -47,7 +47,7 @@ PACKED_TINY = 38_912  # packed record of H=256, I=64 (K=64 padded to 128 columns
 
 
 def _desc(lib, **kw):
-    d = dict(hidden=256, inter=64, n_experts=32, top_k=4, n_shared=1, reserved0=0,
+    d = dict(hidden=256, inter=64, n_experts=32, top_k=4, n_shared=1, router_mode=0,
              router_w=0x10000, router_bias=None, experts=0x20000, expert_stride=PACKED_TINY,
              shared_gate=0x30000, shared_up=0x40000, shared_down=0x50000)
     d.update(kw)
@@ -99,8 +99,13 @@ def _ws(lib, desc, t):
     (dict(router_w=0x10008), -2),
     (dict(expert_stride=PACKED_TINY + 8), -2),
     (dict(expert_stride=PACKED_TINY - 16), -3),
-    (dict(reserved0=1), -1),
-    (dict(reserved1=1), -1),
+    (dict(router_mode=1), 0),
+    (dict(router_mode=2), -1),
+    (dict(router_mode=-1), -1),
+    (dict(routed_scale=2.5), 0),
+    (dict(routed_scale=-1.0), -1),
+    (dict(routed_scale=float("nan")), -1),
+    (dict(routed_scale=float("inf")), -1),
     (dict(expert_slot=0x20000, n_slots=3), 0),     # an expert pool of 3 records
     (dict(expert_slot=0x20000, n_slots=0), -1),
     (dict(expert_slot=None, n_slots=2), -1),

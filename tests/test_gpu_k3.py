@@ -146,3 +146,32 @@ def test_k3_prefill_4096_with_bias(b, k3):
     err = rel_l2_per_token(y[sample], ref)
     print(f"K3 prefill sampled rel L2 {err.max():.3e}")
     assert err.max() <= REL_TOL
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_k3_router_bias_in_choice_only_with_routed_scale(b, k3, T):
+    """K3 decode with the bias in the choice only (key sigmoid(l) + b, b of
+    N(0, 0.025)) and a routed scale of 2.5."""
+    from synth import router_bias
+    bias_h = (router_bias(0, 0, 896) * np.float32(0.05)).astype(np.float32)
+    lay = b.Layer(7168, 1536, 896, 16, k3.lib.router_w, k3.lib.experts, k3.lib.shared_gate,
+                  k3.lib.shared_up, k3.lib.shared_down, router_bias=torch.from_numpy(bias_h).cuda(),
+                  router_mode=b.ROUTER_BIAS_SELECT, routed_scale=2.5)
+    orc = M.Layer(7168, 1536, 896, 16, k3.oracle.router_w, k3.oracle.expert_record,
+                  shared=k3.oracle.shared, router_bias=bias_h, bias_mode="select",
+                  routed_scale=2.5)
+    xh, xd = SD.upload_tokens(5100 + T, T, 7168)
+    ids = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 16), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, 7168), dtype=torch.int16, device="cuda")
+    b.moe_layer(lay, xd, y, ids, w, lay.workspace(T), path=b.PATH_GEMV)
+    torch.cuda.synchronize()
+    ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
+    s, key = M.router_scores(xh, orc)
+    check_routing(ids, w / np.float32(2.5), key, 16)
+    wo = M.combine_weights(s, ids, 2.5)
+    np.testing.assert_allclose(w, wo, rtol=0, atol=5e-6)
+    sample = sorted({0, T - 1})
+    err = rel_l2_per_token(y[sample], M.moe_forward(xh, orc, ids, wo, tokens=sample))
+    print(f"K3 select-mode bias, scale 2.5, T={T}: rel L2 {err.max():.3e}")
+    assert err.max() <= REL_TOL
