@@ -1,7 +1,7 @@
 """Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config b1|b8|b64|stack12|prefill|prefill128|b1_stream]
+                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream]
 
 A step is one full pass of the layer (router GEMV + top-k, token->expert
 plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
@@ -52,6 +52,9 @@ PCIE_PEAK_GBS = 64.0            # PCIe 5.0 x16, one direction
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
                desc="K3 MoE layer decode, batch 1 (H 7168, 896 experts x I 1536 MXFP4, top-16, 2 bf16 shared)"),
+    "b2": dict(tokens=2, layers=1, replicas=8,
+               desc="K3 MoE layer decode, batch 2 (the speculative-verify shape: the current "
+                    "token and one drafted token)"),
     "b8": dict(tokens=8, layers=1, replicas=8,
                desc="K3 MoE layer decode, batch 8"),
     "b64": dict(tokens=64, layers=1, replicas=1,

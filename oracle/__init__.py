@@ -11,7 +11,8 @@ Sources (page title, section):
     one Apple Silicon Mac"), "How it works" and "Techniques / Compute":
     16 of 896 experts are read per MoE layer, and MXFP4 weights are decoded
     inside the product (dequant fused with the GEMV, e8m0 scale applied to
-    the fp32 exponent).
+    the fp32 exponent); the dense weights kept as row-scaled int8 and
+    expanded to fp32 by a fused convert-scale-copy kernel (spine.py).
   * Deltafin explainer (bhfrc.com, "Kimi K3 extreme deployment"), section 2.1:
     hidden 7168, 896 routed experts with 16 selected, 2 shared experts,
     MXFP4 weights with MXFP8 activations; section 5.1: the two shared

@@ -175,3 +175,16 @@ def test_k3_router_bias_in_choice_only_with_routed_scale(b, k3, T):
     err = rel_l2_per_token(y[sample], M.moe_forward(xh, orc, ids, wo, tokens=sample))
     print(f"K3 select-mode bias, scale 2.5, T={T}: rel L2 {err.max():.3e}")
     assert err.max() <= REL_TOL
+
+
+def test_k3_decode_batch2_speculative_verify(b, k3):
+    """T = 2, the shape a speculative step verifies (the current token and
+    one drafted token), in the launch configuration the benchmark times."""
+    xh, xd = SD.upload_tokens(5200, 2, 7168)
+    ids, w, y = _run(b, k3, xd)
+    _, _, s = M.route(xh, k3.oracle)
+    check_routing(ids, w, s, 16)
+    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids))
+    err = rel_l2_per_token(y, ref)
+    print(f"K3 T=2: rel L2 {err}")
+    assert err.max() <= REL_TOL
