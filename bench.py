@@ -1,7 +1,7 @@
 """Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream]
+                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream|int8_dequant]
 
 A step is one full pass of the layer (router GEMV + top-k, token->expert
 plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
@@ -68,6 +68,9 @@ CONFIGS = {
     "b1_stream": dict(tokens=1, layers=1, replicas=1, pool_slots=256, steps=100, warmup=10,
                       desc="K3 MoE layer decode, batch 1, experts streamed from pinned host memory "
                            "into a 256-slot HBM pool (least recently used eviction)"),
+    "int8_dequant": dict(kind="int8_dequant", rows=32768, cols=7168, steps=50, warmup=5,
+                         desc="row-scaled int8 -> fp32 expansion of a dense weight matrix, "
+                              "32768 x 7168 (235 MB int8 -> 940 MB fp32)"),
     "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
                     desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
                          "MXFP8 activations on block-scaled MFMA"),
@@ -189,6 +192,77 @@ def cpu_baseline(cfg_name, n_tokens):
                       f"{dt:.1f} s; BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
 
 
+def int8_dequant_bench(args, cfgd):
+    """One step = one row-scaled int8 -> fp32 expansion of the whole matrix.
+    Bytes per element: 1 read + 4 written (+ 4 per row for the scale)."""
+    import torch
+    from mxfp4_routed_expert_x896_amd import binding as b
+    R, C = cfgd["rows"], cfgd["cols"]
+    steps = args.steps if args.steps is not None else cfgd["steps"]
+    warmup = args.warmup if args.warmup is not None else cfgd["warmup"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    # two input copies used alternately, so a step does not find the previous
+    # step's 235 MB of int8 in the 256 MB Infinity Cache
+    qs = [torch.randint(-128, 128, (R, C), dtype=torch.int8, device=dev, generator=g)
+          for _ in range(2)]
+    ss = [(torch.rand(R, device=dev, generator=g) * 1e-3 + 1e-5).float() for _ in range(2)]
+    out = torch.empty((R, C), dtype=torch.float32, device=dev)
+    nbytes = R * C * (1 + 4) + R * 4
+    for i in range(warmup):
+        b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the launch alone: events on the stream the library launches on (torch's current)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        evs[2 * i].record()
+        b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
+        evs[2 * i + 1].record()
+    torch.cuda.synchronize()
+    k_us = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(steps)]))
+    achieved = nbytes / (k_us * 1e-6) / 1e9
+    res = {
+        "metric": "GB/s, row-scaled int8 -> fp32 expansion (int8 read + fp32 written)",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8*f32->f32",
+        "data": "synthetic (seeded; int8 uniform over -128..127, scales uniform 1e-5..1e-3)",
+        "config": {"workload": cfgd["desc"], "rows": R, "cols": C},
+        "kernel_us": {"int8_row_dequant": round(k_us, 2)},
+        "roofline": {"kernel": "int8_row_dequant", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": nbytes},
+    }
+    del qs, ss, out
+    if not args.no_cpu_baseline:
+        from oracle import spine as S
+        rng = np.random.default_rng(0)
+        rs = 2048
+        q = rng.integers(-128, 128, size=(rs, C), dtype=np.int16).astype(np.int8)
+        sc = (rng.random(rs) * 1e-3 + 1e-5).astype(np.float32)
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < 10.0:
+            S.int8_row_dequant(q, sc)
+            n += 1
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(n * (rs * C * 5 + rs * 4) / dt / 1e9, 3),
+                               "unit": "GB/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} calls of the float64 numpy oracle on {rs} x {C} "
+                                         "(the same bytes per element), about 10 s"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -197,12 +271,16 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    cfgd = CONFIGS[args.config]
+    if cfgd.get("kind") == "int8_dequant":
+        int8_dequant_bench(args, cfgd)
+        return
+
     import torch
     import synth
     import synth.device as SD
     from mxfp4_routed_expert_x896_amd import binding as b
 
-    cfgd = CONFIGS[args.config]
     T, n_layers = cfgd["tokens"], cfgd["layers"]
     if args.steps is None:
         args.steps = cfgd.get("steps", 200)

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION ((2u << 16) | 1u)
+#define MOE_ABI_VERSION ((2u << 16) | 2u)
 
 /* status codes */
 #define MOE_OK 0
@@ -300,6 +300,22 @@ int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int32_t matr
  */
 int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* codes,
                        uint8_t* scales, hipStream_t stream);
+
+/*
+ * Row-scaled int8 -> fp32 expansion of a dense weight matrix (Deltafin
+ * README, Techniques / Compute: the non-expert weights are kept as int8
+ * with one scale per row, and a fused kernel converts, scales and copies
+ * them into the fp32 weights, bit-exact against the unfused path).
+ *   q:     device int8 [rows][cols], row-major, 4-byte aligned
+ *   scale: device fp32 [rows], 4-byte aligned
+ *   out:   device fp32 [rows][cols], 16-byte aligned; must not overlap q
+ *   out[r][c] = (float)q[r][c] * scale[r], one fp32 rounding (IEEE: a zero
+ *   times a negative scale is -0, times inf or NaN is NaN).
+ *   cols a multiple of 4 and rows * cols <= 2^40, else MOE_ESHAPE.  One
+ *   launch on stream; nothing allocated.
+ */
+int moe_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
+                         float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

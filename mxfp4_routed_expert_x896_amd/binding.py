@@ -79,6 +79,7 @@ _SIGNATURES = {
     "moe_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _I64, _I32, _P, _P]),
     "moe_dequant_export": (ctypes.c_int, [_DESC, _I32, _I32, _P, _P]),
     "moe_mxfp8_quantize": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "moe_int8_row_dequant": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P]),
     "moe_packed_record_bytes": (ctypes.c_int, [_I32, _I32, ctypes.POINTER(_U64)]),
     "moe_pack_experts": (ctypes.c_int, [_P, _U64, _P, _U64, _I32, _I32, _I32, _P]),
     "moe_pack_bf16": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
@@ -309,3 +310,9 @@ def profile_count():
 def mxfp8_quantize(x, codes, scales, stream=None):
     _check(_lib().moe_mxfp8_quantize(_ptr(x), x.shape[0], x.shape[1], _ptr(codes),
                                      _ptr(scales), _stream(stream)), "moe_mxfp8_quantize")
+
+
+def int8_row_dequant(q, scale, out, stream=None):
+    """out[r][c] = q[r][c] * scale[r] (int8 [R, C], fp32 [R] -> fp32 [R, C])."""
+    _check(_lib().moe_int8_row_dequant(_ptr(q), _ptr(scale), q.shape[0], q.shape[1], _ptr(out),
+                                       _stream(stream)), "moe_int8_row_dequant")

@@ -591,6 +591,22 @@ MOE_API int moe_dequant_export(const moe_layer_desc* layer, int32_t expert, int3
       moe::launch_dequant_export(rec, layer->hidden, layer->inter, matrix, out, stream), stream);
 }
 
+MOE_API int moe_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
+                                 float* out, hipStream_t stream) {
+  if (q == nullptr || scale == nullptr || out == nullptr || rows <= 0 || cols <= 0)
+    return MOE_EINVAL;
+  if (cols % 4) return MOE_ESHAPE;
+  if ((reinterpret_cast<uintptr_t>(q) & 3u) || (reinterpret_cast<uintptr_t>(scale) & 3u) ||
+      !aligned16(out))
+    return MOE_EALIGN;
+  if (rows > (int64_t(1) << 40) / cols || moe::int8_dequant_blocks(rows, cols) > int64_t(UINT_MAX))
+    return MOE_ESHAPE;
+  int st = check_device();
+  if (st) return st;
+  prof_begin(stream);
+  return launched(moe::launch_int8_row_dequant(q, scale, rows, cols, out, stream), stream);
+}
+
 MOE_API int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* codes,
                                uint8_t* scales, hipStream_t stream) {
   if (x == nullptr || codes == nullptr || scales == nullptr || n_rows <= 0 || k <= 0)

@@ -122,6 +122,10 @@ hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, i
                           uint16_t* out, hipStream_t stream);
 hipError_t launch_dequant_export(const uint8_t* record, int H, int I, int matrix, float* out,
                                  hipStream_t stream);
+// Row-scaled int8 -> fp32 (spine.hip); blocks the launch uses (< 2^32 required).
+int64_t int8_dequant_blocks(int64_t rows, int64_t cols);
+hipError_t launch_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
+                                   float* out, hipStream_t stream);
 hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream);
 

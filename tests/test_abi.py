@@ -155,6 +155,20 @@ def test_calls_reject_bad_arguments_before_launch(lib):
         assert L.moe_status_string(code)
 
 
+def test_int8_dequant_rejects_bad_arguments(lib):
+    L = lib.lib()
+    P = ctypes.c_void_p
+    q, s, o = P(0x100000), P(0x200000), P(0x300000)
+    assert L.moe_int8_row_dequant(None, s, 4, 64, o, None) == -1
+    assert L.moe_int8_row_dequant(q, s, 0, 64, o, None) == -1
+    assert L.moe_int8_row_dequant(q, s, 4, -4, o, None) == -1
+    assert L.moe_int8_row_dequant(q, s, 4, 66, o, None) == -3
+    assert L.moe_int8_row_dequant(P(0x100002), s, 4, 64, o, None) == -2
+    assert L.moe_int8_row_dequant(q, P(0x200002), 4, 64, o, None) == -2
+    assert L.moe_int8_row_dequant(q, s, 4, 64, P(0x300004), None) == -2
+    assert L.moe_int8_row_dequant(q, s, 1 << 30, 1 << 12, o, None) == -3  # 2^42 elements
+
+
 def test_pool_calls_reject_bad_arguments(lib):
     L = lib.lib()
     P = ctypes.c_void_p
