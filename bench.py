@@ -88,7 +88,72 @@ def parse():
     p.add_argument("--cpu-tokens", type=int, default=1)
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/pmc_<kernel>_<config>.json from two rocprofv3 --pmc "
+                        "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     return p.parse_args()
+
+
+# dominant launch per config: (HIP kernel name in traces, name in kernel_us)
+PMC_KERNELS = {"b1": ("moe_routed_gateup", "shared_down_routed_gateup"),
+               "int8_dequant": ("int8_row_dequant_kernel", "int8_row_dequant")}
+
+
+def pmc_summary(args):
+    """HBM bytes per launch of the config's dominant kernel from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads
+    for the largest plain device copy in the same run (1 GiB read and
+    1 GiB written)."""
+    import collections
+    import csv
+    ksub, name = PMC_KERNELS[args.config]
+
+    def per_kernel(path, counter):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return d
+    f = per_kernel(args.pmc_summary[0], "FETCH_SIZE")
+    w = per_kernel(args.pmc_summary[1], "WRITE_SIZE")
+    kf = [k for k in f if ksub in k and "copyBuffer" not in k]
+    assert len(kf) == 1, kf
+    calib_f = max(max(v) for k, v in f.items() if "copyBuffer" in k)
+    calib_w = max(max(v) for k, v in w.items() if "copyBuffer" in k)
+    copy_kib = (1 << 30) / 1024
+    fs, wsc = copy_kib / calib_f, copy_kib / calib_w
+    fetch = float(np.mean(f[kf[0]]))
+    write = float(np.mean(w[kf[0]]))
+    if args.config == "int8_dequant":
+        c = CONFIGS["int8_dequant"]
+        alg = c["rows"] * c["cols"] * 5 + c["rows"] * 4
+    else:
+        alg = kernel_bytes(name, 1, 16, 16, 2)
+    out = {"kernel": ksub, "bench_name": name, "config": args.config,
+           "source_hash": source_hash(), "dispatches": len(f[kf[0]]),
+           "fetch_kib_raw_mean": round(fetch, 1), "write_kib_raw_mean": round(write, 1),
+           "calibration": {"copy_bytes": 1 << 30, "fetch_kib_raw": calib_f, "write_kib_raw": calib_w,
+                           "fetch_scale": round(fs, 3), "write_scale": round(wsc, 3)},
+           "fetch_bytes_per_launch": round(fetch * 1024 * fs),
+           "write_bytes_per_launch": round(write * 1024 * wsc)}
+    out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    out["algorithmic_bytes"] = alg
+    out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
+    path = os.path.join(ROOT, "profiles", f"pmc_{name}_{args.config}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+def pmc_traffic(name, config):
+    """bytes_per_launch of a committed counter summary, or None once the
+    kernel sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{name}_{config}.json")
+    if os.path.exists(path):
+        pmc = json.load(open(path))
+        if pmc.get("source_hash") == source_hash():
+            return pmc.get("bytes_per_launch")
+    return None
 
 
 def source_hash():
@@ -239,9 +304,17 @@ def int8_dequant_bench(args, cfgd):
         "kernel_us": {"int8_row_dequant": round(k_us, 2)},
         "roofline": {"kernel": "int8_row_dequant", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes": nbytes},
+                     "traffic": pmc_traffic("int8_row_dequant", "int8_dequant"),
+                     "algorithmic_bytes": nbytes},
     }
     del qs, ss, out
+    if args.calib_copy:  # a plain 1 GiB device copy for the counter calibration
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         from oracle import spine as S
         rng = np.random.default_rng(0)
@@ -272,6 +345,9 @@ def main():
         sys.exit(2)
 
     cfgd = CONFIGS[args.config]
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if cfgd.get("kind") == "int8_dequant":
         int8_dequant_bench(args, cfgd)
         return
@@ -417,12 +493,7 @@ def main():
                      "frac_of_bounding_roof": round(t_bound / t_dom, 4)}
     achieved = dom_bytes / (kern_us[dom] * 1e-6) / 1e9
 
-    traffic = None
-    pmc_path = os.path.join(ROOT, "profiles", f"pmc_{dom}_{args.config}.json")
-    if os.path.exists(pmc_path):
-        pmc = json.load(open(pmc_path))
-        if pmc.get("source_hash") == source_hash():
-            traffic = pmc.get("bytes_per_launch")
+    traffic = pmc_traffic(dom, args.config)
 
     # the box's practical HBM ceiling: a plain 1 GiB device-to-device copy
     # (read + write bytes over its time), outside the timed region
