@@ -251,7 +251,9 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_t
  *   *copied (may be NULL) receives the number of records copied.  Work is
  *   ordered on stream, so kernels enqueued before it that read the pool
  *   finish before a slot is overwritten, and layer calls enqueued after it
- *   see the records.  Calls on one pool must not run concurrently.
+ *   see the records.  Calls on one pool must not run concurrently.  A
+ *   failed copy or launch returns MOE_ELAUNCH and empties the pool's
+ *   bookkeeping (no record counts as resident until fetched again).
  * moe_pool_stats: records fetched so far (copied) and found resident.
  */
 typedef struct moe_expert_pool moe_expert_pool;

@@ -363,7 +363,7 @@ int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hi
   s3.n_sdmx = S > 0 ? xcd_grid(S * ((L->hidden + 255) / 256), T) : 0;
   if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
   moe::Stage s4;
-  s4.n_comb = int(T);
+  s4.n_comb = int(T) * moe::combine_chunks(L->hidden);
   return stage(moe::StageKind::Combine, G, s4, stream);
 }
 

@@ -16,6 +16,8 @@ static_assert(kDownRows % 16 == 0, "whole row groups");
 // of the contraction, one workgroup per (16 experts, quarter).
 constexpr int kRouterSplit = 4;
 constexpr int kRouterSplitMin = 5;
+// Prefill combine workgroups per token: 1024-column chunks of the output row.
+__host__ __device__ inline int combine_chunks(int H) { return (H + 1023) / 1024; }
 // Consecutive prefill token tiles that one XCD runs side by side.
 constexpr int kMxGroup = 4;
 

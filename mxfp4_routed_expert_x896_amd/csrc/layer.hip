@@ -1073,7 +1073,13 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
 // Prefill combine: y[t] = sum_j w[t][j] part[t k + j] + sum_s ysh[s][t]
 // (+ residual), rounded once to bf16; one token per workgroup, four outputs
 // per thread and step.
-__device__ void combine_role(const GemvLayer& L, int t) {
+static_assert(4 * kThreads == 1024, "combine_chunks counts 1024-column chunks");
+__device__ void combine_role(const GemvLayer& L, int b) {
+  // workgroup = (token, 4 kThreads columns): one short pass per workgroup
+  // streams better than one workgroup looping over a token's row (measured:
+  // 392 -> 368 us at 4096 tokens x 7168)
+  const int nch = combine_chunks(L.H);
+  const int t = b / nch, ch = b - t * nch;
   if (t >= L.T) return;
   const int H = L.H, k = L.k;
   // Every load is unconditional (clamped index, stand-in rows for absent
@@ -1081,7 +1087,8 @@ __device__ void combine_role(const GemvLayer& L, int t) {
   // condition would be waited for on its own, one round trip each.
   const float* ysh = L.S > 0 ? L.ysh : L.part;
   const uint16_t* res = L.residual != nullptr ? L.residual : L.x;
-  for (int n = 4 * threadIdx.x; n < H; n += 4 * kThreads) {
+  for (int n = ch * 4 * kThreads + 4 * threadIdx.x; n < min(H, (ch + 1) * 4 * kThreads);
+       n += 4 * kThreads) {
     mx::f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     mx::f32x4 sv[4];
     u32x2 rv = {0u, 0u};

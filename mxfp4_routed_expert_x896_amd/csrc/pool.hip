@@ -58,6 +58,15 @@ __global__ void pool_map_update(int32_t* map, MapUpdate u) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// After a failed copy or launch the slots' contents are unknown: forget
+// every resident record, so later fetches copy what they need again.
+int pool_failed(moe_expert_pool* p) {
+  p->slot_of.assign(p->n_experts, -1);
+  p->owner.assign(p->n_slots, -1);
+  p->used_at.assign(p->n_slots, 0);
+  return MOE_ELAUNCH;
+}
+
 }  // namespace
 
 MOE_API int moe_pool_create(const uint8_t* host_records, uint64_t stride, int32_t n_experts,
@@ -134,11 +143,11 @@ MOE_API int moe_pool_fetch(moe_expert_pool* p, const int32_t* ids, int64_t n_ids
           victim = s;
         }
     }
-    if (victim < 0) return MOE_ESHAPE;  // unreachable given the size check
+    if (victim < 0) return pool_failed(p);  // unreachable given the size check
     if (p->owner[victim] >= 0) p->slot_of[p->owner[victim]] = -1;
     if (hipMemcpyAsync(p->slots + uint64_t(victim) * p->stride, p->host + uint64_t(e) * p->stride,
                        p->stride, hipMemcpyHostToDevice, stream) != hipSuccess)
-      return MOE_ELAUNCH;
+      return pool_failed(p);
     p->owner[victim] = e;
     p->slot_of[e] = victim;
     p->used_at[victim] = now;
@@ -147,13 +156,13 @@ MOE_API int moe_pool_fetch(moe_expert_pool* p, const int32_t* ids, int64_t n_ids
     u.slot[u.n] = victim;
     if (++u.n == kMapBatch) {
       hipLaunchKernelGGL(pool_map_update, dim3(1), dim3(kMapBatch), 0, stream, p->slot_map, u);
-      if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+      if (hipGetLastError() != hipSuccess) return pool_failed(p);
       u.n = 0;
     }
   }
   if (u.n > 0) {
     hipLaunchKernelGGL(pool_map_update, dim3(1), dim3(kMapBatch), 0, stream, p->slot_map, u);
-    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    if (hipGetLastError() != hipSuccess) return pool_failed(p);
   }
   p->copied += n_copied;
   if (copied != nullptr) *copied = n_copied;
