@@ -121,3 +121,24 @@ def test_routed_scale_two_doubles_output_bitwise(b, path):
     y1f = y1.astype(np.uint32) << 16
     y2f = y2.astype(np.uint32) << 16
     np.testing.assert_array_equal(y2f.view(np.float32), 2.0 * y1f.view(np.float32))
+
+
+def test_select_mode_many_winners_in_one_lane_takes_the_exact_path(b):
+    """Experts 5, 69, 133, ... (e = 5 mod 64) sit in one lane of the top-k
+    wave; +20 on their score-side bias makes all 16 of them winners, more
+    than the lane's candidate list holds, so the selection runs its exact
+    k-round path -- with keys sigmoid(l) + b and weights re-read from the
+    unbiased logits."""
+    built = _built(MANY, 46, 0.05, 1.5)
+    bias = built.oracle.router_bias.copy()
+    bias[5::64] += 20.0
+    built.dev["router_bias"].copy_(torch.from_numpy(bias))
+    built.oracle.router_bias = bias
+    xh, xd = SD.upload_tokens(4600, 5, MANY["hidden"])
+    ids, w, y = _layer(b, built, xd, b.PATH_GEMV)
+    _check_route(built, xh, ids, w)
+    for t in range(5):
+        assert set(range(5, 1024, 64)) <= set(ids[t].tolist())
+        assert np.all(ids[t][:16] % 64 == 5)
+    s, _ = M.router_scores(xh, built.oracle)
+    check_parity(y, M.moe_forward(xh, built.oracle, ids, M.combine_weights(s, ids, 1.5)))
