@@ -283,14 +283,23 @@ def int8_dequant_bench(args, cfgd):
         b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    # the launch alone: events on the stream the library launches on (torch's current)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    for i in range(steps):
-        evs[2 * i].record()
-        b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
-        evs[2 * i + 1].record()
+    # the kernel alone: it stamps a pair of events with its own start and end
+    # (moe_profile_events), on the stream it runs on
+    import ctypes
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in evs:
+        e.record()
     torch.cuda.synchronize()
-    k_us = float(np.mean([evs[2 * i].elapsed_time(evs[2 * i + 1]) * 1e3 for i in range(steps)]))
+    arr = (ctypes.c_void_p * 2)(*[e.cuda_event for e in evs])
+    b.profile_events(arr, 2)
+    k = []
+    for i in range(steps):
+        b.int8_row_dequant(qs[i % 2], ss[i % 2], out)
+        assert b.profile_count() == 2
+        torch.cuda.synchronize()
+        k.append(evs[0].elapsed_time(evs[1]) * 1e3)
+    b.profile_events(None, 0)
+    k_us = float(np.mean(k))
     achieved = nbytes / (k_us * 1e-6) / 1e9
     res = {
         "metric": "GB/s, row-scaled int8 -> fp32 expansion (int8 read + fp32 written)",
@@ -452,8 +461,9 @@ def main():
     exp_bytes = (D * REC_BYTES + S * 3 * SHARED_MAT_BYTES).sum(axis=1).mean()
     exp_gbs = exp_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # ---- per-kernel durations: the library records an event after each kernel
-    n_ev = 8
+    # ---- per-kernel durations: each of the library's kernels stamps a pair of
+    # events with its own start and end (moe_profile_events)
+    n_ev = 16
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in evs:
         e.record()
@@ -469,8 +479,8 @@ def main():
         b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=path)
         cnt = b.profile_count()
         torch.cuda.synchronize()
-        for j, name in enumerate(KERNELS[:cnt - 1]):
-            per_kernel[name].append(evs[j].elapsed_time(evs[j + 1]) * 1e3)
+        for j, name in enumerate(KERNELS[:cnt // 2]):
+            per_kernel[name].append(evs[2 * j].elapsed_time(evs[2 * j + 1]) * 1e3)
         span.append(evs[0].elapsed_time(evs[cnt - 1]) * 1e3)
     b.profile_events(None, 0)
     kern_us = {n: float(np.mean(v)) for n, v in per_kernel.items() if v}

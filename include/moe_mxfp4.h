@@ -267,10 +267,14 @@ int moe_pool_destroy(moe_expert_pool* pool);
 
 /*
  * Optional per-kernel timing for benchmarks.  While an event array is set
- * (per host thread), every call that launches kernels records events[0] on
- * its stream before its first kernel and events[i] right after its i-th
- * kernel (i < n_events); moe_profile_count() returns how many the last such
- * call recorded.  Kernel order: moe_route: router logits, top-k;
+ * (per host thread), every call that launches layer kernels (moe_route,
+ * moe_forward, moe_layer) or the int8 expansion has its i-th kernel stamp
+ * events[2i] with its start and events[2i+1] with its end, while
+ * 2i + 1 < n_events: the dispatch takes the timestamps
+ * (hipExtLaunchKernelGGL), so a pair spans exactly that kernel's execution,
+ * as a kernel trace measures it.  moe_profile_count() returns how many
+ * events the last such call stamped (twice its kernels).  Kernel order:
+ * moe_route: router logits, top-k;
  * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
@@ -279,8 +283,8 @@ int moe_pool_destroy(moe_expert_pool* pool);
  * moe_layer (MFMA path): x to MXFP8 + router logits, top-k + plan, routed +
  * shared gate/up, routed + shared down, combine; moe_forward (MFMA path):
  * plan + x to MXFP8, then the same last three.  The caller creates and owns the hipEvent_t
- * handles; pass NULL / 0 to stop.  Timing records only add event markers;
- * no kernel is skipped or changed.
+ * handles; pass NULL / 0 to stop.  Timing only attaches events to the
+ * launches; no kernel is skipped or changed.
  */
 int moe_profile_events(hipEvent_t* events, int32_t n_events);
 int moe_profile_count(void);

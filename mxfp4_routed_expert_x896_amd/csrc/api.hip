@@ -25,18 +25,22 @@ struct ProfileHook {
 };
 thread_local ProfileHook g_prof;
 
-void prof_begin(hipStream_t stream) {
-  g_prof.used = 0;
-  if (g_prof.events != nullptr && g_prof.n > 0) {
-    (void)hipEventRecord(g_prof.events[0], stream);
-    g_prof.used = 1;
+// Each call that launches timed kernels starts a new sequence of event pairs.
+void prof_begin(hipStream_t) { g_prof.used = 0; }
+
+}  // namespace
+
+moe::LaunchEvents moe::next_launch_events() {
+  LaunchEvents ev;
+  if (g_prof.events != nullptr && g_prof.used + 2 <= g_prof.n) {
+    ev.start = g_prof.events[g_prof.used];
+    ev.stop = g_prof.events[g_prof.used + 1];
+    g_prof.used += 2;
   }
+  return ev;
 }
 
-void prof_mark(hipStream_t stream) {
-  if (g_prof.events != nullptr && g_prof.used > 0 && g_prof.used < g_prof.n)
-    (void)hipEventRecord(g_prof.events[g_prof.used++], stream);
-}
+namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
@@ -57,12 +61,11 @@ int check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int launched(hipError_t e, hipStream_t stream) {
+int launched(hipError_t e, hipStream_t) {
   if (e != hipSuccess) {
     g_last_hip_error = int(e);
     return MOE_ELAUNCH;
   }
-  prof_mark(stream);
   return MOE_OK;
 }
 

@@ -1,12 +1,31 @@
 // Host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.hpp"
 
 namespace moe {
+
+// Timing hook: the pair of events the next kernel launch stamps with its own
+// start and end (both null when the calling thread registered none).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents next_launch_events();  // api.hip
+
+// A launch that stamps ev when the hook is active: the dispatch itself takes
+// the timestamps, so the pair spans exactly the kernel's execution.
+template <typename K, typename... A>
+inline void launch_timed(LaunchEvents ev, K kernel, dim3 grid, dim3 block, uint32_t lds,
+                         hipStream_t stream, A... args) {
+  if (ev.start != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+}
 
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;

@@ -1408,43 +1408,44 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
                   st.n_sdmx + st.n_selw;
   if (wgs <= 0) return hipSuccess;
   const dim3 grid(wgs), block(kThreads);
+  const LaunchEvents ev = next_launch_events();
   switch (kind) {
     case StageKind::RouterSharedGateUp: {
       const int per_lane = (L.H / 8 + kWave - 1) / kWave;
       if (per_lane <= 4)
-        hipLaunchKernelGGL(moe_router_shared_gateup<4>, grid, block, lds, stream, L, st);
+        launch_timed(ev, moe_router_shared_gateup<4>, grid, block, lds, stream, L, st);
       else if (per_lane <= 8)
-        hipLaunchKernelGGL(moe_router_shared_gateup<8>, grid, block, lds, stream, L, st);
+        launch_timed(ev, moe_router_shared_gateup<8>, grid, block, lds, stream, L, st);
       else
-        hipLaunchKernelGGL(moe_router_shared_gateup<16>, grid, block, lds, stream, L, st);
+        launch_timed(ev, moe_router_shared_gateup<16>, grid, block, lds, stream, L, st);
       break;
     }
     case StageKind::SelectSharedDown:
-      hipLaunchKernelGGL(moe_select_shared_down, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_select_shared_down, grid, block, lds, stream, L, st);
       break;
     case StageKind::PlanSharedGateUp:
-      hipLaunchKernelGGL(moe_plan_shared_gateup, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_plan_shared_gateup, grid, block, lds, stream, L, st);
       break;
     case StageKind::RoutedGateUp:
-      hipLaunchKernelGGL(moe_routed_gateup, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_routed_gateup, grid, block, lds, stream, L, st);
       break;
     case StageKind::RoutedDownCombine:
-      hipLaunchKernelGGL(moe_routed_down_combine, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_routed_down_combine, grid, block, lds, stream, L, st);
       break;
     case StageKind::PlanQuantSharedGateUp:
-      hipLaunchKernelGGL(moe_plan_quant_shared_gateup, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_plan_quant_shared_gateup, grid, block, lds, stream, L, st);
       break;
     case StageKind::RouterMxQuant:
-      hipLaunchKernelGGL(moe_router_mx_quant, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_router_mx_quant, grid, block, lds, stream, L, st);
       break;
     case StageKind::MxGateUp:
-      hipLaunchKernelGGL(moe_mx_gateup, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_mx_gateup, grid, block, lds, stream, L, st);
       break;
     case StageKind::MxDown:
-      hipLaunchKernelGGL(moe_mx_down, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_mx_down, grid, block, lds, stream, L, st);
       break;
     case StageKind::Combine:
-      hipLaunchKernelGGL(moe_combine, grid, block, lds, stream, L, st);
+      launch_timed(ev, moe_combine, grid, block, lds, stream, L, st);
       break;
   }
   return hipGetLastError();

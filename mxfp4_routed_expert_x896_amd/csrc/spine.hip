@@ -84,8 +84,8 @@ int64_t int8_dequant_blocks(int64_t rows, int64_t cols) {
 hipError_t launch_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
                                    float* out, hipStream_t stream) {
   const uint32_t cpr = uint32_t((cols + kDqChunk - 1) / kDqChunk);
-  hipLaunchKernelGGL(int8_row_dequant_kernel, dim3(uint32_t(rows * cpr)), dim3(kDqThreads), 0,
-                     stream, q, scale, cols, cpr, out);
+  launch_timed(next_launch_events(), int8_row_dequant_kernel, dim3(uint32_t(rows * cpr)),
+               dim3(kDqThreads), 0u, stream, q, scale, cols, cpr, out);
   return hipGetLastError();
 }
 
