@@ -81,7 +81,7 @@ extern "C" {
 #define MOE_EWORKSPACE -4  /* workspace smaller than moe_workspace_bytes() */
 #define MOE_EDEVICE -5     /* current device is not gfx950 */
 #define MOE_ELAUNCH -6     /* a kernel launch failed; see moe_last_hip_error() */
-#define MOE_EUNSUPPORTED -7 /* valid request this build does not implement */
+#define MOE_EUNSUPPORTED -7 /* valid request the library does not implement */
 
 /* moe_layer_desc.router_mode */
 #define MOE_ROUTER_BIAS_LOGITS 0

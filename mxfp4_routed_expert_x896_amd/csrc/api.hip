@@ -428,7 +428,7 @@ MOE_API const char* moe_status_string(int status) {
     case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_EDEVICE: return "current device is not gfx950";
     case MOE_ELAUNCH: return "kernel launch failed (see moe_last_hip_error)";
-    case MOE_EUNSUPPORTED: return "request not implemented by this build";
+    case MOE_EUNSUPPORTED: return "request not implemented by the library";
     default: return "unknown status";
   }
 }
