@@ -188,3 +188,30 @@ def test_k3_decode_batch2_speculative_verify(b, k3):
     err = rel_l2_per_token(y, ref)
     print(f"K3 T=2: rel L2 {err}")
     assert err.max() <= REL_TOL
+
+
+def test_k3_pooled_experts_equal_resident(b, k3):
+    """The 896 K3 records in pinned host memory, 64 HBM slots filled on
+    demand: consecutive single tokens (new experts each time, some slots
+    evicted) give the resident layer's output bit for bit."""
+    host = torch.empty(k3.lib.experts.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(k3.lib.experts)
+    pool = b.ExpertPool(host, 64)
+    lay = b.Layer(7168, 1536, 896, 16, k3.lib.router_w, pool.slots, k3.lib.shared_gate,
+                  k3.lib.shared_up, k3.lib.shared_down, pool=pool)
+    copied = 0
+    for i in range(6):
+        xh, xd = SD.upload_tokens(5300 + i, 1, 7168)
+        ids = torch.empty((1, 16), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, 16), dtype=torch.float32, device="cuda")
+        b.route(k3.lib, xd, ids, w, k3.lib.workspace(1))
+        copied += pool.fetch(ids.cpu().numpy())
+        ys = []
+        for layer in (lay, k3.lib):
+            y = torch.empty((1, 7168), dtype=torch.int16, device="cuda")
+            b.forward(layer, xd, ids, w, y, layer.workspace(1), path=b.PATH_GEMV)
+            torch.cuda.synchronize()
+            ys.append(to_np_u16(y))
+        np.testing.assert_array_equal(ys[0], ys[1])
+    assert copied > 64  # the pool evicted and refilled
+    del lay, pool, host
