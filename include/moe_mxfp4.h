@@ -273,7 +273,8 @@ int moe_pool_destroy(moe_expert_pool* pool);
  * 2i + 1 < n_events: the dispatch takes the timestamps
  * (hipExtLaunchKernelGGL), so a pair spans exactly that kernel's execution,
  * as a kernel trace measures it.  moe_profile_count() returns how many
- * events the last such call stamped (twice its kernels).  Kernel order:
+ * events the last call into the library stamped (twice its timed kernels;
+ * 0 after calls that launch none of these).  Kernel order:
  * moe_route: router logits, top-k;
  * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
