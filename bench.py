@@ -99,7 +99,7 @@ PMC_KERNELS = {"b1": ("moe_routed_gateup", "shared_down_routed_gateup"),
                "int8_dequant": ("int8_row_dequant_kernel", "int8_row_dequant")}
 
 
-def pmc_summary(args):
+def pmc_summary(args, out_dir=None):
     """HBM bytes per launch of the config's dominant kernel from FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads
     for the largest plain device copy in the same run (1 GiB read and
@@ -139,10 +139,11 @@ def pmc_summary(args):
     out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
     out["algorithmic_bytes"] = alg
     out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
-    path = os.path.join(ROOT, "profiles", f"pmc_{name}_{args.config}.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"pmc_{name}_{args.config}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out), flush=True)
+    return out
 
 
 def pmc_traffic(name, config):
