@@ -10,6 +10,7 @@ import itertools
 import math
 
 import numpy as np
+import pytest
 
 import synth
 from oracle import formats as F
@@ -199,3 +200,57 @@ def test_routed_scale_multiplies_the_routed_part_only():
     sh = M.shared_sum(x, mk(1.0))
     np.testing.assert_allclose(y2 - y1, y1 - sh, rtol=0, atol=1e-12 * np.abs(y1).max())
     assert np.abs(y1 - sh).max() > 1e-3  # the routed part is not empty
+
+
+# ---- the tie rule at the K3 expert count and the largest supported one
+
+def _wide_layer(router, k, bias=None, bias_mode="logits"):
+    E, H = router.shape
+    return M.Layer(H, 64, E, k, router,
+                   expert_record=lambda e: synth.expert_record(0, 0, e, H, 64),
+                   router_bias=bias, bias_mode=bias_mode)
+
+
+@pytest.mark.parametrize("E,k", [(896, 16), (1024, 32)])
+def test_all_tied_rows_pick_the_lowest_indices(E, k):
+    """Every router row equal: all E scores tie exactly, so the choice is
+    experts 0..k-1 in index order and each weight is 1/k.  At these sizes an
+    unstable sort returns the top indices first, so this pins the tie rule
+    where the K3 layer (E = 896) and the largest layer (E = 1024) use it."""
+    H = 256
+    row = synth.router_weight(0, 0, 1, H)
+    layer = _wide_layer(np.repeat(row, E, axis=0), k)
+    x = synth.activations(1020, 3, H)
+    ids, w, s = M.route(x, layer)
+    assert (s == s[:, :1]).all()
+    assert ids.tolist() == [list(range(k))] * 3
+    np.testing.assert_allclose(w, 1.0 / k, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("E,k", [(896, 16), (1024, 32)])
+def test_tied_score_classes_follow_the_lexicographic_order(E, k):
+    """Router rows drawn from 5 distinct rows: the scores take 5 values, each
+    shared by about E/5 experts spread over all indices.  The selection must
+    equal the first k of all experts listed by (score descending, index
+    ascending), written here as a plain sort on that tuple."""
+    H = 256
+    rows = synth.router_weight(7, 0, 5, H)
+    pick = np.random.default_rng([7, E]).integers(0, 5, size=E)
+    layer = _wide_layer(rows[pick], k)
+    x = synth.activations(1021, 4, H)
+    ids, w, s = M.route(x, layer)
+    for t in range(x.shape[0]):
+        want = sorted(range(E), key=lambda e: (-s[t, e], e))[:k]
+        assert ids[t].tolist() == want
+        assert len(set(s[t].tolist())) == 5
+
+
+def test_select_mode_ties_at_k3_size_pick_the_lowest_indices():
+    """The choice on s + b with every row and bias equal: all keys tie."""
+    E, k, H = 896, 16, 256
+    row = synth.router_weight(0, 0, 1, H)
+    layer = _wide_layer(np.repeat(row, E, axis=0), k, bias=np.full(E, 0.125, np.float32),
+                        bias_mode="select")
+    ids, w, key = M.route(synth.activations(1022, 2, H), layer)
+    assert ids.tolist() == [list(range(k))] * 2
+    np.testing.assert_allclose(w, 1.0 / k, rtol=0, atol=1e-15)
