@@ -54,8 +54,10 @@
  *   - pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t
  *     bit patterns; every device pointer must be 16-byte aligned.
  *   - the caller owns every buffer.  The library allocates nothing, keeps no
- *     mutable global state, never synchronises the host, and enqueues all
- *     work on the given stream (NULL = the default stream).
+ *     mutable global state (beyond two per-host-thread settings: the timing
+ *     hook and the wait limit), never synchronises the host (except
+ *     moe_workspace_status, a query), and enqueues all work on the given
+ *     stream (NULL = the default stream).
  *   - arguments are validated on the host before anything is launched; on
  *     error nothing is launched and a negative MOE_E* code is returned.
  *     Device-side faults surface at the caller's next synchronisation.
@@ -71,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION ((2u << 16) | 2u)
+#define MOE_ABI_VERSION ((2u << 16) | 3u)
 
 /* status codes */
 #define MOE_OK 0
@@ -82,6 +84,7 @@ extern "C" {
 #define MOE_EDEVICE -5     /* current device is not gfx950 */
 #define MOE_ELAUNCH -6     /* a kernel launch failed; see moe_last_hip_error() */
 #define MOE_EUNSUPPORTED -7 /* valid request the library does not implement */
+#define MOE_ETIMEOUT -8    /* a top-k wait gave up (moe_workspace_status) */
 
 /* moe_layer_desc.router_mode */
 #define MOE_ROUTER_BIAS_LOGITS 0
@@ -110,7 +113,14 @@ extern "C" {
  *                so a zeroed descriptor keeps plain weights summing to 1;
  *                negative, infinite or NaN: MOE_EINVAL
  *   experts:     E PACKED records (moe_pack_experts), expert_stride bytes
- *                apart (stride >= moe_packed_record_bytes, multiple of 16)
+ *                apart (stride >= moe_packed_record_bytes, multiple of 16).
+ *                Not the canonical record: a caller holding canonical
+ *                records repacks them once with moe_pack_experts (same size
+ *                at K3 shape).  The packed order makes every wave-wide
+ *                16-byte load one contiguous KiB that holds each lane's MFMA
+ *                operand; on canonical rows the 16 lanes of a quarter-wave
+ *                read 16 different rows (64 cache lines per load), which
+ *                doubled the decode gate/up time when measured.
  *   shared_gate, shared_up: S packed bf16 [I][H] matrices, back to back;
  *   shared_down: S packed bf16 [H][I] matrices (moe_pack_bf16); NULL when
  *                n_shared == 0
@@ -177,7 +187,8 @@ int moe_pack_bf16(const uint16_t* src, uint16_t* dst, int32_t count, int32_t row
 /* Workspace needed by moe_route / moe_forward / moe_layer for n_tokens
  * tokens of this layer.  The caller allocates it (any device memory, e.g. a
  * torch uint8 tensor); its contents need no initialisation and are
- * overwritten by every call.  Calls that share a workspace must be ordered
+ * overwritten by every call (except the status marker, see
+ * moe_workspace_status).  Calls that share a workspace must be ordered
  * (same stream). */
 int moe_workspace_bytes(const moe_layer_desc* layer, int64_t n_tokens, uint64_t* out_bytes);
 
@@ -214,6 +225,56 @@ int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens
 int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
               const uint16_t* residual, uint16_t* y, int32_t* topk_ids, float* topk_w,
               int32_t path, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Status of the calls that used a workspace.  For up to 4 tokens on the GEMV
+ * path, moe_layer runs the top-k inside the router launch, in a workgroup
+ * that waits for the other workgroups' logits (a bounded wait: see
+ * moe_set_wait_limit).  If that wait ever gives up, the call's routing (and
+ * output) is wrong, and the first 8 bytes of its workspace are set to a
+ * marker that no call clears.  moe_workspace_status synchronises `stream`
+ * (the stream of those calls), reads the marker and returns MOE_ETIMEOUT if
+ * it is set -- clearing it, so a later query reports only later calls --
+ * else MOE_OK.  A workspace whose first bytes were never written by a call
+ * reads as MOE_OK.  Host-synchronous (unlike every other call).
+ */
+int moe_workspace_status(const void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Polls (~0.3 us each) after which the top-k wait above gives up, for calls
+ * made later from the calling host thread; negative restores the default
+ * (2^20, ~0.3 s).  A diagnostic and test knob: 0 makes every such wait give
+ * up at once, so the failure path can be exercised with every kernel still
+ * exiting normally.
+ */
+int moe_set_wait_limit(int64_t polls);
+
+/*
+ * Test export: where a region of the workspace of a call with n_tokens
+ * tokens lives (*offset bytes from its start, *bytes long), so that tests
+ * can compare the layer's intermediate values with an independent model.
+ * Kq = H and Iq = I rounded up to multiples of 512.  Scale rows are in
+ * "MFMA order": the byte of block b of a row is at position
+ * (b & ~15) | ((b & 3) << 2) | ((b & 15) >> 2).
+ *   MOE_WS_PAIRS:    int32 [T k]: the pair t k + j at each plan position
+ *                    (pairs grouped by expert, experts ascending); written
+ *                    by every call except single-token GEMV calls
+ *   MOE_WS_X_CODES:  uint8 E4M3 [T][Kq] MXFP8 codes of x (MFMA path; zero
+ *                    codes past H)
+ *   MOE_WS_X_SCALES: uint8 E8M0 [T][Kq/32], MFMA order (127 past H)
+ *   MOE_WS_H_CODES:  uint8 E4M3 [T k][Iq]: MXFP8 codes of SiLU(g) u of the
+ *                    pair at each plan position (MFMA path)
+ *   MOE_WS_H_SCALES: uint8 E8M0 [T k][Iq/32], MFMA order
+ * Contents are those of the last call on the workspace once its stream has
+ * reached that point.
+ */
+#define MOE_WS_PAIRS 0
+#define MOE_WS_X_CODES 1
+#define MOE_WS_X_SCALES 2
+#define MOE_WS_H_CODES 3
+#define MOE_WS_H_SCALES 4
+int moe_workspace_region(const moe_layer_desc* layer, int64_t n_tokens, int32_t region,
+                         uint64_t* offset, uint64_t* bytes);
 
 /* Smallest n_tokens for which MOE_PATH_AUTO takes the MFMA path. */
 int64_t moe_mfma_min_tokens(void);

@@ -20,11 +20,13 @@ ABI_MAJOR = 2
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE",
                 -4: "MOE_EWORKSPACE", -5: "MOE_EDEVICE", -6: "MOE_ELAUNCH",
-                -7: "MOE_EUNSUPPORTED"}
+                -7: "MOE_EUNSUPPORTED", -8: "MOE_ETIMEOUT"}
 
 PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
 ROUTER_BIAS_LOGITS, ROUTER_BIAS_SELECT = 0, 1
 GATE, UP, DOWN = 0, 1, 2
+WS_PAIRS, WS_X_CODES, WS_X_SCALES, WS_H_CODES, WS_H_SCALES = range(5)
+MOE_ETIMEOUT = -8
 
 
 class MoeError(RuntimeError):
@@ -89,6 +91,10 @@ _SIGNATURES = {
     "moe_pool_fetch": (ctypes.c_int, [_P, _P, _I64, _P, ctypes.POINTER(_I32)]),
     "moe_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "moe_pool_destroy": (ctypes.c_int, [_P]),
+    "moe_workspace_status": (ctypes.c_int, [_P, _U64, _P]),
+    "moe_set_wait_limit": (ctypes.c_int, [_I64]),
+    "moe_workspace_region": (ctypes.c_int, [_DESC, _I64, _I32, ctypes.POINTER(_U64),
+                                            ctypes.POINTER(_U64)]),
 }
 
 
@@ -316,3 +322,25 @@ def int8_row_dequant(q, scale, out, stream=None):
     """out[r][c] = q[r][c] * scale[r] (int8 [R, C], fp32 [R] -> fp32 [R, C])."""
     _check(_lib().moe_int8_row_dequant(_ptr(q), _ptr(scale), q.shape[0], q.shape[1], _ptr(out),
                                        _stream(stream)), "moe_int8_row_dequant")
+
+
+def workspace_status(ws, stream=None):
+    """MOE_OK, or MOE_ETIMEOUT if a top-k wait of a call on ws gave up since
+    the last query (synchronises the stream; clears the marker)."""
+    st = _lib().moe_workspace_status(_ptr(ws), ws.numel(), _stream(stream))
+    if st not in (MOE_OK, MOE_ETIMEOUT):
+        _check(st, "moe_workspace_status")
+    return st
+
+
+def set_wait_limit(polls):
+    """Polls before a top-k wait gives up (this host thread); -1: default."""
+    _check(_lib().moe_set_wait_limit(int(polls)), "moe_set_wait_limit")
+
+
+def workspace_region(layer, n_tokens, region, ws):
+    """uint8 view of one region of a workspace tensor (test export)."""
+    off, n = _U64(), _U64()
+    _check(_lib().moe_workspace_region(layer.desc, n_tokens, region, ctypes.byref(off),
+                                       ctypes.byref(n)), "moe_workspace_region")
+    return ws[off.value:off.value + n.value]

@@ -25,6 +25,9 @@ struct ProfileHook {
 };
 thread_local ProfileHook g_prof;
 
+// Polls before a top-k wait gives up (moe_set_wait_limit), per host thread.
+thread_local long g_wait_limit = moe::kDefaultSpinLimit;
+
 // Each call that launches timed kernels starts a new sequence of event pairs.
 void prof_begin(hipStream_t) { g_prof.used = 0; }
 
@@ -133,7 +136,7 @@ unsigned long long next_epoch() {
 
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t lflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
+  uint64_t status, lflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
   uint64_t n_mtiles, mtiles, xq, xs, hq, hs8, total;
 };
 
@@ -147,7 +150,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
     off = align256(off + bytes);
     return at;
   };
-  c.lflags = take(uint64_t(n_logit_wgs(L) + 1) * 8);  // first: same place for every T
+  c.status = take(8);  // first: the same place for every layer and T
+  c.lflags = take(uint64_t(n_logit_wgs(L)) * 8);
   c.logits = take(t * E * 4 * (T >= moe::kRouterSplitMin ? moe::kRouterSplit : 1));
   c.n_active = take(4);
   c.active = take(E * 4);
@@ -204,7 +208,9 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.rscale = L->routed_scale == 0.0f ? 1.0f : L->routed_scale;
   G.logits = at<float>(ws, c.logits);
   G.lflags = at<unsigned long long>(ws, c.lflags);
+  G.status = at<unsigned long long>(ws, c.status);
   G.epoch = next_epoch();
+  G.spin_limit = g_wait_limit;
   G.lsplit = 1;
   G.sel_cnt = at<int>(ws, c.sel_cnt);
   G.experts = L->experts;
@@ -429,6 +435,7 @@ MOE_API const char* moe_status_string(int status) {
     case MOE_EDEVICE: return "current device is not gfx950";
     case MOE_ELAUNCH: return "kernel launch failed (see moe_last_hip_error)";
     case MOE_EUNSUPPORTED: return "request not implemented by the library";
+    case MOE_ETIMEOUT: return "a top-k wait gave up: the routing of a call on this workspace is wrong";
     default: return "unknown status";
   }
 }
@@ -621,4 +628,48 @@ MOE_API int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uin
   if (st) return st;
   prof_begin(stream);
   return launched(moe::launch_mxfp8_quantize(x, n_rows, k, codes, scales, stream), stream);
+}
+
+MOE_API int moe_set_wait_limit(int64_t polls) {
+  g_wait_limit = polls < 0 ? moe::kDefaultSpinLimit : long(polls);
+  return MOE_OK;
+}
+
+MOE_API int moe_workspace_status(const void* workspace, uint64_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (workspace == nullptr || workspace_bytes < 8) return MOE_EINVAL;
+  if (!aligned16(workspace)) return MOE_EALIGN;
+  int st = check_device();
+  if (st) return st;
+  // the word is the first 8 bytes of every workspace (see carve)
+  unsigned long long word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, 8, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if ((st = launched(e, stream))) return st;
+  if (word != moe::kWaitGaveUp) return MOE_OK;
+  const unsigned long long zero = 0;
+  e = hipMemcpyAsync(const_cast<void*>(workspace), &zero, 8, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if ((st = launched(e, stream))) return st;
+  return MOE_ETIMEOUT;
+}
+
+MOE_API int moe_workspace_region(const moe_layer_desc* layer, int64_t n_tokens, int32_t region,
+                                 uint64_t* offset, uint64_t* bytes) {
+  if (offset == nullptr || bytes == nullptr) return MOE_EINVAL;
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  const Carve c = carve(layer, n_tokens);
+  const uint64_t t = uint64_t(n_tokens), k = uint64_t(layer->top_k);
+  const uint64_t Kq = pad512(layer->hidden), Iq = pad512(layer->inter);
+  switch (region) {
+    case MOE_WS_PAIRS: *offset = c.pairs; *bytes = t * k * 4; break;
+    case MOE_WS_X_CODES: *offset = c.xq; *bytes = t * Kq; break;
+    case MOE_WS_X_SCALES: *offset = c.xs; *bytes = t * Kq / 32; break;
+    case MOE_WS_H_CODES: *offset = c.hq; *bytes = t * k * Iq; break;
+    case MOE_WS_H_SCALES: *offset = c.hs8; *bytes = t * k * Iq / 32; break;
+    default: return MOE_EINVAL;
+  }
+  return MOE_OK;
 }

@@ -27,6 +27,12 @@ inline void launch_timed(LaunchEvents ev, K kernel, dim3 grid, dim3 block, uint3
     hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
 }
 
+// Value of the workspace status word after a top-k wait gave up (even, so
+// never an epoch; any other value means no wait gave up).
+constexpr unsigned long long kWaitGaveUp = 0x5449'4D45'4F55'5400ull;
+// Default number of polls before a top-k wait gives up (~0.3 us each).
+constexpr long kDefaultSpinLimit = 1l << 20;
+
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
@@ -65,13 +71,16 @@ struct GemvLayer {
   // Direct mode (one token): expert slot a is pair a, its expert ids_in[a];
   // no plan is built (the k experts of one token are distinct).
   int direct;
-  // Completion flags of the logits workgroups ([n_logits], at the start of
-  // the workspace): each stores `epoch` once its logits are stored, for a
+  // Completion flags of the logits workgroups ([n_logits], near the start
+  // of the workspace): each stores `epoch` once its logits are stored, for a
   // top-k workgroup of the same launch to wait on; that workgroup clears
-  // them.  epoch differs between calls; lflags[n_logits] is 1 if the wait
-  // gave up, else 0 (see select_waits in layer.hip).
+  // them.  epoch differs between calls (odd values).  A wait that gives up
+  // after spin_limit polls stores kWaitGaveUp into *status (the first word
+  // of the workspace), which only moe_workspace_status clears.
   unsigned long long* lflags;
+  unsigned long long* status;
   unsigned long long epoch;
+  long spin_limit;
   // 1: logits[t][e] complete; kRouterSplit: logits holds kRouterSplit partial
   // sums [q][t][e] over quarters of the contraction (bias in quarter 0),
   // which the top-k adds in order

@@ -1137,20 +1137,20 @@ __device__ void combine_role(const GemvLayer& L, int b) {
 // block) waits until every logits workgroup has flagged its logits with this
 // call's epoch, then clears the flags for the next call.  Only this one
 // workgroup waits, on workgroups that wait on nothing, so the others always
-// get to run.  The wait is bounded: lflags[n] is set to 1 if it gave up (0
-// otherwise), and the selection then runs on what is there (wrong results,
-// no hang).
-constexpr long kSelectSpinLimit = 1l << 20;  // polls of ~0.3 us
+// get to run.  The wait is bounded (L.spin_limit polls): if it gives up, the
+// workspace status word is set to kWaitGaveUp, which the caller reads with
+// moe_workspace_status, and the selection runs on what is there (wrong
+// results, no hang).
 __device__ void select_waits(const GemvLayer& L, int n) {
   bool done = false;
-  for (long it = 0; it < kSelectSpinLimit && !done; ++it) {
+  for (long it = 0; it < L.spin_limit && !done; ++it) {
     int ok = 1;
     for (int i = threadIdx.x; i < n; i += kThreads) ok &= load_coherent(&L.lflags[i]) == L.epoch;
     done = __syncthreads_and(ok) != 0;
     if (!done) __builtin_amdgcn_s_sleep(8);
   }
   for (int i = threadIdx.x; i < n; i += kThreads) L.lflags[i] = 0;
-  if (threadIdx.x == 0) L.lflags[n] = done ? 0ull : 1ull;
+  if (threadIdx.x == 0 && !done) store_coherent(L.status, kWaitGaveUp);
 }
 
 template <bool kCoherent = false>

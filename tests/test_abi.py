@@ -199,3 +199,31 @@ def test_valid_call_without_gfx950_refuses(lib):
     st = L.moe_route(ctypes.byref(d), P(0x100000), 2, P(0x200000), P(0x300000), P(0x500000),
                      need, None)
     assert st == -5
+
+
+def test_status_and_region_calls(lib):
+    """The workspace status query and the region export validate on the host;
+    the regions of one workspace are disjoint and inside it."""
+    L = lib.lib()
+    P = ctypes.c_void_p
+    assert L.moe_workspace_status(None, 64, None) == -1
+    assert L.moe_workspace_status(P(0x100000), 4, None) == -1
+    assert L.moe_workspace_status(P(0x100004), 64, None) == -2
+    assert L.moe_set_wait_limit(-1) == 0
+    assert L.moe_status_string(-8)
+    d = _desc(lib)
+    off, n = ctypes.c_uint64(), ctypes.c_uint64()
+    for T in (1, 7, 300):
+        _, total = _ws(lib, d, T)
+        spans = []
+        for region in range(5):
+            assert L.moe_workspace_region(ctypes.byref(d), T, region, ctypes.byref(off),
+                                          ctypes.byref(n)) == 0
+            assert off.value % 16 == 0 and off.value + n.value <= total
+            spans.append((off.value, off.value + n.value))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[0][0] >= 8  # the status word stays first
+    assert L.moe_workspace_region(ctypes.byref(d), 4, 5, ctypes.byref(off), ctypes.byref(n)) == -1
+    assert L.moe_workspace_region(ctypes.byref(d), 0, 0, ctypes.byref(off), ctypes.byref(n)) == -1
+    assert L.moe_workspace_region(ctypes.byref(d), 4, 0, None, ctypes.byref(n)) == -1

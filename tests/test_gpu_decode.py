@@ -15,7 +15,8 @@ import synth.device as SD
 from oracle import formats as F
 from oracle import moe as M
 from oracle import record as R
-from tests._gpu import Built, check_parity, check_routing, oracle_weights, to_np_u16
+from tests._gpu import (Built, check_parity, check_routing, oracle_weights, to_np_u16,
+                        topk_candidates)
 
 pytestmark = pytest.mark.gpu
 
@@ -154,9 +155,12 @@ def test_route_entry_matches_oracle_and_layer_routing(b):
 
 
 def test_route_many_winners_in_one_lane(b):
-    # Experts 5, 69, 133, ... (e = 5 mod 64) sit in one lane of the top-k
-    # wave; a large bias makes all 16 of them winners, more than the lane's
-    # candidate list holds, so the selection must take its exact path.
+    """Experts 5, 69, 133, ... (e = 5 mod 64) sit in one lane of the top-k
+    wave; a bias of +20 makes all 16 of them winners, so one lane contributes
+    a single maximum but 16 of the 32 selected experts.  The threshold (k-th
+    of the 64 lane maxima) then admits 56-58 candidates, all ranked in the
+    candidate list (the exact path past 256 candidates is covered by
+    test_gpu_topk_exact.py)."""
     built = Built(MANY, seed=6, bias=True)
     bias = built.dev["host_bias"].copy()
     bias[5::64] += 20.0
@@ -165,6 +169,7 @@ def test_route_many_winners_in_one_lane(b):
     xh, xd = SD.upload_tokens(1301, 5, MANY["hidden"])
     ids, w = _route(b, built, xd)
     _, _, s = M.route(xh, built.oracle)
+    assert all(32 < topk_candidates(s[t], 32) <= 256 for t in range(5))
     check_routing(ids, w, s, MANY["top_k"])
     np.testing.assert_allclose(w, oracle_weights(s, ids), rtol=0, atol=2e-6)
     for t in range(5):
@@ -322,13 +327,13 @@ def test_alternating_batch_sizes_share_a_workspace(b):
     """One workspace, token counts alternating over the three launch
     structures (one token: no plan; 2-4 tokens: top-k and plan inside the
     router launch; more: a top-k launch).  Every call matches the oracle,
-    and after each call the logits completion flags at the start of the
-    workspace are all clear (the top-k workgroup clears what it waited on,
-    and the give-up word is 0)."""
+    and after each call the logits completion flags (after the status
+    word's 256-byte slot at the start of the workspace) are all clear (the
+    top-k workgroup clears what it waited on) and no wait gave up."""
     cfg = dict(hidden=512, inter=128, n_experts=64, top_k=6, n_shared=2)
     built = Built(cfg, seed=11)
     ws = built.lib.workspace(9)
-    n_flags = (64 + 3) // 4 + 1
+    n_flags = (64 + 3) // 4
     for i, T in enumerate([1, 4, 9, 2, 1, 3, 9, 1]):
         xh, xd = SD.upload_tokens(1900 + i, T, 512)
         ids = torch.empty((T, 6), dtype=torch.int32, device="cuda")
@@ -337,8 +342,9 @@ def test_alternating_batch_sizes_share_a_workspace(b):
         b.moe_layer(built.lib, xd, y, ids, w, ws, path=b.PATH_GEMV)
         torch.cuda.synchronize()
         if T <= 4:
-            flags = ws[: 8 * n_flags].cpu().numpy().view(np.uint64)
+            flags = ws[256:256 + 8 * n_flags].cpu().numpy().view(np.uint64)
             assert not flags.any(), (T, flags)
+        assert b.workspace_status(ws) == b.MOE_OK
         _, _, s = M.route(xh, built.oracle)
         ids_np = ids.cpu().numpy()
         check_routing(ids_np, w.cpu().numpy(), s, 6)

@@ -13,7 +13,8 @@ import synth
 import synth.device as SD
 from oracle import moe as M
 from oracle import record as R
-from tests._gpu import REL_TOL, Built, check_routing, oracle_weights, rel_l2_per_token, to_np_u16
+from tests._gpu import (Built, check_mxfp8_workspace, check_parity, check_routing, oracle_rows,
+                        oracle_weights, to_np_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,10 +60,9 @@ def test_k3_decode_batch1(b, k3, seed):
     ids, w, y = _run(b, k3, xd)
     _, _, s = M.route(xh, k3.oracle)
     check_routing(ids, w, s, 16)
-    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids))
-    err = rel_l2_per_token(y, ref)
+    ref = oracle_rows(xh, k3.oracle, ids, oracle_weights(s, ids), [0])
+    err = check_parity(y, ref, strict=True)
     print(f"K3 b=1 seed {seed}: rel L2 {err.max():.3e}")
-    assert err.max() <= REL_TOL
 
 
 def test_k3_batched_decode_64(b, k3):
@@ -73,11 +73,13 @@ def test_k3_batched_decode_64(b, k3):
     distinct = len(np.unique(ids))
     print(f"K3 b=64: {distinct} distinct experts")
     assert 500 < distinct < 700
-    sample = [0, 21, 42, 63]
-    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids), tokens=sample)
-    err = rel_l2_per_token(y[sample], ref)
-    print(f"K3 b=64 sampled rel L2 {err.max():.3e}")
-    assert err.max() <= REL_TOL
+    # tokens of the experts that 4 or more tokens share, plus a spread
+    cnt = np.bincount(ids.ravel(), minlength=896)
+    busy = np.nonzero(np.isin(ids, np.nonzero(cnt >= 4)[0]).any(axis=1))[0]
+    sample = sorted(set([0, 21, 42, 63]) | set(busy[:12].tolist()))
+    ref = oracle_rows(xh, k3.oracle, ids, oracle_weights(s, ids), sample)
+    err = check_parity(y[sample], ref, strict=True)
+    print(f"K3 b=64 {len(sample)} sampled tokens rel L2 {err.max():.3e}")
 
 
 def test_k3_eight_tokens_with_residual(b, k3):
@@ -86,10 +88,9 @@ def test_k3_eight_tokens_with_residual(b, k3):
     ids, w, y = _run(b, k3, xd, residual=rd)
     _, _, s = M.route(xh, k3.oracle)
     check_routing(ids, w, s, 16)
-    sample = [1, 6]
-    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids), residual_bits=rh,
-                        tokens=sample)
-    assert rel_l2_per_token(y[sample], ref).max() <= REL_TOL
+    sample = list(range(8))
+    ref = oracle_rows(xh, k3.oracle, ids, oracle_weights(s, ids), sample, residual_bits=rh)
+    check_parity(y[sample], ref, strict=True)
 
 
 @pytest.mark.parametrize("top_k,T", [(8, 1), (8, 8), (4, 64)])
@@ -111,16 +112,20 @@ def test_k3_reduced_top_k(b, k3, top_k, T):
     _, _, s = M.route(xh, orc)
     check_routing(ids, w, s, top_k)
     sample = sorted({0, T // 2, T - 1})
-    ref = M.moe_forward(xh, orc, ids, oracle_weights(s, ids), tokens=sample)
-    err = rel_l2_per_token(y[sample], ref)
+    ref = oracle_rows(xh, orc, ids, oracle_weights(s, ids), sample)
+    err = check_parity(y[sample], ref, strict=True)
     print(f"K3 top-{top_k} T={T}: rel L2 {err.max():.3e}")
-    assert err.max() <= REL_TOL
 
 
 def test_k3_prefill_4096_with_bias(b, k3):
     """K3 prefill (4096 tokens, per-expert logit bias N(0, 0.5)) on the MFMA
-    path: routing for every token, output on sampled tokens against the
-    oracle in its MXFP8-activation mode."""
+    path: routing for every token; the layer's MXFP8 x codes bit-exact on
+    512 tokens; its h codes element by element for every pair of every
+    expert the sampled tokens use; and the output of 32 or more
+    tokens against the oracle in its MXFP8-activation mode -- every token of
+    the most loaded expert's last (ragged) 64-token tile, every token of
+    the least loaded expert and of one with about 3 pairs, the first and
+    last token, and a spread."""
     from synth import router_bias
     bias_h = router_bias(0, 0, 896)
     lay = b.Layer(7168, 1536, 896, 16, k3.lib.router_w, k3.lib.experts, k3.lib.shared_gate,
@@ -132,7 +137,8 @@ def test_k3_prefill_4096_with_bias(b, k3):
     ids = torch.empty((T, 16), dtype=torch.int32, device="cuda")
     w = torch.empty((T, 16), dtype=torch.float32, device="cuda")
     y = torch.empty((T, 7168), dtype=torch.int16, device="cuda")
-    b.moe_layer(lay, xd, y, ids, w, lay.workspace(T), path=b.PATH_MFMA)
+    ws = lay.workspace(T)
+    b.moe_layer(lay, xd, y, ids, w, ws, path=b.PATH_MFMA)
     torch.cuda.synchronize()
     ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
     _, _, s = M.route(xh, orc)
@@ -141,11 +147,33 @@ def test_k3_prefill_4096_with_bias(b, k3):
     print(f"K3 prefill: {n_amb} near-tie tokens; pairs per expert min {per_expert.min()} "
           f"median {int(np.median(per_expert))} max {per_expert.max()}")
     assert per_expert.sum() == T * 16 and (per_expert > 0).all()
-    sample = [0, 1777, 4095]
-    ref = M.moe_forward(xh, orc, ids, oracle_weights(s, ids), act_mxfp8=True, tokens=sample)
-    err = rel_l2_per_token(y[sample], ref)
-    print(f"K3 prefill sampled rel L2 {err.max():.3e}")
-    assert err.max() <= REL_TOL
+    busiest, idlest = int(per_expert.argmax()), int(per_expert.argmin())
+    few = int(np.argmin(np.abs(per_expert - 3)))  # an expert with (about) 3 pairs
+    assert per_expert[busiest] % 64 != 0 and per_expert[few] <= 4
+    # the busiest expert's last tile: its last pairs in the plan's order
+    pairs = b.workspace_region(lay, T, b.WS_PAIRS, ws).cpu().numpy().view(np.int32)
+    grp = pairs[ids.reshape(-1)[pairs] == busiest]
+    last_tile = grp[(len(grp) - 1) // 64 * 64:] // 16
+    small = np.nonzero(np.isin(ids, [idlest, few]).any(axis=1))[0]
+    rng = np.random.default_rng(4)
+    sample = set(last_tile.tolist()) | set(small.tolist()) | {0, T - 1}
+    sample |= set(rng.choice(T, 6, replace=False).tolist())
+    while len(sample) < 32:
+        sample.add(int(rng.integers(T)))
+    sample = sorted(sample)
+    # h codes of every pair of every expert the sampled tokens use (the
+    # busiest, idlest and 3-pair experts among them), and the exact effect of
+    # the legitimately different codes on the sampled tokens
+    eff = check_mxfp8_workspace(b, lay, ws, T, xh, ids, w, orc, tokens=sample,
+                                x_rows=np.sort(rng.choice(T, 512, replace=False)))
+    ref = oracle_rows(xh, orc, ids, oracle_weights(s, ids), sample, act_mxfp8=True)
+    err = check_parity(y[sample], ref, eff, strict=True)
+    moved = np.linalg.norm(eff, axis=1) / np.linalg.norm(ref, axis=1)
+    print(f"K3 prefill: h-code flips move {np.count_nonzero(moved)} of {len(sample)} sampled "
+          f"tokens, by at most {moved.max():.2e} relative")
+    print(f"K3 prefill {len(sample)} sampled tokens (busiest expert {busiest}: "
+          f"{per_expert[busiest]} pairs, last tile {len(last_tile)}; idlest {idlest}: "
+          f"{per_expert[idlest]}; {few}: {per_expert[few]}): rel L2 max {err.max():.3e}")
 
 
 @pytest.mark.parametrize("T", [1, 64])
@@ -172,9 +200,8 @@ def test_k3_router_bias_in_choice_only_with_routed_scale(b, k3, T):
     wo = M.combine_weights(s, ids, 2.5)
     np.testing.assert_allclose(w, wo, rtol=0, atol=5e-6)
     sample = sorted({0, T - 1})
-    err = rel_l2_per_token(y[sample], M.moe_forward(xh, orc, ids, wo, tokens=sample))
+    err = check_parity(y[sample], oracle_rows(xh, orc, ids, wo, sample), strict=True)
     print(f"K3 select-mode bias, scale 2.5, T={T}: rel L2 {err.max():.3e}")
-    assert err.max() <= REL_TOL
 
 
 def test_k3_decode_batch2_speculative_verify(b, k3):
@@ -184,16 +211,16 @@ def test_k3_decode_batch2_speculative_verify(b, k3):
     ids, w, y = _run(b, k3, xd)
     _, _, s = M.route(xh, k3.oracle)
     check_routing(ids, w, s, 16)
-    ref = M.moe_forward(xh, k3.oracle, ids, oracle_weights(s, ids))
-    err = rel_l2_per_token(y, ref)
+    ref = oracle_rows(xh, k3.oracle, ids, oracle_weights(s, ids), [0, 1])
+    err = check_parity(y, ref, strict=True)
     print(f"K3 T=2: rel L2 {err}")
-    assert err.max() <= REL_TOL
 
 
 def test_k3_pooled_experts_equal_resident(b, k3):
     """The 896 K3 records in pinned host memory, 64 HBM slots filled on
     demand: consecutive single tokens (new experts each time, some slots
-    evicted) give the resident layer's output bit for bit."""
+    evicted) give the resident layer's output bit for bit, and the first and
+    last tokens' pooled outputs match the oracle."""
     host = torch.empty(k3.lib.experts.shape, dtype=torch.uint8, pin_memory=True)
     host.copy_(k3.lib.experts)
     pool = b.ExpertPool(host, 64)
@@ -213,5 +240,55 @@ def test_k3_pooled_experts_equal_resident(b, k3):
             torch.cuda.synchronize()
             ys.append(to_np_u16(y))
         np.testing.assert_array_equal(ys[0], ys[1])
+        if i in (0, 5):
+            ids_np = ids.cpu().numpy()
+            _, _, s = M.route(xh, k3.oracle)
+            check_routing(ids_np, w.cpu().numpy(), s, 16)
+            ref = oracle_rows(xh, k3.oracle, ids_np, oracle_weights(s, ids_np), [0])
+            print(f"K3 pooled token {i}: rel L2 {check_parity(ys[0], ref, strict=True)[0]:.3e}")
     assert copied > 64  # the pool evicted and refilled
     del lay, pool, host
+
+
+def test_k3_three_stacked_layers_teacher_forced(b, k3):
+    """Three resident K3 layers (seeds [0, l, ...]), each RMSNorm -> MoE ->
+    residual, 8 decode tokens, in the launch configuration of the 12-layer
+    benchmark: per layer, the RMSNorm output within one bf16 ulp of the
+    oracle's, routing, and every token's output against the oracle given the
+    GPU's input to that layer (teacher forcing)."""
+    layers = [k3]
+    for l in (1, 2):
+        built = Built(synth.K3, seed=0, layer=l)
+        del built.dev["experts"]  # the packed copy is what the layer reads
+        layers.append(built)
+    T = 8
+    gammas = [SD.upload_gamma(0, l, 7168) for l in range(3)]
+    xh, xd = SD.upload_tokens(5400, T, 7168)
+    ws = k3.lib.workspace(T)
+    ys, normed, ids, wts = [xd], [], [], []
+    for l in range(3):
+        nd = torch.empty_like(xd)
+        b.rmsnorm(ys[-1], gammas[l][1], 1e-6, nd)
+        i_d = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+        w_d = torch.empty((T, 16), dtype=torch.float32, device="cuda")
+        y = torch.empty_like(xd)
+        b.moe_layer(layers[l].lib, nd, y, i_d, w_d, ws, residual=ys[-1], path=b.PATH_GEMV)
+        normed.append(nd)
+        ids.append(i_d)
+        wts.append(w_d)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert b.workspace_status(ws) == b.MOE_OK
+    for l in range(3):
+        x_in, n_gpu = to_np_u16(ys[l]), to_np_u16(normed[l])
+        n_ref = M.rmsnorm(x_in, gammas[l][0])
+        ulps = np.abs(n_gpu.view(np.int16).astype(np.int32) - n_ref.view(np.int16).astype(np.int32))
+        assert ulps.max() <= 1, f"layer {l}: RMSNorm off by {ulps.max()} ulp"
+        orc = layers[l].oracle
+        _, _, s = M.route(n_gpu, orc)
+        i_np = ids[l].cpu().numpy()
+        check_routing(i_np, wts[l].cpu().numpy(), s, 16)
+        ref = oracle_rows(n_gpu, orc, i_np, oracle_weights(s, i_np), range(T), residual_bits=x_in)
+        err = check_parity(to_np_u16(ys[l + 1]), ref, strict=True)
+        print(f"K3 stack layer {l}: {len(np.unique(i_np))} experts, rel L2 max {err.max():.3e}")
+    del layers[1:]

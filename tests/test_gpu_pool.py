@@ -3,8 +3,9 @@ a few HBM slots filled on demand; Deltafin README, I/O and streaming).
 
 The pooled layer runs the same kernels on the same packed records, only
 found through the slot map, so its output must equal the resident layer's
-bit for bit; the resident layer itself is pinned to the oracle by the other
-GPU tests.  The fetch bookkeeping (copies, hits, least-recently-used
+bit for bit; it is also compared with the oracle directly (routing, the
+per-token relative L2 bar and the element-wise bound; on the MFMA path the
+pooled call's MXFP8 codes too).  The fetch bookkeeping (copies, hits, least-recently-used
 eviction among the experts a call does not need) is checked by counts.
 """
 
@@ -14,7 +15,9 @@ import torch
 
 import synth
 import synth.device as SD
-from tests._gpu import Built, to_np_u16
+from oracle import moe as M
+from tests._gpu import (Built, check_mxfp8_workspace, check_parity, check_routing,
+                        oracle_weights, to_np_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,11 +50,27 @@ def _route(b, built, xd):
     return ids, w
 
 
-def _forward(b, lay, xd, ids, w, path):
+def _forward(b, lay, xd, ids, w, path, ws=None):
     y = torch.empty((xd.shape[0], lay.hidden), dtype=torch.int16, device="cuda")
-    b.forward(lay, xd, ids, w, y, lay.workspace(xd.shape[0]), path=path)
+    ws = lay.workspace(xd.shape[0]) if ws is None else ws
+    b.forward(lay, xd, ids, w, y, ws, path=path)
     torch.cuda.synchronize()
     return to_np_u16(y)
+
+
+def _check_oracle(built, xh, ids, w, y, mx=None):
+    """Pooled output against the oracle under the call's routing; mx =
+    (binding, layer, workspace) of an MFMA-path call to check its codes."""
+    ids_np, w_np = ids.cpu().numpy(), w.cpu().numpy()
+    _, _, s = M.route(xh, built.oracle)
+    check_routing(ids_np, w_np, s, built.cfg["top_k"])
+    ref = M.moe_forward(xh, built.oracle, ids_np, oracle_weights(s, ids_np),
+                        act_mxfp8=mx is not None)
+    eff = None
+    if mx is not None:
+        b, lay, ws = mx
+        eff = check_mxfp8_workspace(b, lay, ws, xh.shape[0], xh, ids_np, w_np, built.oracle)
+    check_parity(y, ref, eff)
 
 
 @pytest.mark.parametrize("cfg", [synth.TINY, RAGGED], ids=["tiny", "ragged"])
@@ -61,15 +80,16 @@ def test_pooled_layer_equals_resident_gemv(b, cfg, T):
     calls = []
     for call in range(6):  # new tokens each call
         xh, xd = SD.upload_tokens(3100 + 10 * T + call, T, cfg["hidden"])
-        calls.append((xd, *_route(b, built, xd)))
+        calls.append((xh, xd, *_route(b, built, xd)))
     # as many slots as the largest call needs: later calls must evict
-    n_slots = max(np.unique(ids.cpu().numpy()).size for _, ids, _ in calls)
+    n_slots = max(np.unique(ids.cpu().numpy()).size for _, _, ids, _ in calls)
     pool, lay = _pooled(b, built, n_slots)
     copied_total = 0
-    for xd, ids, w in calls:
+    for xh, xd, ids, w in calls:
         copied_total += pool.fetch(ids.cpu().numpy())
-        np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_GEMV),
-                                      _forward(b, built.lib, xd, ids, w, b.PATH_GEMV))
+        y = _forward(b, lay, xd, ids, w, b.PATH_GEMV)
+        np.testing.assert_array_equal(y, _forward(b, built.lib, xd, ids, w, b.PATH_GEMV))
+        _check_oracle(built, xh, ids, w, y)
     assert copied_total > n_slots  # some records were evicted and refilled
 
 
@@ -88,8 +108,10 @@ def test_pooled_layer_equals_resident_mfma(b, cfg, T):
     xh, xd = SD.upload_tokens(3300 + T, T, cfg["hidden"])
     ids, w = _route(b, built, xd)
     assert pool.fetch(ids.cpu().numpy()) == 0
-    np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_MFMA),
-                                  _forward(b, built.lib, xd, ids, w, b.PATH_MFMA))
+    ws = lay.workspace(T)
+    y = _forward(b, lay, xd, ids, w, b.PATH_MFMA, ws)
+    np.testing.assert_array_equal(y, _forward(b, built.lib, xd, ids, w, b.PATH_MFMA))
+    _check_oracle(built, xh, ids, w, y, mx=(b, lay, ws))
 
 
 def test_fetch_counts_and_lru_eviction(b):

@@ -19,7 +19,7 @@ import torch
 import synth.device as SD
 from oracle import formats as F
 from oracle import moe as M
-from tests._gpu import (Built, check_parity, check_routing, mxfp8_h_flip_allowance,
+from tests._gpu import (Built, check_mxfp8_workspace, check_parity, check_routing,
                         oracle_weights, to_np_u16)
 
 pytestmark = pytest.mark.gpu
@@ -42,7 +42,9 @@ def test_twelve_layer_stack_teacher_forced(b, path):
     gammas = [SD.upload_gamma(40, l, H) for l in range(N_LAYERS)]
     xh, xd = SD.upload_tokens(5000, T, H)
     p = b.PATH_GEMV if path == "gemv" else b.PATH_MFMA
-    ws = layers[0].lib.workspace(T)
+    # the MFMA path keeps each layer's workspace, whose MXFP8 codes are checked
+    shared_ws = layers[0].lib.workspace(T)
+    wss = [layers[l].lib.workspace(T) if path == "mfma" else shared_ws for l in range(N_LAYERS)]
     ys = [xd]
     normed, ids, wts = [], [], []
     for l in range(N_LAYERS):
@@ -51,7 +53,7 @@ def test_twelve_layer_stack_teacher_forced(b, path):
         i_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
         w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
         y = torch.empty_like(xd)
-        b.moe_layer(layers[l].lib, nd, y, i_d, w_d, ws, residual=ys[-1], path=p)
+        b.moe_layer(layers[l].lib, nd, y, i_d, w_d, wss[l], residual=ys[-1], path=p)
         normed.append(nd)
         ids.append(i_d)
         wts.append(w_d)
@@ -69,9 +71,9 @@ def test_twelve_layer_stack_teacher_forced(b, path):
         check_routing(i_np, w_np, s, k)
         w_ref = oracle_weights(s, i_np)
         ref = M.moe_forward(n_gpu, layers[l].oracle, i_np, w_ref, residual_bits=x_in, **act)
-        allow = (mxfp8_h_flip_allowance(n_gpu, layers[l].oracle, i_np, w_ref)
-                 if path == "mfma" else 0.0)
-        check_parity(to_np_u16(ys[l + 1]), ref, allow)
+        eff = (check_mxfp8_workspace(b, layers[l].lib, wss[l], T, n_gpu, i_np, w_np,
+                                     layers[l].oracle) if path == "mfma" else None)
+        check_parity(to_np_u16(ys[l + 1]), ref, eff)
     # end-to-end drift of the oracle's own chain (reported, not asserted)
     cur = xh
     for l in range(N_LAYERS):
