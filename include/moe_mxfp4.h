@@ -276,6 +276,25 @@ int moe_set_wait_limit(int64_t polls);
 int moe_workspace_region(const moe_layer_desc* layer, int64_t n_tokens, int32_t region,
                          uint64_t* offset, uint64_t* bytes);
 
+/*
+ * moe_layer for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same call
+ * without a workspace argument.  Its workspace is a static device array of
+ * MOE_SCRATCH_BYTES that the library holds on each device it runs on until
+ * the process ends; the call allocates nothing and calls no allocating
+ * routine.  A call whose workspace (moe_workspace_bytes) exceeds
+ * MOE_SCRATCH_BYTES returns MOE_EWORKSPACE and launches nothing (at the K3
+ * shape: up to 64 tokens fit).  Every call on a device shares that device's
+ * array: calls that overlap on one device (other streams, other host
+ * threads) race and must be ordered by the caller.  The array keeps the last
+ * call's contents; nothing in it needs clearing between calls.  A top-k wait
+ * that gives up (see moe_workspace_status) cannot be queried for these calls.
+ */
+#define MOE_SCRATCH_BYTES (64ull << 20)
+int moe_layer_scratch(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                      const uint16_t* residual, uint16_t* y, int32_t* topk_ids, float* topk_w,
+                      int32_t path, hipStream_t stream);
+
 /* Smallest n_tokens for which MOE_PATH_AUTO takes the MFMA path. */
 int64_t moe_mfma_min_tokens(void);
 

@@ -92,6 +92,7 @@ _SIGNATURES = {
     "moe_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "moe_pool_destroy": (ctypes.c_int, [_P]),
     "moe_workspace_status": (ctypes.c_int, [_P, _U64, _P]),
+    "moe_layer_scratch": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P]),
     "moe_set_wait_limit": (ctypes.c_int, [_I64]),
     "moe_workspace_region": (ctypes.c_int, [_DESC, _I64, _I32, ctypes.POINTER(_U64),
                                             ctypes.POINTER(_U64)]),
@@ -290,6 +291,13 @@ def moe_layer(layer, x, y, topk_ids, topk_w, ws, residual=None, path=PATH_AUTO, 
     _check(_lib().moe_layer(layer.desc, _ptr(x), x.shape[0], _ptr(residual), _ptr(y),
                             _ptr(topk_ids), _ptr(topk_w), path, _ptr(ws), ws.numel(),
                             _stream(stream)), "moe_layer")
+
+
+def moe_layer_scratch(layer, x, y, topk_ids, topk_w, residual=None, path=PATH_AUTO, stream=None):
+    """moe_layer on the library's static per-device scratch (no workspace)."""
+    _check(_lib().moe_layer_scratch(layer.desc, _ptr(x), x.shape[0], _ptr(residual), _ptr(y),
+                                    _ptr(topk_ids), _ptr(topk_w), path, _stream(stream)),
+           "moe_layer_scratch")
 
 
 def rmsnorm(x, gamma, eps, out, stream=None):

@@ -6,6 +6,7 @@
 #include <chrono>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_mxfp4.h"
 #include "common.hpp"
@@ -571,6 +572,60 @@ MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
     return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
   return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
+}
+
+// The workspace of moe_layer_scratch: one array per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once per
+// device (scratch_address), and only that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MOE_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (looked up on the device's
+// first call, with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EDEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const int st = launched(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), nullptr);
+      if (st) return st;
+      if (p == nullptr) return MOE_ELAUNCH;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API int moe_layer_scratch(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                              const uint16_t* residual, uint16_t* y, int32_t* topk_ids,
+                              float* topk_w, int32_t path, hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_EALIGN;
+  if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (carve(layer, n_tokens).total > MOE_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  prof_begin(stream);
+  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
+    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, ws, stream);
+  return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, ws, stream);
 }
 
 MOE_API int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n_tokens,
