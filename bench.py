@@ -41,7 +41,9 @@ REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
 SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 # kernels of one moe_layer call, in launch order (see moe_profile_events)
 KERNELS_GEMV = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
-# up to 4 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
+# one token: router, top-k, shared experts and routed gate/up in one launch
+KERNELS_GEMV_ONE = ["decode_front", "routed_down_combine"]
+# 2 to 4 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
 KERNELS_GEMV_SMALL = ["router_shared_gateup_topk", "shared_down_routed_gateup", "routed_down_combine"]
 KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
@@ -95,7 +97,7 @@ def parse():
 
 
 # dominant launch per config: (HIP kernel name in traces, name in kernel_us)
-PMC_KERNELS = {"b1": ("moe_routed_gateup", "shared_down_routed_gateup"),
+PMC_KERNELS = {"b1": ("moe_decode_front", "decode_front"),
                "int8_dequant": ("int8_row_dequant_kernel", "int8_row_dequant")}
 
 
@@ -187,6 +189,10 @@ def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
                 + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
     if name == "routed_down_combine":
         return D * MAT_BYTES + T * k * I * 4 + T * k * 4 + S * T * H * 4 + x
+    if name == "decode_front":  # router + top-k + shared experts + routed gate/up
+        return (kernel_bytes("router_shared_gateup_topk", T, k, D, S, H, I, E)
+                + D * 2 * MAT_BYTES + T * k * 4 + T * k * I * 4
+                + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
     # prefill (MFMA) path; MXFP8 rows are padded to multiples of 512 (exact at K3)
     xq = T * H * (1 + 1 / 32)
     hq = T * k * I * (1 + 1 / 32)
@@ -374,7 +380,8 @@ def main():
         args.warmup = cfgd.get("warmup", 20)
     mfma = cfgd.get("path") == "mfma"
     path = b.PATH_MFMA if mfma else b.PATH_GEMV
-    KERNELS = KERNELS_MFMA if mfma else (KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
+    KERNELS = (KERNELS_MFMA if mfma else KERNELS_GEMV_ONE if T == 1
+               else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
     replicas = args.replicas or cfgd["replicas"]
     c = synth.K3
     H, I, E, k, S = c["hidden"], c["inter"], c["n_experts"], c["top_k"], c["n_shared"]

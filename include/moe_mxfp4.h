@@ -359,8 +359,10 @@ int moe_pool_destroy(moe_expert_pool* pool);
  * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
- * + combine -- for up to 4 tokens: router logits + shared gate/up + top-k
- * (and plan), shared down + routed gate/up, routed down + combine;
+ * + combine -- for 2 to 4 tokens: router logits + shared gate/up + top-k
+ * and plan, shared down + routed gate/up, routed down + combine; for one
+ * token: router logits + shared gate/up + top-k + routed gate/up + shared
+ * down (one launch), routed down + combine;
  * moe_layer (MFMA path): x to MXFP8 + router logits, top-k + plan, routed +
  * shared gate/up, routed + shared down, combine; moe_forward (MFMA path):
  * plan + x to MXFP8, then the same last three.  The caller creates and owns the hipEvent_t

@@ -137,7 +137,7 @@ unsigned long long next_epoch() {
 
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t status, lflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
+  uint64_t status, lflags, idsflag, sgflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
   uint64_t n_mtiles, mtiles, xq, xs, hq, hs8, total;
 };
 
@@ -153,6 +153,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
   };
   c.status = take(8);  // first: the same place for every layer and T
   c.lflags = take(uint64_t(n_logit_wgs(L)) * 8);
+  c.idsflag = take(8);
+  c.sgflags = take(S * (I / 16) * 8);
   c.logits = take(t * E * 4 * (T >= moe::kRouterSplitMin ? moe::kRouterSplit : 1));
   c.n_active = take(4);
   c.active = take(E * 4);
@@ -210,6 +212,8 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.logits = at<float>(ws, c.logits);
   G.lflags = at<unsigned long long>(ws, c.lflags);
   G.status = at<unsigned long long>(ws, c.status);
+  G.idsflag = at<unsigned long long>(ws, c.idsflag);
+  G.sgflags = at<unsigned long long>(ws, c.sgflags);
   G.epoch = next_epoch();
   G.spin_limit = g_wait_limit;
   G.lsplit = 1;
@@ -312,11 +316,27 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   moe::Stage s1;
   s1.n_logits = n_router_wgs(L, T);
   s1.n_sgu = S * (L->inter / 16);
+  if (T == 1) {
+    // one token: router, top-k, shared experts and routed gate/up in one
+    // launch whose workgroups wait on flags of earlier blocks
+    // (moe_decode_front); no plan (direct mode); then the routed down and the
+    // combine
+    G.direct = 1;
+    G.front = 1;
+    s1.n_selw = 1;
+    s1.plan_after_select = 1;
+    s1.n_rgu = ma * tiles_gu;
+    s1.n_sdn = S * n_shared_tiles(L);
+    int st = stage(moe::StageKind::DecodeFront, G, s1, stream);
+    if (st) return st;
+    G.front = 0;
+    moe::Stage s4;
+    s4.n_rdn = ma * n_tiles(L);
+    return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
+  }
   if (n_select_wgs(T) == 1) {
-    // up to 4 tokens: the top-k (and for several tokens the plan) runs in
-    // the router launch, on one workgroup that waits for the logits; one
-    // token needs no plan (direct mode)
-    G.direct = T == 1;
+    // 2 to 4 tokens: the top-k and the plan run in the router launch, on one
+    // workgroup that waits for the logits
     s1.n_selw = 1;
     s1.plan_after_select = 1;
     int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);

@@ -95,6 +95,15 @@ struct GemvLayer {
   float* ysh;               // fp32 [S][T][H]  shared expert outputs
   int* tile_cnt;            // [n_tiles] routed down arrivals per output tile (zeroed by
                             // the plan builder of the same call)
+  // One-token decode front (moe_decode_front: router, top-k, shared experts
+  // and routed gate/up in one launch): the top-k stores `epoch` into
+  // *idsflag once its ids and weights are stored, which the routed gate/up
+  // workgroups wait for; each shared gate/up workgroup stores it into
+  // sgflags[sx * I/16 + rg] once its h rows are stored, which the shared
+  // down workgroups of expert sx wait for.
+  int front;
+  unsigned long long* idsflag;
+  unsigned long long* sgflags;
   // prefill (MFMA) path: MXFP8 activations, rows padded to Kq / Iq columns
   // (multiples of 512, zero codes past H / I); scale rows in MFMA order
   int Kq, Iq;
@@ -129,6 +138,8 @@ struct Stage {
 
 enum class StageKind {
   RouterSharedGateUp,  // roles: logits, shared gate/up, top-k waiting for the logits
+  DecodeFront,         // one token: logits, shared gate/up, top-k, routed gate/up, shared
+                       // down, each waiting on flags of blocks before it
   SelectSharedDown,    // roles: top-k (+ plan), shared down
   PlanSharedGateUp,    // roles: plan, shared gate/up
   RoutedGateUp,        // roles: shared down, routed gate/up

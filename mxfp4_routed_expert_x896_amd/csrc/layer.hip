@@ -222,6 +222,22 @@ __device__ __forceinline__ void pipelineN(int s0, int s1, Buf (&b)[D], Load load
 }
 
 // ------------------------------------------------------------------------
+// Waits until flags[0 .. n) all hold this call's epoch, or gives up after
+// L.spin_limit polls and sets the workspace status marker (the caller reads
+// it with moe_workspace_status; the work then runs on what is there: wrong
+// results, no hang).  Every thread of the workgroup calls it.
+__device__ void wait_flags(const GemvLayer& L, const unsigned long long* flags, int n) {
+  bool done = false;
+  for (long it = 0; it < L.spin_limit && !done; ++it) {
+    int ok = 1;
+    for (int i = threadIdx.x; i < n; i += kThreads) ok &= load_coherent(&flags[i]) == L.epoch;
+    done = __syncthreads_and(ok) != 0;
+    if (!done) __builtin_amdgcn_s_sleep(8);
+  }
+  if (threadIdx.x == 0 && !done) store_coherent(L.status, kWaitGaveUp);
+}
+
+// ------------------------------------------------------------------------
 // Gate/up.  Workgroup = (expert, 32 rows): wave w takes row group w / 2 of
 // the tile and half w % 2 of the contraction; the halves meet in LDS.  The
 // tokens' x rows are staged in LDS (B operand), mtp at a time.  Weight
@@ -321,7 +337,9 @@ __device__ __forceinline__ void slot_of(const GemvLayer& L, int a, int& n, int& 
                                         int& p1) {
   if (L.direct) {
     n = L.T * L.k;
-    e = min(max(L.ids_in[min(a, n - 1)], 0), L.E - 1);  // clamped like the plan's ids
+    const int32_t* p = L.ids_in + min(a, n - 1);
+    // in the front launch the top-k wrote them in this launch: coherent load
+    e = min(max(L.front ? load_coherent(p) : *p, 0), L.E - 1);  // clamped like the plan's ids
     p0 = a;
     p1 = a + 1;
     return;
@@ -454,15 +472,25 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
     });
     join_quarters(ag, au, red);
     if (wave == 0 && c < mt) {
+      uint64_t hi4 = 0, lo4 = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint16_t hi, lo;
         split_bf16(silu(ag[i]) * au[i], hi, lo);
-        const size_t o = (size_t(sx) * L.T + t0 + c) * I + rg * 16 + 4 * g + i;
-        L.hs[o] = hi;
-        L.hs[plane + o] = lo;
+        hi4 |= uint64_t(hi) << (16 * i);
+        lo4 |= uint64_t(lo) << (16 * i);
       }
+      // rows 4 g .. 4 g + 3: one 8-byte store per part (through the coherent
+      // level: in the front launch the shared down reads them)
+      const size_t o = (size_t(sx) * L.T + t0 + c) * I + rg * 16 + 4 * g;
+      store_coherent(reinterpret_cast<uint64_t*>(L.hs + o), hi4);
+      store_coherent(reinterpret_cast<uint64_t*>(L.hs + plane + o), lo4);
     }
+  }
+  if (L.front) {  // h rows stored: flag them for the shared down of this launch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent(&L.sgflags[sx * (I / 16) + rg], L.epoch);
   }
 }
 
@@ -1142,15 +1170,9 @@ __device__ void combine_role(const GemvLayer& L, int b) {
 // moe_workspace_status, and the selection runs on what is there (wrong
 // results, no hang).
 __device__ void select_waits(const GemvLayer& L, int n) {
-  bool done = false;
-  for (long it = 0; it < L.spin_limit && !done; ++it) {
-    int ok = 1;
-    for (int i = threadIdx.x; i < n; i += kThreads) ok &= load_coherent(&L.lflags[i]) == L.epoch;
-    done = __syncthreads_and(ok) != 0;
-    if (!done) __builtin_amdgcn_s_sleep(8);
-  }
+  wait_flags(L, L.lflags, n);
+  __syncthreads();
   for (int i = threadIdx.x; i < n; i += kThreads) L.lflags[i] = 0;
-  if (threadIdx.x == 0 && !done) store_coherent(L.status, kWaitGaveUp);
 }
 
 template <bool kCoherent = false>
@@ -1182,15 +1204,20 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
       select_token<kCoherent>(lrow, 0, L.E, L.k, id, w, sc[wave], nullptr, L.rscale);
     }
     if (lane < L.k) {
-      if (single) {
+      if (single && !L.front) {
         L.ids_out[size_t(t) * L.k + lane] = id;
         L.w_out[size_t(t) * L.k + lane] = w;
         own_ids[t * L.k + lane] = id;
-      } else {
+      } else {  // read by other workgroups of this launch (or the next top-k's plan)
         store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
         store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
       }
     }
+  }
+  if (L.front) {  // ids and weights stored (above): flag them for the routed gate/up
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent(L.idsflag, L.epoch);
   }
   if (!st.plan_after_select) return;
   if (L.direct) {  // no plan: only the combine's arrival counters need clearing
@@ -1347,7 +1374,62 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   }
 }
 
+// One-token decode front: every workgroup role of the layer up to the
+// routed down, in one launch, in this block order: router logits (each flags
+// its logits), shared gate/up (each flags its h rows), the top-k (waits for
+// the logits flags, flags its ids and weights), routed gate/up (waits for the
+// ids flag), shared down (waits for its shared expert's gate/up flags).  A
+// workgroup only waits for blocks with lower indices, which the dispatcher
+// hands out first (in order on every XCD), so the lowest-indexed unfinished
+// block can always run to its end: every wait ends; each is bounded besides
+// (wait_flags).  The routed gate/up stream starts as soon as the top-k is
+// done, while the shared experts still stream, instead of after a launch
+// boundary.
+template <int NCH>
+__device__ __forceinline__ void front_body(const GemvLayer& L, const Stage& st) {
+  extern __shared__ u32x4 lds_raw[];
+  uint16_t* lds16p = reinterpret_cast<uint16_t*>(lds_raw);
+  __shared__ float red[kWaves * kWave * 8];
+  const int sgu_rows = L.I / 16, gu_tiles = L.I / 32;
+  int b = blockIdx.x;
+  if (b < st.n_logits) {
+    if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
+    router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent(&L.lflags[b], L.epoch);
+    return;
+  }
+  b -= st.n_logits;
+  if (b < st.n_sgu) {
+    shared_gateup<false>(L, b / sgu_rows, b % sgu_rows, red);
+    return;
+  }
+  b -= st.n_sgu;
+  if (b < st.n_selw) {
+    select_waits(L, st.n_logits);
+    select_role<true>(L, st, 0);
+    return;
+  }
+  b -= st.n_selw;
+  if (b < st.n_rgu) {
+    wait_flags(L, L.idsflag, 1);
+    routed_gateup(L, b / gu_tiles, b % gu_tiles, lds16p, red);
+    return;
+  }
+  b -= st.n_rgu;
+  if (b < st.n_sdn) {
+    const int sx = b / L.n_stiles;
+    wait_flags(L, L.sgflags + sx * sgu_rows, sgu_rows);
+    shared_down<false>(L, sx, b % L.n_stiles);
+  }
+}
+
 // The launches, named for what they run.
+template <int NCH>
+__global__ __launch_bounds__(kThreads) void moe_decode_front(GemvLayer L, Stage st) {
+  front_body<NCH>(L, st);
+}
 template <int NCH>
 __global__ __launch_bounds__(kThreads) void moe_router_shared_gateup(GemvLayer L, Stage st) {
   stage_body<kRoleLogits | kRoleSharedGU | kRoleSelectWait, NCH>(L, st);
@@ -1420,6 +1502,17 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
         launch_timed(ev, moe_router_shared_gateup<16>, grid, block, lds, stream, L, st);
       break;
     }
+    case StageKind::DecodeFront: {
+      const int per_lane = (L.H / 8 + kWave - 1) / kWave;
+      if (per_lane <= 4)
+        launch_timed(ev, moe_decode_front<4>, grid, block, lds, stream, L, st);
+      else if (per_lane <= 8)
+        launch_timed(ev, moe_decode_front<8>, grid, block, lds, stream, L, st);
+      else
+        launch_timed(ev, moe_decode_front<16>, grid, block, lds, stream, L, st);
+      break;
+    }
+
     case StageKind::SelectSharedDown:
       launch_timed(ev, moe_select_shared_down, grid, block, lds, stream, L, st);
       break;
