@@ -1,7 +1,8 @@
 """Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream|int8_dequant]
+                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream|int8_dequant|
+                              mfma_rate]
 
 A step is one full pass of the layer (router GEMV + top-k, token->expert
 plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
@@ -73,6 +74,9 @@ CONFIGS = {
     "int8_dequant": dict(kind="int8_dequant", rows=32768, cols=7168, steps=50, warmup=5,
                          desc="row-scaled int8 -> fp32 expansion of a dense weight matrix, "
                               "32768 x 7168 (235 MB int8 -> 940 MB fp32)"),
+    "mfma_rate": dict(kind="mfma_rate", steps=10, warmup=3,
+                      desc="issue rate of the block-scaled 16x16x128 MFMA: FP4 x FP4 vs FP4 x FP8 "
+                           "(vs FP8 x FP8), register operands, 8 independent accumulators per wave"),
     "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
                     desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
                          "MXFP8 activations on block-scaled MFMA"),
@@ -93,6 +97,9 @@ def parse():
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/pmc_<kernel>_<config>.json from two rocprofv3 --pmc "
                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
+    p.add_argument("--stats-summary", metavar="KERNEL_STATS_CSV",
+                   help="write profiles/kernel_stats_<config>.json from a rocprofv3 --stats "
+                        "run_kernel_stats.csv of this config and exit")
     return p.parse_args()
 
 
@@ -146,6 +153,57 @@ def pmc_summary(args, out_dir=None):
         json.dump(out, fh, indent=1)
     print(json.dumps(out), flush=True)
     return out
+
+
+# the HIP kernel (a substring of its name in a kernel trace) of each timed launch
+HIP_KERNEL = {"decode_front": "moe_decode_front", "routed_down_combine": "moe_routed_down_combine",
+              "routed_gateup": "moe_routed_gateup", "shared_down_routed_gateup": "moe_routed_gateup",
+              "router_shared_gateup": "moe_router_shared_gateup",
+              "router_shared_gateup_topk": "moe_router_shared_gateup",
+              "select_shared_down": "moe_select_shared_down", "select_plan": "moe_select_shared_down",
+              "router_quant": "moe_router_mx_quant", "mx_gateup": "moe_mx_gateup",
+              "mx_down": "moe_mx_down", "combine": "moe_combine(",
+              "int8_row_dequant": "int8_row_dequant_kernel"}
+
+
+def config_kernels(config):
+    cfgd = CONFIGS[config]
+    if cfgd.get("kind") == "int8_dequant":
+        return ["int8_row_dequant"]
+    T = cfgd["tokens"]
+    return (KERNELS_MFMA if cfgd.get("path") == "mfma" else KERNELS_GEMV_ONE if T == 1
+            else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
+
+
+def stats_summary(args):
+    """Average kernel durations of a rocprofv3 --kernel-trace --stats run of
+    this config, per timed launch, with the hash of the kernel sources."""
+    import csv
+    rows = list(csv.DictReader(open(args.stats_summary)))
+    out = {"config": args.config, "source_hash": source_hash(), "kernels": {}}
+    for name in config_kernels(args.config):
+        hit = [r for r in rows if HIP_KERNEL[name] in r["Name"]]
+        assert len(hit) == 1, (name, [r["Name"] for r in hit])
+        r = hit[0]
+        out["kernels"][name] = {"calls": int(r["Calls"]),
+                                "avg_us": round(float(r["AverageNs"]) / 1e3, 2),
+                                "min_us": round(float(r["MinNs"]) / 1e3, 2),
+                                "max_us": round(float(r["MaxNs"]) / 1e3, 2)}
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{args.config}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+def rocprof_us(name, config):
+    """A launch's average duration in the committed rocprofv3 summary of this
+    config, or None once the kernel sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"kernel_stats_{config}.json")
+    if os.path.exists(path):
+        d = json.load(open(path))
+        if d.get("source_hash") == source_hash() and name in d["kernels"]:
+            return d["kernels"][name]["avg_us"]
+    return None
 
 
 def pmc_traffic(name, config):
@@ -264,6 +322,57 @@ def cpu_baseline(cfg_name, n_tokens):
                       f"{dt:.1f} s; BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
 
 
+def mfma_rate_bench(args, cfgd):
+    """Matrix-core rate of the block-scaled MFMA per operand-format pair, at 2
+    and 4 waves per SIMD, timed by the launch-stamped events (interleaved
+    order, median of `steps` launches per case)."""
+    import ctypes
+    import torch
+    from mxfp4_routed_expert_x896_amd import binding as b
+    steps = args.steps if args.steps is not None else cfgd["steps"]
+    warmup = args.warmup if args.warmup is not None else cfgd["warmup"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4000
+    pairs = [("fp4xfp4", 4, 4), ("fp4xfp8", 4, 0), ("fp8xfp8", 0, 0)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    arr = (ctypes.c_void_p * 2)(*[e.cuda_event for e in evs])
+    res = {}
+    for wps in (2, 4):
+        blocks = cu * wps  # 4 waves per workgroup, one per SIMD
+        out = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+        flops = blocks * 4 * iters * 8 * 2 * 16 * 16 * 128
+        times = {n: [] for n, _, _ in pairs}
+        for _ in range(warmup):
+            for n, af, bf in pairs:
+                b.mfma_rate(af, bf, iters, blocks, out)
+        torch.cuda.synchronize()
+        b.profile_events(arr, 2)
+        for i in range(steps):  # ABBA: alternate the order of the cases
+            for n, af, bf in (pairs if i % 2 == 0 else pairs[::-1]):
+                b.mfma_rate(af, bf, iters, blocks, out)
+                torch.cuda.synchronize()
+                times[n].append(evs[0].elapsed_time(evs[1]) * 1e-3)
+        b.profile_events(None, 0)
+        assert torch.isfinite(out).all()
+        for n in times:
+            res[f"{n}_tflops_{wps}w"] = round(flops / float(np.median(times[n])) / 1e12, 1)
+    ratio = res["fp4xfp4_tflops_4w"] / res["fp4xfp8_tflops_4w"]
+    out = {
+        "metric": "block-scaled MFMA issue rate (diagnostic)",
+        "value": res["fp4xfp4_tflops_4w"], "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "higher_is_better": True, "vs_baseline": None, "dtype": "fp4*fp4->f32",
+        "data": "register operands", "config": {"workload": cfgd["desc"], "iters": iters},
+        "rates_tflops": res, "fp4xfp4_over_fp4xfp8": round(ratio, 3),
+        "peaks_tflops": {"fp4": FP4_MFMA_PEAK_TFLOPS, "fp8": FP8_MFMA_PEAK_TFLOPS},
+        "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def int8_dequant_bench(args, cfgd):
     """One step = one row-scaled int8 -> fp32 expansion of the whole matrix.
     Bytes per element: 1 read + 4 written (+ 4 per row for the scale)."""
@@ -364,8 +473,14 @@ def main():
     if args.pmc_summary:
         pmc_summary(args)
         return
+    if args.stats_summary:
+        stats_summary(args)
+        return
     if cfgd.get("kind") == "int8_dequant":
         int8_dequant_bench(args, cfgd)
+        return
+    if cfgd.get("kind") == "mfma_rate":
+        mfma_rate_bench(args, cfgd)
         return
 
     import torch
@@ -380,8 +495,7 @@ def main():
         args.warmup = cfgd.get("warmup", 20)
     mfma = cfgd.get("path") == "mfma"
     path = b.PATH_MFMA if mfma else b.PATH_GEMV
-    KERNELS = (KERNELS_MFMA if mfma else KERNELS_GEMV_ONE if T == 1
-               else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
+    KERNELS = config_kernels(args.config)
     replicas = args.replicas or cfgd["replicas"]
     c = synth.K3
     H, I, E, k, S = c["hidden"], c["inter"], c["n_experts"], c["top_k"], c["n_shared"]
@@ -564,8 +678,13 @@ def main():
         "hbm_copy_gbs": copy_gbs,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": round(dom_bytes)},
+                     "traffic": traffic, "algorithmic_bytes": round(dom_bytes),
+                     "us_events": round(kern_us[dom], 2)},
     }
+    rp = rocprof_us(dom, args.config)
+    if rp is not None:  # the same launch in the committed rocprofv3 summary (its own timing)
+        out["roofline"]["us_rocprof"] = rp
+        out["roofline"]["frac_rocprof"] = round(dom_bytes / (rp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
     if mfma_info is not None:
         out["mfma"] = mfma_info
     if pool is not None:

@@ -406,6 +406,21 @@ int moe_mxfp8_quantize(const uint16_t* x, int64_t n_rows, int32_t k, uint8_t* co
 int moe_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
                          float* out, hipStream_t stream);
 
+/*
+ * Measurement export: the issue rate of the block-scaled 16x16x128 MFMA for
+ * an operand-format pair, the fact the choice between MXFP8 and MXFP4
+ * activations for the prefill matrix cores turns on (Deltafin explainer,
+ * section 2.1: MXFP4 weights with MXFP8 activations).  Formats: 4 = FP4
+ * E2M1, 0 = FP8 E4M3; supported pairs (a, b) = (4, 4), (4, 0), (0, 0), else
+ * MOE_EUNSUPPORTED.  Launches n_blocks workgroups of 4 waves; each wave
+ * issues iters x 8 MFMAs (2 x 16 x 16 x 128 FLOP each) on register
+ * operands with eight independent accumulators, and writes one checksum
+ * float to out[n_blocks * 4] (device, 4-byte aligned).  Time the launch with
+ * moe_profile_events.
+ */
+int moe_mfma_rate(int32_t a_fmt, int32_t b_fmt, int64_t iters, int32_t n_blocks, float* out,
+                  hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

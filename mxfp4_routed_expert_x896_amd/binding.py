@@ -93,6 +93,7 @@ _SIGNATURES = {
     "moe_pool_destroy": (ctypes.c_int, [_P]),
     "moe_workspace_status": (ctypes.c_int, [_P, _U64, _P]),
     "moe_layer_scratch": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P]),
+    "moe_mfma_rate": (ctypes.c_int, [_I32, _I32, _I64, _I32, _P, _P]),
     "moe_set_wait_limit": (ctypes.c_int, [_I64]),
     "moe_workspace_region": (ctypes.c_int, [_DESC, _I64, _I32, ctypes.POINTER(_U64),
                                             ctypes.POINTER(_U64)]),
@@ -352,3 +353,9 @@ def workspace_region(layer, n_tokens, region, ws):
     _check(_lib().moe_workspace_region(layer.desc, n_tokens, region, ctypes.byref(off),
                                        ctypes.byref(n)), "moe_workspace_region")
     return ws[off.value:off.value + n.value]
+
+
+def mfma_rate(a_fmt, b_fmt, iters, n_blocks, out, stream=None):
+    """Block-scaled MFMA issue-rate launch (formats 4 = FP4, 0 = FP8)."""
+    _check(_lib().moe_mfma_rate(a_fmt, b_fmt, iters, n_blocks, _ptr(out), _stream(stream)),
+           "moe_mfma_rate")

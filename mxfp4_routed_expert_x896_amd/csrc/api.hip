@@ -748,3 +748,16 @@ MOE_API int moe_workspace_region(const moe_layer_desc* layer, int64_t n_tokens, 
   }
   return MOE_OK;
 }
+
+MOE_API int moe_mfma_rate(int32_t a_fmt, int32_t b_fmt, int64_t iters, int32_t n_blocks,
+                          float* out, hipStream_t stream) {
+  if (out == nullptr || iters <= 0 || n_blocks <= 0) return MOE_EINVAL;
+  if (!((a_fmt == 4 && (b_fmt == 4 || b_fmt == 0)) || (a_fmt == 0 && b_fmt == 0)))
+    return MOE_EUNSUPPORTED;
+  if (iters > (int64_t(1) << 40) || n_blocks > (1 << 20)) return MOE_ESHAPE;
+  if (reinterpret_cast<uintptr_t>(out) & 3u) return MOE_EALIGN;
+  int st = check_device();
+  if (st) return st;
+  prof_begin(stream);
+  return launched(moe::launch_mfma_rate(a_fmt, b_fmt, iters, n_blocks, out, stream), stream);
+}

@@ -167,6 +167,10 @@ hipError_t launch_dequant_export(const uint8_t* record, int H, int I, int matrix
 int64_t int8_dequant_blocks(int64_t rows, int64_t cols);
 hipError_t launch_int8_row_dequant(const int8_t* q, const float* scale, int64_t rows, int64_t cols,
                                    float* out, hipStream_t stream);
+// Block-scaled 16x16x128 MFMA issue rate (rate.hip): formats 4 = FP4 E2M1,
+// 0 = FP8 E4M3; supported pairs (4, 4), (4, 0), (0, 0).
+hipError_t launch_mfma_rate(int a_fmt, int b_fmt, int64_t iters, int blocks, float* out,
+                            hipStream_t stream);
 hipError_t launch_mxfp8_quantize(const uint16_t* x, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream);
 

@@ -227,3 +227,15 @@ def test_status_and_region_calls(lib):
     assert L.moe_workspace_region(ctypes.byref(d), 4, 5, ctypes.byref(off), ctypes.byref(n)) == -1
     assert L.moe_workspace_region(ctypes.byref(d), 0, 0, ctypes.byref(off), ctypes.byref(n)) == -1
     assert L.moe_workspace_region(ctypes.byref(d), 4, 0, None, ctypes.byref(n)) == -1
+
+
+def test_mfma_rate_rejects_bad_arguments(lib):
+    L = lib.lib()
+    P = ctypes.c_void_p
+    out = P(0x100000)
+    assert L.moe_mfma_rate(4, 4, 10, 4, None, None) == -1
+    assert L.moe_mfma_rate(4, 4, 0, 4, out, None) == -1
+    assert L.moe_mfma_rate(4, 4, 10, 0, out, None) == -1
+    assert L.moe_mfma_rate(0, 4, 10, 4, out, None) == -7   # FP8 x FP4: not offered
+    assert L.moe_mfma_rate(2, 2, 10, 4, out, None) == -7
+    assert L.moe_mfma_rate(4, 0, 10, 4, P(0x100002), None) == -2
