@@ -221,3 +221,73 @@ def mxfp8_roundtrip(v):
     """Value after MXFP8 quantisation (float64)."""
     c, s = mxfp8_quantize(v)
     return mxfp8_dequant(c, s)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 activations (the prefill path's FP4 x FP4 variant)
+# ----------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+E2M1_EMAX = 2  # exponent of the largest normal, 6 = 1.5 * 2**2
+
+
+def e2m1_encode_rne_sat(v):
+    """float64 -> E2M1 codes (0..15), round to nearest, ties to even, saturating to +-6.
+
+    Magnitude spacing: 0.5 on [0, 2) (the subnormal 0.5 and the binade
+    [1, 2)), 1 on [2, 4), 2 on [4, 6]; "even" is the code whose mantissa bit
+    (bit 0) is clear.  A magnitude above 6 becomes 6 (the MX conversion
+    saturates).  The sign of zero is kept (code 8 is -0).  NaN inputs are
+    rejected.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.isnan(v)):
+        raise ValueError("NaN input to E2M1 quantiser")
+    a = np.minimum(np.abs(v), E2M1_MAX)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    q = np.rint(a / step) * step  # numpy's rint rounds half to even
+    # a tie at a binade edge rounds onto the edge from below (1.75 -> 2, 3.5 -> 4)
+    # with the next binade's code; the even choice inside a binade is rint's
+    q = np.minimum(q, E2M1_MAX)
+    # codes 0..7 are the magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 in increasing order
+    code = np.searchsorted(e2m1_decode(np.arange(8)), q).astype(np.int64)
+    code = np.where(np.signbit(v), code | 8, code)
+    return code.astype(np.uint8)
+
+
+def mxfp4_quantize(v):
+    """Quantise rows of v (float64 [..., K], K % 32 == 0) to MXFP4: per block
+    of 32 consecutive elements along the last axis, a = max |v_i|,
+    E = clamp(floor(log2 a) - 2, -127, 127) (E = -127 when a == 0) and
+    q_i = RNE_E2M1(v_i / 2**E) saturated to +-6 -- the MXFP8 rule with E2M1's
+    largest normal exponent (2) in place of E4M3's (8).
+    Returns (codes uint8 [..., K], one E2M1 code per element; scale bytes
+    uint8 [..., K/32] = E + 127).  The value is e2m1_decode(code) * 2**E.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    k = v.shape[-1]
+    if k % MX_BLOCK:
+        raise ValueError("MXFP4 blocks need K % 32 == 0")
+    blocks = v.reshape(v.shape[:-1] + (k // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blocks), axis=-1)
+    with np.errstate(divide="ignore"):
+        _, ex = np.frexp(amax)
+    e = np.where(amax == 0, -127, np.clip(ex - 1 - E2M1_EMAX, -127, 127))
+    scaled = np.ldexp(blocks, -e[..., None])
+    codes = e2m1_encode_rne_sat(scaled).reshape(v.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp4_act_dequant(codes, scales):
+    """Inverse of mxfp4_quantize: e2m1 value * 2**(scale - 127)."""
+    codes = np.asarray(codes)
+    k = codes.shape[-1]
+    vals = e2m1_decode(codes)
+    sc = e8m0_decode(scales)
+    return vals * np.repeat(sc, MX_BLOCK, axis=-1).reshape(vals.shape[:-1] + (k,))
+
+
+def mxfp4_roundtrip(v):
+    """Value after MXFP4 quantisation (float64)."""
+    c, s = mxfp4_quantize(v)
+    return mxfp4_act_dequant(c, s)

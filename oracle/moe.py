@@ -22,12 +22,14 @@ router's formula or the expert's activation; the readings used here:
   * prefill variant: the routed experts see x, and later h, rounded to MXFP8
     (E4M3 codes plus an E8M0 exponent per 32 elements along the contraction),
     following the MXFP8-activation training noted in the explainer, section
-    2.1.  The router and the shared experts keep the bf16 x.
+    2.1.  The router and the shared experts keep the bf16 x.  A second
+    prefill variant rounds them to MXFP4 instead (E2M1 codes, the weights'
+    own format), for the FP4 x FP4 matrix-core rate.
 """
 
 import numpy as np
 
-from .formats import bf16_decode, bf16_encode_rne, mxfp8_roundtrip
+from .formats import bf16_decode, bf16_encode_rne, mxfp4_roundtrip, mxfp8_roundtrip
 from .record import dequant_expert
 
 
@@ -123,18 +125,21 @@ def route(x_bits, layer):
     return ids, combine_weights(s, ids, layer.routed_scale), key
 
 
-def expert_ffn(xv, wg, wu, wd, act_mxfp8=False):
+def expert_ffn(xv, wg, wu, wd, act_mxfp8=False, act_mxfp4=False):
     """SwiGLU expert on float64 rows xv [T, H]: Wd (SiLU(Wg x) * (Wu x)).
 
-    act_mxfp8: x and h are replaced by their MXFP8 values along the
-    contraction dimension before the respective products.
+    act_mxfp8 / act_mxfp4: x and h are replaced by their MXFP8 (or MXFP4)
+    values along the contraction dimension before the respective products.
     """
-    xin = mxfp8_roundtrip(xv) if act_mxfp8 else xv
+    if act_mxfp8 and act_mxfp4:
+        raise ValueError("one activation format")
+    rnd = mxfp8_roundtrip if act_mxfp8 else mxfp4_roundtrip if act_mxfp4 else None
+    xin = rnd(xv) if rnd else xv
     g = xin @ wg.T
     u = xin @ wu.T
     h = silu(g) * u
-    if act_mxfp8:
-        h = mxfp8_roundtrip(h)
+    if rnd:
+        h = rnd(h)
     return h @ wd.T
 
 
@@ -146,7 +151,7 @@ def shared_ffn(xv, gate_bits, up_bits, down_bits):
     return (silu(xv @ wg.T) * (xv @ wu.T)) @ wd.T
 
 
-def routed_sum(x_bits, layer, topk_ids, topk_w, act_mxfp8=False, tokens=None):
+def routed_sum(x_bits, layer, topk_ids, topk_w, act_mxfp8=False, tokens=None, act_mxfp4=False):
     """sum_j w[t, j] * expert_{ids[t, j]}(x_t) for the given routing.
 
     Each expert touched is dequantised once and applied to all its tokens.
@@ -166,7 +171,7 @@ def routed_sum(x_bits, layer, topk_ids, topk_w, act_mxfp8=False, tokens=None):
     for e in np.unique(ids):
         t_idx, j_idx = np.nonzero(ids == e)
         wg, wu, wd = dequant_expert(layer.expert_record(int(e)), layer.hidden, layer.inter)
-        ye = expert_ffn(xv[t_idx], wg, wu, wd, act_mxfp8)
+        ye = expert_ffn(xv[t_idx], wg, wu, wd, act_mxfp8, act_mxfp4)
         for r, (t, j) in enumerate(zip(t_idx, j_idx)):
             contrib[(int(t), int(j))] = ye[r]
     for t in range(len(rows)):
@@ -187,12 +192,12 @@ def shared_sum(x_bits, layer, tokens=None):
 
 
 def moe_forward(x_bits, layer, topk_ids, topk_w, act_mxfp8=False,
-                residual_bits=None, tokens=None):
+                residual_bits=None, tokens=None, act_mxfp4=False):
     """y = [residual +] sum_j w_j expert_{id_j}(x) + sum_s shared_s(x).
 
     Unrounded float64; the product rounds once, to bf16, at the output.
     """
-    y = routed_sum(x_bits, layer, topk_ids, topk_w, act_mxfp8, tokens)
+    y = routed_sum(x_bits, layer, topk_ids, topk_w, act_mxfp8, tokens, act_mxfp4)
     y = y + shared_sum(x_bits, layer, tokens)
     if residual_bits is not None:
         r = np.asarray(residual_bits, dtype=np.uint16)
@@ -201,10 +206,10 @@ def moe_forward(x_bits, layer, topk_ids, topk_w, act_mxfp8=False,
     return y
 
 
-def moe_layer(x_bits, layer, act_mxfp8=False, residual_bits=None):
+def moe_layer(x_bits, layer, act_mxfp8=False, residual_bits=None, act_mxfp4=False):
     """Route then combine: (y float64 [T,H], ids, weights)."""
     ids, w, _ = route(x_bits, layer)
-    y = moe_forward(x_bits, layer, ids, w, act_mxfp8, residual_bits)
+    y = moe_forward(x_bits, layer, ids, w, act_mxfp8, residual_bits, act_mxfp4=act_mxfp4)
     return y, ids, w
 
 

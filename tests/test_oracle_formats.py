@@ -256,3 +256,76 @@ def test_mxfp8_brute_force_over_all_bf16():
     exp = _brute_nearest_e4m3(np.ldexp(np.abs(blocks), 5)).astype(np.uint8)
     exp = np.where(np.signbit(blocks), exp | 0x80, exp)
     np.testing.assert_array_equal(c, exp)
+
+
+# ------------------------------------------------- MXFP4 activations ----
+
+def _brute_nearest_e2m1(a):
+    """Nearest E2M1 magnitude code (0..7) to each non-negative a, ties to the
+    code with its mantissa bit clear, above 6 saturating -- by enumerating
+    the eight magnitudes from the closed form."""
+    mags = F.e2m1_decode(np.arange(8))
+    a = np.minimum(np.asarray(a, dtype=np.float64), 6.0)
+    d = np.abs(a[:, None] - mags[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand & (np.arange(8)[None, :] % 2 == 0)
+    return np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+
+
+def test_e2m1_encode_brute_force_dense_grid():
+    """Every multiple of 1/64 in [0, 8] (all midpoints and ties included) and
+    every finite bf16 value up to 8, both signs, against the brute force."""
+    grid = np.arange(0, 8 * 64 + 1) / 64.0
+    bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    bf = F.bf16_decode(bits)
+    for v in (grid, bf[bf <= 8.0]):
+        got = F.e2m1_encode_rne_sat(v)
+        exp = _brute_nearest_e2m1(v).astype(np.uint8)
+        np.testing.assert_array_equal(got, exp)
+        np.testing.assert_array_equal(F.e2m1_encode_rne_sat(-v), exp | 8)
+
+
+def test_e2m1_ties_and_saturation_by_hand():
+    v = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 1e30, -0.25])
+    assert F.e2m1_decode(F.e2m1_encode_rne_sat(v)).tolist() == \
+        [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0, 6.0, -0.0]
+    assert F.e2m1_encode_rne_sat(np.array([-0.25]))[0] == 8  # -0 keeps its sign
+    c = np.arange(16, dtype=np.uint8)
+    np.testing.assert_array_equal(F.e2m1_encode_rne_sat(F.e2m1_decode(c)), c)
+
+
+def test_mxfp4_scale_rule_and_saturation():
+    blk = np.zeros((1, 32))
+    blk[0, 0] = 4.0  # amax = 2**2 -> E = 0
+    blk[0, 1] = 1.0 / 3
+    c, s = F.mxfp4_quantize(blk)
+    assert s[0, 0] == 127 and F.e2m1_decode(c[0, 0]) == 4.0 and F.e2m1_decode(c[0, 1]) == 0.5
+    blk[0, 0] = 7.9  # amax in [4, 8): E = 0, 7.9 saturates to 6
+    c, s = F.mxfp4_quantize(blk)
+    assert s[0, 0] == 127 and F.e2m1_decode(c[0, 0]) == 6.0
+    blk[0, 0] = 1.0  # amax 1 -> E = -2: scaled values x4
+    c, s = F.mxfp4_quantize(blk)
+    assert s[0, 0] == 125 and F.e2m1_decode(c[0, 0]) == 4.0
+    c, s = F.mxfp4_quantize(np.zeros((2, 64)))
+    assert np.all(s == 0) and np.all(c == 0)
+    c, s = F.mxfp4_quantize(np.full((1, 32), 2.0 ** 140))
+    assert s[0, 0] == 127 + 127
+
+
+def test_mxfp4_brute_force_blocks():
+    """Blocks of grid values under a block maximum of 2**3: E = 1, each
+    element's code the brute-force nearest of v / 2."""
+    v = np.arange(0, 8 * 64) / 64.0
+    pad = (-len(v)) % 31
+    v = np.concatenate([v, np.zeros(pad)]).reshape(-1, 31)
+    blocks = np.concatenate([np.full((v.shape[0], 1), 8.0), v], axis=1)
+    sign = np.where(np.arange(blocks.size).reshape(blocks.shape) % 3 == 0, -1.0, 1.0)
+    blocks = blocks * sign
+    c, s = F.mxfp4_quantize(blocks)
+    assert np.all(s == 128)
+    exp = _brute_nearest_e2m1((np.abs(blocks) / 2).ravel()).reshape(blocks.shape).astype(np.uint8)
+    exp = np.where(np.signbit(blocks), exp | 8, exp)
+    np.testing.assert_array_equal(c, exp)
+    # the dequantised value is the code's E2M1 value times 2**E
+    np.testing.assert_array_equal(F.mxfp4_act_dequant(c, s), F.e2m1_decode(c) * 2.0)

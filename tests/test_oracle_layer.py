@@ -184,3 +184,37 @@ def test_rmsnorm_closed_form_and_torch():
     ref = torch.nn.functional.rms_norm(torch.from_numpy(F.bf16_decode(xb)), (7168,),
                                        weight=torch.from_numpy(F.bf16_decode(gb)), eps=1e-6)
     np.testing.assert_array_equal(M.rmsnorm(xb, gb, 1e-6), F.bf16_encode_rne(ref.numpy()))
+
+
+def test_mxfp4_activation_path_on_grid_input():
+    """x already on the MXFP4 grid is unchanged; h is rounded to MXFP4 (the
+    same closed form as the MXFP8 pin above, with the E2M1 grid)."""
+    g = np.random.default_rng(2)
+    xv = F.e2m1_decode(g.integers(0, 16, size=(2, H))).astype(np.float64)
+    xv[:, 0] = 6.0   # amax 6 in both blocks: E = 0, values on the grid stay
+    xv[:, 32] = -6.0
+    x_bits = F.bf16_encode_rne(xv)
+    np.testing.assert_array_equal(F.mxfp4_roundtrip(xv), xv)
+    rec = _expert_a()
+    wg, wu, wd = R.dequant_expert(rec, H, I)
+    y = M.expert_ffn(F.bf16_decode(x_bits), wg, wu, wd, act_mxfp4=True)
+    for t in range(2):
+        h = np.array([_silu(xv[t, n]) * 2.0 * xv[t, n + 1] for n in range(I)])
+        hq = F.mxfp4_roundtrip(h[None, :])[0]
+        np.testing.assert_allclose(y[t], [0.5 * hq[m % I] for m in range(H)], rtol=1e-15)
+        assert not np.allclose(hq, h, rtol=1e-3)  # the rounding did something
+    with pytest.raises(ValueError):
+        M.expert_ffn(xv, wg, wu, wd, act_mxfp8=True, act_mxfp4=True)
+
+
+def test_mxfp4_mode_all_experts_equal_is_dense_ffn_of_rounded_activations():
+    """Every expert identical: the routed sum is one expert's FFN, whatever the
+    routing, computed on MXFP4-rounded x and h."""
+    rec = synth.expert_record(5, 0, 0, H, I)
+    layer = M.Layer(H, I, 8, 3, synth.router_weight(5, 0, 8, H), expert_record=lambda e: rec)
+    x = synth.activations(1500, 5, H)
+    y, ids, w = M.moe_layer(x, layer, act_mxfp4=True)
+    wg, wu, wd = R.dequant_expert(rec, H, I)
+    xq = F.mxfp4_roundtrip(F.bf16_decode(x))
+    hq = F.mxfp4_roundtrip(M.silu(xq @ wg.T) * (xq @ wu.T))
+    np.testing.assert_allclose(y, hq @ wd.T, rtol=1e-12, atol=1e-12 * np.abs(y).max())
