@@ -1,8 +1,8 @@
 """Throughput of the K3-shape MXFP4 MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config b1|b2|b8|b64|stack12|prefill|prefill128|b1_stream|int8_dequant|
-                              mfma_rate]
+                    [--config b1|b2|b8|b64|stack12|prefill|prefill_fp4|prefill128|b1_stream|
+                              int8_dequant|mfma_rate]
 
 A step is one full pass of the layer (router GEMV + top-k, token->expert
 plan, routed MXFP4 gate/up and down GEMVs, shared bf16 experts, weighted
@@ -77,6 +77,14 @@ CONFIGS = {
     "mfma_rate": dict(kind="mfma_rate", steps=10, warmup=3,
                       desc="issue rate of the block-scaled 16x16x128 MFMA: FP4 x FP4 vs FP4 x FP8 "
                            "(vs FP8 x FP8), register operands, 8 independent accumulators per wave"),
+    "prefill128_fp4": dict(tokens=4096, layers=1, replicas=1, bias=True, favor=128,
+                           path="mfma_fp4", steps=20, warmup=3,
+                           desc="compute-bound diagnostic of the FP4 x FP4 prefill kernels: 4096 "
+                                "tokens routed to 128 experts (512 tokens each), MXFP4 activations"),
+    "prefill_fp4": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma_fp4", steps=20,
+                        warmup=3,
+                        desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
+                             "MXFP4 activations on block-scaled FP4 x FP4 MFMA"),
     "prefill": dict(tokens=4096, layers=1, replicas=1, bias=True, path="mfma", steps=20, warmup=3,
                     desc="K3 MoE layer prefill, 4096 tokens, per-expert logit bias N(0,0.5), "
                          "MXFP8 activations on block-scaled MFMA"),
@@ -171,8 +179,8 @@ def config_kernels(config):
     if cfgd.get("kind") == "int8_dequant":
         return ["int8_row_dequant"]
     T = cfgd["tokens"]
-    return (KERNELS_MFMA if cfgd.get("path") == "mfma" else KERNELS_GEMV_ONE if T == 1
-            else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
+    return (KERNELS_MFMA if cfgd.get("path") in ("mfma", "mfma_fp4") else KERNELS_GEMV_ONE
+            if T == 1 else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
 
 
 def stats_summary(args):
@@ -294,6 +302,7 @@ def cpu_baseline(cfg_name, n_tokens):
     H, I = c["hidden"], c["inter"]
     cfg = CONFIGS[cfg_name]
     mx = cfg.get("path") == "mfma"
+    mx4 = cfg.get("path") == "mfma_fp4"
     bias = synth.router_bias(0, 0, c["n_experts"]) if cfg.get("bias") else None
     if bias is not None and cfg.get("favor"):
         bias = bias.copy()
@@ -307,7 +316,7 @@ def cpu_baseline(cfg_name, n_tokens):
     done = 0
     for i in range(n_tokens):
         # one token of the workload's input through one layer (route + experts)
-        M.moe_layer(synth.activations(1000 + i, 1, H), layer, act_mxfp8=mx)
+        M.moe_layer(synth.activations(1000 + i, 1, H), layer, act_mxfp8=mx, act_mxfp4=mx4)
         done += 1
         if time.perf_counter() - t0 > 30:
             break
@@ -317,6 +326,7 @@ def cpu_baseline(cfg_name, n_tokens):
             "kind": "oracle",
             "sample": f"{done} single-token layer call(s) of {cfg_name} through the float64 numpy "
                       f"oracle ({'MXFP8 activations, logit bias, ' if mx else ''}"
+                      f"{'MXFP4 activations, logit bias, ' if mx4 else ''}"
                       f"router + 16 experts dequantised and applied + 2 shared"
                       f"{', scaled by 1/%d layers' % n_layers if n_layers > 1 else ''}), "
                       f"{dt:.1f} s; BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
@@ -493,8 +503,9 @@ def main():
         args.steps = cfgd.get("steps", 200)
     if args.warmup is None:
         args.warmup = cfgd.get("warmup", 20)
-    mfma = cfgd.get("path") == "mfma"
-    path = b.PATH_MFMA if mfma else b.PATH_GEMV
+    mfma = cfgd.get("path") in ("mfma", "mfma_fp4")
+    fp4_act = cfgd.get("path") == "mfma_fp4"
+    path = b.PATH_MFMA_FP4 if fp4_act else b.PATH_MFMA if mfma else b.PATH_GEMV
     KERNELS = config_kernels(args.config)
     replicas = args.replicas or cfgd["replicas"]
     c = synth.K3
@@ -614,10 +625,14 @@ def main():
         f8, f16 = mfma_flops(dom, T, k, S)
         t_dom = kern_us[dom] * 1e-6
         # the launch's bounding roof: its bytes at the HBM peak or its MFMA work
-        # at the dense peaks (routed at the MXFP8 rate, shared at bf16), whichever is longer
+        # at the dense peaks (routed at the MXFP8 rate -- a FP4 x FP8 MFMA runs at
+        # the FP8 rate -- or the FP4 rate on the FP4 x FP4 path, shared at bf16),
+        # whichever is longer
+        routed_peak = FP4_MFMA_PEAK_TFLOPS if fp4_act else FP8_MFMA_PEAK_TFLOPS
         t_bound = max(dom_bytes / (HBM_PEAK_GBS * 1e9),
-                      f8 / (FP8_MFMA_PEAK_TFLOPS * 1e12) + f16 / (BF16_MFMA_PEAK_TFLOPS * 1e12))
-        mfma_info = {"kernel": dom, "fp4xfp8_tflops": round(f8 / t_dom / 1e12, 1),
+                      f8 / (routed_peak * 1e12) + f16 / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        name = "fp4xfp4_tflops" if fp4_act else "fp4xfp8_tflops"
+        mfma_info = {"kernel": dom, name: round(f8 / t_dom / 1e12, 1),
                      "frac_of_fp8_peak": round(f8 / t_dom / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
                      "frac_of_fp4_peak": round(f8 / t_dom / 1e12 / FP4_MFMA_PEAK_TFLOPS, 4),
                      "bf16_tflops_same_launch": round(f16 / t_dom / 1e12, 1),
@@ -660,13 +675,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4*mxfp8->f32" if mfma else "mxfp4*bf16->f32",
+        "dtype": ("mxfp4*mxfp4->f32" if fp4_act else "mxfp4*mxfp8->f32" if mfma
+                  else "mxfp4*bf16->f32"),
         "data": "synthetic (seeded; codes uniform, E8M0 118..126, N(0,0.02) bf16 router/shared, N(0,1) tokens"
                 + ((", logit bias N(0,0.5)" + (f", +20 on experts 0..{cfgd['favor'] - 1}"
                                                   if cfgd.get("favor") else "") + ")")
                    if cfgd.get("bias") else ")"),
         "config": {"workload": cfgd["desc"], "tokens_per_step": T, "layers": n_layers,
-                   "resident_copies": len(layers), "path": "mfma" if mfma else "gemv"},
+                   "resident_copies": len(layers), "path": cfgd.get("path", "gemv")},
         "expert_weight_gbs": round(float(exp_gbs), 1),
         "expert_weight_hbm_frac": round(float(exp_gbs) / HBM_PEAK_GBS, 4),
         "distinct_experts_mean": round(float(D.mean()), 2),

@@ -94,6 +94,7 @@ extern "C" {
 #define MOE_PATH_AUTO 0  /* GEMV path for small T, MXFP8 MFMA path for large T */
 #define MOE_PATH_GEMV 1  /* bf16 activations, dequant-fused GEMV (decode) */
 #define MOE_PATH_MFMA 2  /* MXFP8 activations, scaled FP4 MFMA (prefill) */
+#define MOE_PATH_MFMA_FP4 3  /* MXFP4 activations, scaled FP4 x FP4 MFMA (prefill; opt-in) */
 
 /*
  * One MoE layer.  Host struct; the pointers in it are device pointers.
@@ -211,7 +212,12 @@ int moe_route(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
  *         exponent per 32 along the contraction) for the routed experts, the
  *         reading of the MXFP8 activations in the Deltafin explainer,
  *         section 2.1;
- *         MOE_PATH_AUTO picks MFMA when n_tokens >= moe_mfma_min_tokens().
+ *         MOE_PATH_MFMA_FP4 rounds them to MXFP4 instead (E2M1 with one E8M0
+ *         exponent per 32 along the contraction, the weights' own format:
+ *         E = clamp(floor(log2 amax) - 2), round to nearest even, saturating
+ *         at 6), for the FP4 x FP4 matrix-core rate (about twice FP4 x FP8);
+ *         MOE_PATH_AUTO picks MFMA when n_tokens >= moe_mfma_min_tokens()
+ *         (never the FP4 variant).
  * Routing ids out of range are clamped on the device (never read out of
  * bounds); they are the caller's error.
  */
@@ -260,10 +266,13 @@ int moe_set_wait_limit(int64_t polls);
  *                    (pairs grouped by expert, experts ascending); written
  *                    by every call except single-token GEMV calls
  *   MOE_WS_X_CODES:  uint8 E4M3 [T][Kq] MXFP8 codes of x (MFMA path; zero
- *                    codes past H)
+ *                    codes past H); on the MXFP4 path the first T Kq / 2
+ *                    bytes hold [T][Kq / 2] E2M1 codes, two per byte, even
+ *                    element in the low nibble
  *   MOE_WS_X_SCALES: uint8 E8M0 [T][Kq/32], MFMA order (127 past H)
  *   MOE_WS_H_CODES:  uint8 E4M3 [T k][Iq]: MXFP8 codes of SiLU(g) u of the
- *                    pair at each plan position (MFMA path)
+ *                    pair at each plan position (MFMA path); MXFP4 path:
+ *                    [T k][Iq / 2] E2M1 codes in the first T k Iq / 2 bytes
  *   MOE_WS_H_SCALES: uint8 E8M0 [T k][Iq/32], MFMA order
  * Contents are those of the last call on the workspace once its stream has
  * reached that point.

@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE
                 -4: "MOE_EWORKSPACE", -5: "MOE_EDEVICE", -6: "MOE_ELAUNCH",
                 -7: "MOE_EUNSUPPORTED", -8: "MOE_ETIMEOUT"}
 
-PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_MFMA_FP4 = 0, 1, 2, 3
 ROUTER_BIAS_LOGITS, ROUTER_BIAS_SELECT = 0, 1
 GATE, UP, DOWN = 0, 1, 2
 WS_PAIRS, WS_X_CODES, WS_X_SCALES, WS_H_CODES, WS_H_SCALES = range(5)

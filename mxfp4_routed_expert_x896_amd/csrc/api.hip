@@ -400,8 +400,9 @@ int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hi
 // Prefill layer: x -> MXFP8 + router logits (MFMA); top-k + plan; experts.
 int do_layer_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T,
                   const uint16_t* residual, uint16_t* y, int32_t* ids, float* w, void* ws,
-                  hipStream_t stream) {
+                  int afmt, hipStream_t stream) {
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.afmt = afmt;
   G.ids_out = ids;
   G.w_out = w;
   G.w = w;
@@ -422,9 +423,10 @@ int do_layer_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T,
 // Prefill (MFMA) path for a given routing: plan + x -> MXFP8, then the
 // experts.
 int do_forward_mfma(const moe_layer_desc* L, const uint16_t* x, int64_t T, const int32_t* ids,
-                    const float* w, const uint16_t* residual, uint16_t* y, void* ws,
+                    const float* w, const uint16_t* residual, uint16_t* y, void* ws, int afmt,
                     hipStream_t stream) {
   moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.afmt = afmt;
   G.ids_in = ids;
   G.w = w;
   G.residual = residual;
@@ -441,6 +443,10 @@ int resolve_path(int32_t path, int64_t T) {
   if (path == MOE_PATH_AUTO) return T >= moe_mfma_min_tokens() ? MOE_PATH_MFMA : MOE_PATH_GEMV;
   return path;
 }
+
+bool valid_path(int32_t path) { return path >= MOE_PATH_AUTO && path <= MOE_PATH_MFMA_FP4; }
+// MX activation format of an MFMA path (the MFMA's B-operand format code).
+int act_format(int path) { return path == MOE_PATH_MFMA_FP4 ? 4 : 0; }
 
 }  // namespace
 
@@ -565,12 +571,14 @@ MOE_API int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t 
   if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
     return MOE_EALIGN;
   if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (!valid_path(path)) return MOE_EINVAL;
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
   prof_begin(stream);
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
-    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+  const int p = resolve_path(path, n_tokens);
+  if (p != MOE_PATH_GEMV)
+    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace,
+                           act_format(p), stream);
   return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
 }
 
@@ -585,12 +593,14 @@ MOE_API int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_
   if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
     return MOE_EALIGN;
   if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (!valid_path(path)) return MOE_EINVAL;
   if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
   if ((st = check_device())) return st;
   prof_begin(stream);
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
-    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
+  const int p = resolve_path(path, n_tokens);
+  if (p != MOE_PATH_GEMV)
+    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace,
+                         act_format(p), stream);
   return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, workspace, stream);
 }
 
@@ -637,14 +647,16 @@ MOE_API int moe_layer_scratch(const moe_layer_desc* layer, const uint16_t* x, in
   if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
     return MOE_EALIGN;
   if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_MFMA) return MOE_EINVAL;
+  if (!valid_path(path)) return MOE_EINVAL;
   if (carve(layer, n_tokens).total > MOE_SCRATCH_BYTES) return MOE_EWORKSPACE;
   if ((st = check_device())) return st;
   void* ws = nullptr;
   if ((st = scratch_address(&ws))) return st;
   prof_begin(stream);
-  if (resolve_path(path, n_tokens) == MOE_PATH_MFMA)
-    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, ws, stream);
+  const int p = resolve_path(path, n_tokens);
+  if (p != MOE_PATH_GEMV)
+    return do_layer_mfma(layer, x, n_tokens, residual, y, topk_ids, topk_w, ws, act_format(p),
+                         stream);
   return do_layer_gemv(layer, x, n_tokens, residual, y, topk_ids, topk_w, ws, stream);
 }
 

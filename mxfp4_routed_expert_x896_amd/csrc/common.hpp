@@ -178,6 +178,31 @@ __device__ __forceinline__ int mxfp8_block_exp(float amax) {
   return max(-127, min(127, E));
 }
 
+// E2M1 code (0..15, sign in bit 3) of v, round to nearest even, saturating
+// at +-6.  The magnitude grid has step 0.5 below 2, 1 below 4 and 2 up to 6;
+// rintf (round half to even under the default mode) picks the even multiple
+// of the step, which is the code with its mantissa bit clear, and a tie at a
+// binade's top rounds up onto the next binade's even code (1.75 -> 2).
+__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fminf(fabsf(v), 6.0f);
+  float q;
+  if (a < 2.0f) q = rintf(a * 2.0f) * 0.5f;
+  else if (a < 4.0f) q = rintf(a);
+  else q = rintf(a * 0.5f) * 2.0f;
+  // magnitudes 0, 0.5, 1, 1.5 -> codes 0..3; 2, 3 -> 4, 5; 4 -> 6; 6 -> 7
+  const uint32_t code = q < 2.0f ? uint32_t(q * 2.0f) : q < 4.0f ? uint32_t(q) + 2u
+                                                        : q < 5.0f ? 6u : 7u;
+  return sign | code;
+}
+
+// MXFP4 block exponent (the MXFP8 rule with E2M1's largest normal exponent,
+// 2): clamp(floor(log2 amax) - 2, -127, 127), -127 for 0.
+__device__ __forceinline__ int mxfp4_block_exp(float amax) {
+  const int E = amax == 0.0f ? -127 : floor_log2_f32(amax) - 2;
+  return max(-127, min(127, E));
+}
+
 // Results that cross workgroups of one launch (and XCDs, whose L2s are
 // private) are stored and re-read with device-scope atomic accesses, which
 // the compiler emits as write-through stores and L2-bypassing loads, instead

@@ -104,12 +104,15 @@ struct GemvLayer {
   int front;
   unsigned long long* idsflag;
   unsigned long long* sgflags;
-  // prefill (MFMA) path: MXFP8 activations, rows padded to Kq / Iq columns
-  // (multiples of 512, zero codes past H / I); scale rows in MFMA order
+  // prefill (MFMA) path: MX activations, rows padded to Kq / Iq columns
+  // (multiples of 512, zero codes past H / I); scale rows in MFMA order.
+  // afmt 0: MXFP8 (E4M3, one byte per element); afmt 4: MXFP4 (E2M1, two per
+  // byte, even element in the low nibble: rows of Kq / 2 and Iq / 2 bytes)
   int Kq, Iq;
-  uint8_t* xq;              // E4M3 [T][Kq]
+  int afmt;
+  uint8_t* xq;              // codes [T][Kq] (FP8) or [T][Kq / 2] (FP4)
   uint8_t* xs;              // E8M0 [T][Kq / 32]
-  uint8_t* hq;              // E4M3 [T*k][Iq]   routed SiLU(g)*u per pair
+  uint8_t* hq;              // codes [T*k][Iq] or [T*k][Iq / 2]: routed SiLU(g)*u per pair
   uint8_t* hs8;             // E8M0 [T*k][Iq / 32]
   const float* w;           // fp32 [T][k] combine weights
   const uint16_t* residual; // bf16 [T][H] or null

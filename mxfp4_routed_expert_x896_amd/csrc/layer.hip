@@ -898,13 +898,14 @@ __device__ void shared_down_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
 // ------------------------------------------------------------------------
 // Prefill roles.
 
-// x rows -> MXFP8: thread per 32-element block of the padded row (blocks
-// past H get zero codes and exponent 127).
+// x rows -> MXFP8 or MXFP4 (L.afmt): thread per 32-element block of the
+// padded row (blocks past H get zero codes and exponent 127).
 __device__ void quant_x_role(const GemvLayer& L, int b) {
   const int nbq = L.Kq / 32;
   const size_t gb = size_t(b) * kThreads + threadIdx.x;
   if (gb >= size_t(L.T) * nbq) return;
   const int t = int(gb / nbq), kb = int(gb % nbq);
+  const bool fp4 = L.afmt == mx::kFmtFp4;
   uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int E = 0;
   if (kb * 32 < L.H) {
@@ -918,19 +919,37 @@ __device__ void quant_x_role(const GemvLayer& L, int b) {
       for (int d = 0; d < 4; ++d)
         amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[i][d])), fabsf(bf16_hi(v[i][d]))));
     }
-    E = mxfp8_block_exp(amax);
+    if (fp4) {
+      E = mxfp4_block_exp(amax);
+      // element 2 n in the low nibble of byte n: 8 elements per dword
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t c0 = e4m3_rne_sat(__builtin_ldexpf(bf16_lo(v[i][d]), -E));
-        const uint32_t c1 = e4m3_rne_sat(__builtin_ldexpf(bf16_hi(v[i][d]), -E));
-        words[2 * i + d / 2] |= (c0 | (c1 << 8)) << (16 * (d % 2));
-      }
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t c0 = e2m1_rne_sat(__builtin_ldexpf(bf16_lo(v[i][d]), -E));
+          const uint32_t c1 = e2m1_rne_sat(__builtin_ldexpf(bf16_hi(v[i][d]), -E));
+          words[i] |= (c0 | (c1 << 4)) << (8 * d);
+        }
+    } else {
+      E = mxfp8_block_exp(amax);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t c0 = e4m3_rne_sat(__builtin_ldexpf(bf16_lo(v[i][d]), -E));
+          const uint32_t c1 = e4m3_rne_sat(__builtin_ldexpf(bf16_hi(v[i][d]), -E));
+          words[2 * i + d / 2] |= (c0 | (c1 << 8)) << (16 * (d % 2));
+        }
+    }
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(L.xq + size_t(t) * L.Kq + kb * 32);
-  dst[0] = u32x4{words[0], words[1], words[2], words[3]};
-  dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  if (fp4) {
+    *reinterpret_cast<u32x4*>(L.xq + size_t(t) * (L.Kq / 2) + kb * 16) =
+        u32x4{words[0], words[1], words[2], words[3]};
+  } else {
+    u32x4* dst = reinterpret_cast<u32x4*>(L.xq + size_t(t) * L.Kq + kb * 32);
+    dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+    dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  }
   L.xs[size_t(t) * nbq + mx::scale_pos(kb)] = uint8_t(E + 127);
 }
 
@@ -1002,18 +1021,23 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
   auto tok = [&](int j) { return pairs[j] / L.k; };
+  const bool fp4 = L.afmt == mx::kFmtFp4;
+  const int xrow = fp4 ? L.Kq / 2 : L.Kq, hrow_b = fp4 ? L.Iq / 2 : L.Iq;  // code row bytes
   mx::f32x4 acc[mx::kNS][mx::kSub];
-  mx::gemm_tile(
-      acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs,
-      [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq); },
-      [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq / 32); });
+  auto row = [&](int j) { return uint32_t(tok(j)) * uint32_t(xrow); };
+  auto srow = [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq / 32); };
+  if (fp4)
+    mx::gemm_tile<mx::kFmtFp4>(acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs, row, srow);
+  else
+    mx::gemm_tile<mx::kFmtFp8>(acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs, row, srow);
   if (rt == tiles_r - 1 && L.Iq > I) {
     // h columns I .. Iq are read by the down GEMM against clamped weight
     // tiles: zero codes with a finite exponent make them contribute 0
-    const int pad16 = (L.Iq - I) / 16, pad_blocks = (L.Iq - I) / 32;
+    const int pad_bytes = (fp4 ? (L.Iq - I) / 2 : L.Iq - I), hbase = fp4 ? I / 2 : I;
+    const int pad16 = pad_bytes / 16, pad_blocks = (L.Iq - I) / 32;
     for (int i = threadIdx.x; i < tt.mt * pad16; i += kThreads)
-      *reinterpret_cast<u32x4*>(L.hq + size_t(tt.p0 + i / pad16) * L.Iq + I + 16 * (i % pad16)) =
-          u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(L.hq + size_t(tt.p0 + i / pad16) * hrow_b + hbase +
+                                16 * (i % pad16)) = u32x4{0, 0, 0, 0};
     for (int i = threadIdx.x; i < tt.mt * pad_blocks; i += kThreads)
       L.hs8[size_t(tt.p0 + i / pad_blocks) * (L.Iq / 32) +
             mx::scale_pos(I / 32 + i % pad_blocks)] = 127;
@@ -1033,17 +1057,29 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
       }
     amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
     amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    const int E = mxfp8_block_exp(amax);
+    const int E = fp4 ? mxfp4_block_exp(amax) : mxfp8_block_exp(amax);
     const int j = 16 * u + c;
     if (j < tt.mt) {
       const int pos = tt.p0 + j;  // h rows in plan order: a tile's rows are contiguous
-      uint8_t* hrow = L.hq + size_t(pos) * L.Iq + rt * 128 + 32 * wave;
+      // lane (c, g) holds elements 16 r + 4 g .. + 3 of the wave's 32-row block
+      if (fp4) {
+        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + (rt * 128 + 32 * wave) / 2;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        uint32_t word = 0;
+        for (int r = 0; r < 2; ++r) {
+          uint32_t half = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(__builtin_ldexpf(h[r][i], -E)) << (8 * i);
-        *reinterpret_cast<uint32_t*>(hrow + 16 * r + 4 * g) = word;
+          for (int i = 0; i < 4; ++i) half |= e2m1_rne_sat(__builtin_ldexpf(h[r][i], -E)) << (4 * i);
+          *reinterpret_cast<uint16_t*>(hrow + 8 * r + 2 * g) = uint16_t(half);
+        }
+      } else {
+        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + rt * 128 + 32 * wave;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) word |= e4m3_rne_sat(__builtin_ldexpf(h[r][i], -E)) << (8 * i);
+          *reinterpret_cast<uint32_t*>(hrow + 16 * r + 4 * g) = word;
+        }
       }
       if (g == 0) L.hs8[size_t(pos) * (L.Iq / 32) + mx::scale_pos(blk)] = uint8_t(E + 127);
     }
@@ -1079,11 +1115,16 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
   mx::f32x4 acc[mx::kNS][mx::kSub];
-  mx::gemm_tile(
-      acc, st, pd.nkb4 / 4, lds, tt.mt, L.hq + size_t(tt.p0) * L.Iq,
-      L.hs8 + size_t(tt.p0) * (L.Iq / 32),
-      [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq); },
-      [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq / 32); });
+  const bool fp4 = L.afmt == mx::kFmtFp4;
+  const int hrow_b = fp4 ? L.Iq / 2 : L.Iq;  // code row bytes
+  const uint8_t* hc = L.hq + size_t(tt.p0) * hrow_b;
+  const uint8_t* hs = L.hs8 + size_t(tt.p0) * (L.Iq / 32);
+  auto row = [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(hrow_b); };
+  auto srow = [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq / 32); };
+  if (fp4)
+    mx::gemm_tile<mx::kFmtFp4>(acc, st, pd.nkb4 / 4, lds, tt.mt, hc, hs, row, srow);
+  else
+    mx::gemm_tile<mx::kFmtFp8>(acc, st, pd.nkb4 / 4, lds, tt.mt, hc, hs, row, srow);
 #pragma unroll
   for (int u = 0; u < mx::kSub; ++u) {
     const int j = 16 * u + c;

@@ -35,8 +35,17 @@ namespace mx {
 constexpr int kTok = kPlanTileTokens;  // tokens (B columns) per tile, 4 MFMA column groups
 constexpr int kSub = kTok / 16;
 constexpr int kStep = 512;             // contraction columns per super-step (4 tiles)
-constexpr int kStageBytes = kTok * kStep;  // 32 KiB of activation codes per staging buffer
+constexpr int kStageBytes = kTok * kStep;  // 32 KiB of activation codes per staging buffer (FP8)
 constexpr int kNS = 4;                 // A streams (16-row groups x matrices) per wave
+
+// B (activation) formats: the MFMA's blgp operand code.
+constexpr int kFmtFp8 = 0;  // MXFP8: E4M3 codes, one byte per element
+constexpr int kFmtFp4 = 4;  // MXFP4: E2M1 codes, two per byte, even element in the low nibble
+// Bytes of one token's codes in one super-step, and of a staging buffer.
+template <int BF>
+constexpr int row_bytes() { return BF == kFmtFp4 ? kStep / 2 : kStep; }
+template <int BF>
+constexpr int stage_bytes() { return kTok * row_bytes<BF>(); }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -54,10 +63,10 @@ __host__ __device__ __forceinline__ int scale_pos(int b) {
   return (b & ~15) | ((b & 3) << 2) | ((b & 15) >> 2);
 }
 
-template <int J>
+template <int J, int BF>
 __device__ __forceinline__ f32x4 mma(u32x4 a, i32x8 b, f32x4 c, uint32_t sa, uint32_t sb) {
   const i32x8 av = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, 0, J, int(sa), J,
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, BF, J, int(sa), J,
                                                           int(sb));
 }
 
@@ -90,38 +99,47 @@ __device__ __forceinline__ void load_a(ATiles& t, const AStreams& st, int kq) {
   }
 }
 
-// Staged activations: token j's kStep code bytes of a super-step as 32
-// 16-byte chunks, chunk q at slot q ^ (j % 16) of the token's 512-byte LDS
-// row.  The 16 lanes that read the same chunk of 16 consecutive tokens then
-// hit 16 different bank groups, and a wave-wide staging load still fills
-// 1 KiB of LDS contiguously (two token rows).
+// Staged activations: token j's code bytes of a super-step (row_bytes: 512
+// for FP8, 256 for FP4) as 16-byte chunks, chunk q at slot q ^ (j % 16) of
+// the token's LDS row.  The 16 lanes that read the same chunk of 16
+// consecutive tokens then hit 16 different bank groups, and a wave-wide
+// staging load still fills 1 KiB of LDS contiguously (two FP8 token rows,
+// four FP4 ones).
 //
 // Per lane, as 32-bit byte offsets from the wave-uniform bases: the global
-// chunk each of the wave's 2 NSub staging loads fetches at super-step 0
-// (wave w issues loads w, w + 4, ..., covering the first 16 NSub tokens),
-// and the B exponent dword of each of its token groups.
-template <int NSub>
+// chunk each of the wave's staging loads fetches at super-step 0 (wave w
+// issues loads w, w + 4, ..., covering the first 16 NSub tokens; 2 NSub
+// loads for FP8, NSub for FP4), and the B exponent dword of each of its
+// token groups.
+template <int BF>
+constexpr int tokens_per_load() { return 1024 / row_bytes<BF>(); }
+template <int NSub, int BF>
+constexpr int staging_loads() { return 16 * NSub / 4 / tokens_per_load<BF>(); }
+
+template <int NSub, int BF>
 struct BStage {
   const uint8_t* cbase;
   const uint8_t* sbase;
-  uint32_t src[2 * NSub];
+  uint32_t src[staging_loads<NSub, BF>()];
   uint32_t scl[NSub];
 };
 
 // row(j): token j's code row as a byte offset from cbase; srow(j): its
 // MFMA-ordered exponent row as a byte offset from sbase.
-template <int NSub, typename Row, typename SRow>
-__device__ __forceinline__ void prepare_b(BStage<NSub>& bs, const uint8_t* cbase,
+template <int NSub, int BF, typename Row, typename SRow>
+__device__ __forceinline__ void prepare_b(BStage<NSub, BF>& bs, const uint8_t* cbase,
                                           const uint8_t* sbase, Row row, SRow srow) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
+  constexpr int kChunks = row_bytes<BF>() / 16;  // chunks per token row: 32 (FP8), 16 (FP4)
   bs.cbase = cbase;
   bs.sbase = sbase;
 #pragma unroll
-  for (int i = 0; i < 2 * NSub; ++i) {
-    const int j = 2 * (wave + 4 * i) + lane / 32;  // token of this lane's LDS chunk
-    bs.src[i] = row(j) + 16 * ((lane % 32) ^ (j % 16));
+  for (int i = 0; i < staging_loads<NSub, BF>(); ++i) {
+    // token of this lane's LDS chunk, and the chunk whose slot the lane fills
+    const int j = tokens_per_load<BF>() * (wave + 4 * i) + lane / kChunks;
+    bs.src[i] = row(j) + 16 * ((lane % kChunks) ^ (j % 16));
   }
 #pragma unroll
   for (int u = 0; u < NSub; ++u) bs.scl[u] = srow(16 * u + c) + 4 * g;
@@ -142,26 +160,35 @@ __device__ __forceinline__ void load_to_lds16(const uint8_t* base, uint32_t off,
                : "memory", "m0");
 }
 
-template <int NSub>
-__device__ __forceinline__ void stage_b(uint8_t* lds, int kq, const BStage<NSub>& bs) {
+template <int NSub, int BF>
+__device__ __forceinline__ void stage_b(uint8_t* lds, int kq, const BStage<NSub, BF>& bs) {
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  const uint8_t* base = bs.cbase + size_t(kq) * kStep;
+  const uint8_t* base = bs.cbase + size_t(kq) * row_bytes<BF>();
   const uint32_t l0 = uint32_t(reinterpret_cast<uintptr_t>((lvoid*)lds));
 #pragma unroll
-  for (int i = 0; i < 2 * NSub; ++i)
+  for (int i = 0; i < staging_loads<NSub, BF>(); ++i)
     load_to_lds16(base, bs.src[i], __builtin_amdgcn_readfirstlane(l0 + (wave + 4 * i) * 1024));
 }
 
-// B operand of tile J for token group u: token 16 u + c, bytes K = 16 g ..
-// 16 g + 15 (chunk 8 J + g) and K = 64 + 16 g .. (chunk 8 J + 4 + g).
+// B operand of tile J for token group u, token 16 u + c.  FP8: bytes K =
+// 16 g .. 16 g + 15 (chunk 8 J + g) and K = 64 + 16 g .. (chunk 8 J + 4 + g).
+// FP4 (established with one-hot probes, like the A layout): elements K =
+// 32 g .. 32 g + 31, low nibble first (chunk 4 J + g); the upper half of the
+// operand is unused.
+template <int BF>
 __device__ __forceinline__ i32x8 read_b(const uint8_t* buf, int u, int J) {
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
-  const uint8_t* r = buf + (16 * u + c) * kStep;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + g) ^ c));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + 4 + g) ^ c));
-  return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
-               int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+  const uint8_t* r = buf + (16 * u + c) * row_bytes<BF>();
+  if constexpr (BF == kFmtFp4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(r + 16 * ((4 * J + g) ^ c));
+    return i32x8{int(v[0]), int(v[1]), int(v[2]), int(v[3]), 0, 0, 0, 0};
+  } else {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + g) ^ c));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(r + 16 * ((8 * J + 4 + g) ^ c));
+    return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]),
+                 int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+  }
 }
 
 // The contraction of one tile over nkq super-steps, for the first NSub
@@ -174,7 +201,7 @@ __device__ __forceinline__ i32x8 read_b(const uint8_t* buf, int u, int J) {
 // before the one that uses them.  B operands are read from LDS two (tile, token
 // group) pairs ahead of the MFMAs that use them.  Every wave issues the same loads in the same
 // order, so one counted wait per step covers the staging.
-template <int NSub, typename Row, typename SRow>
+template <int NSub, int BF, typename Row, typename SRow>
 __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStreams& st, int nkq,
                                             uint8_t* lds, const uint8_t* cbase,
                                             const uint8_t* sbase, Row row, SRow srow) {
@@ -182,7 +209,7 @@ __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStre
   for (int s = 0; s < kNS; ++s)
 #pragma unroll
     for (int u = 0; u < kSub; ++u) acc[s][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  BStage<NSub> bs;
+  BStage<NSub, BF> bs;
   prepare_b(bs, cbase, sbase, row, srow);
   ATiles a;
   uint32_t sb[NSub];
@@ -195,11 +222,11 @@ __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStre
   auto step = [&](int kq, auto reload) {
     constexpr bool kReload = decltype(reload)::value;
     constexpr int kGroups = 4 * NSub;  // (tile J, token group u) pairs, J major
-    const uint8_t* cur = lds + (kq & 1) * kStageBytes;
+    const uint8_t* cur = lds + (kq & 1) * stage_bytes<BF>();
     const int kn = kq + 1;
     uint32_t as_n[kNS], sb_n[NSub];  // exponent dwords of step kq + 1
     if constexpr (kReload) {
-      stage_b(lds + (kn & 1) * kStageBytes, kn, bs);
+      stage_b(lds + (kn & 1) * stage_bytes<BF>(), kn, bs);
 #pragma unroll
       for (int s = 0; s < kNS; ++s)
         as_n[s] = *reinterpret_cast<const uint32_t*>(st.scl[s] + 4 * kn + st.lane_scl);
@@ -208,20 +235,20 @@ __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStre
         sb_n[u] = *reinterpret_cast<const uint32_t*>(bs.sbase + 16 * kn + bs.scl[u]);
     }
     i32x8 b[3];  // B operands of groups gi, gi + 1, gi + 2
-    b[0] = read_b(cur, 0, 0);
-    if (kGroups > 1) b[1] = read_b(cur, 1 % NSub, 1 / NSub);
+    b[0] = read_b<BF>(cur, 0, 0);
+    if (kGroups > 1) b[1] = read_b<BF>(cur, 1 % NSub, 1 / NSub);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
       const int J = gi / NSub, u = gi % NSub;
-      if (gi + 2 < kGroups) b[(gi + 2) % 3] = read_b(cur, (gi + 2) % NSub, (gi + 2) / NSub);
+      if (gi + 2 < kGroups) b[(gi + 2) % 3] = read_b<BF>(cur, (gi + 2) % NSub, (gi + 2) / NSub);
 #pragma unroll
       for (int s = 0; s < kNS; ++s) {
         switch (J) {  // opsel J is an immediate
-          case 0: acc[s][u] = mma<0>(a.w[s][0], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
-          case 1: acc[s][u] = mma<1>(a.w[s][1], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
-          case 2: acc[s][u] = mma<2>(a.w[s][2], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
-          default: acc[s][u] = mma<3>(a.w[s][3], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          case 0: acc[s][u] = mma<0, BF>(a.w[s][0], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          case 1: acc[s][u] = mma<1, BF>(a.w[s][1], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          case 2: acc[s][u] = mma<2, BF>(a.w[s][2], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
+          default: acc[s][u] = mma<3, BF>(a.w[s][3], b[gi % 3], acc[s][u], a.s[s], sb[u]); break;
         }
       }
       if constexpr (kReload) {
@@ -241,7 +268,8 @@ __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStre
       for (int u = 0; u < NSub; ++u) sb[u] = sb_n[u];
       // The staging loads for kq + 1 were issued before this step's 20 + NSub
       // exponent and weight loads; vector loads complete in order, so at most
-      // 16 outstanding means every staging load has landed in LDS.  A fenced
+      // 16 outstanding means every staging load has landed in LDS (for either
+      // B format: only the number of staging loads before them differs).  A fenced
       // barrier would wait for all loads: the memory model orders the
       // staging's LDS writes with vmcnt(0).
       __builtin_amdgcn_s_waitcnt(kVmcnt16);
@@ -256,16 +284,18 @@ __device__ __forceinline__ void gemm_tile_n(f32x4 (&acc)[kNS][kSub], const AStre
 // Only the 16-token column groups that hold tokens are staged and multiplied
 // (ntok = the tile's token count, 1 .. kTok); the other groups keep acc = 0.
 // All threads of the workgroup must call it.
-template <typename Row, typename SRow>
+// BF: the activations' format (kFmtFp8 or kFmtFp4); row(j) and srow(j) give
+// token j's code and exponent rows in bytes.
+template <int BF, typename Row, typename SRow>
 __device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], const AStreams& st, int nkq,
                                           uint8_t* lds, int ntok, const uint8_t* cbase,
                                           const uint8_t* sbase, Row row, SRow srow) {
   static_assert(kSub == 4, "one instantiation per group count");
   switch (__builtin_amdgcn_readfirstlane((ntok + 15) / 16)) {
-    case 1: gemm_tile_n<1>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
-    case 2: gemm_tile_n<2>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
-    case 3: gemm_tile_n<3>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
-    default: gemm_tile_n<4>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    case 1: gemm_tile_n<1, BF>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    case 2: gemm_tile_n<2, BF>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    case 3: gemm_tile_n<3, BF>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
+    default: gemm_tile_n<4, BF>(acc, st, nkq, lds, cbase, sbase, row, srow); break;
   }
 }
 

@@ -154,16 +154,37 @@ def _region(b, lay, T, ws, region, dtype):
     return b.workspace_region(lay, T, region, ws).cpu().numpy().view(dtype)
 
 
-def _e4m3_between(v_lo, v_hi):
-    """Decoded E4M3 values that RNE-with-saturation gives to v_lo and v_hi
-    (every value in between rounds to a code between them)."""
-    return (F.e4m3_decode(F.e4m3_encode_rne_sat(v_lo)), F.e4m3_decode(F.e4m3_encode_rne_sat(v_hi)))
+# the two MX activation formats: element encoder, decoder, quantiser, and the
+# largest normal exponent that the block-exponent rule subtracts
+MX_FORMATS = {
+    "e4m3": (F.e4m3_encode_rne_sat, F.e4m3_decode, F.mxfp8_quantize, F.mxfp8_dequant,
+             F.E4M3_EMAX),
+    "e2m1": (F.e2m1_encode_rne_sat, F.e2m1_decode, F.mxfp4_quantize, F.mxfp4_act_dequant,
+             F.E2M1_EMAX),
+}
 
 
-def _block_exp(amax):
+def _between(v_lo, v_hi, fmt):
+    """Decoded values that RNE-with-saturation gives to v_lo and v_hi (every
+    value in between rounds to a code between them)."""
+    enc, dec = MX_FORMATS[fmt][:2]
+    return dec(enc(v_lo)), dec(enc(v_hi))
+
+
+def _block_exp(amax, fmt):
     with np.errstate(divide="ignore"):
         _, ex = np.frexp(np.maximum(amax, 0.0))
-    return np.where(amax <= 0, -127, np.clip(ex - 1 - F.E4M3_EMAX, -127, 127))
+    return np.where(amax <= 0, -127, np.clip(ex - 1 - MX_FORMATS[fmt][4], -127, 127))
+
+
+def unpack_nibbles(packed):
+    """uint8 [..., n] of two E2M1 codes per byte -> uint8 [..., 2 n], the even
+    element from the low nibble."""
+    packed = np.asarray(packed, np.uint8)
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
 
 
 def h_error_bound(xin, wg, wu):
@@ -184,10 +205,11 @@ def h_error_bound(xin, wg, wu):
     return M.silu(g) * u, dh
 
 
-def check_h_block_codes(h, dh, codes_g, scales_g):
-    """Element-by-element check of a kernel's MXFP8 codes of h (rows of I
-    values, codes uint8 [n, I], scale bytes [n, I/32] in plain order)
-    against the oracle's quantisation of the float64 h.  Equal values pass.
+def check_h_block_codes(h, dh, codes_g, scales_g, fmt="e4m3"):
+    """Element-by-element check of a kernel's MX codes of h (MXFP8 for fmt
+    "e4m3", MXFP4 for "e2m1"; rows of I values, codes uint8 [n, I], scale
+    bytes [n, I/32] in plain order) against the oracle's quantisation of the
+    float64 h.  Equal values pass.
     A differing block exponent must be reachable from some block maximum
     within the fp32 bound dh of the float64 one; a differing code must be
     the rounding of some value within dh of h under the kernel's exponent.
@@ -195,9 +217,10 @@ def check_h_block_codes(h, dh, codes_g, scales_g):
     element, and how many elements differ.  Raises AssertionError on a code
     no fp32 evaluation of h could produce."""
     n, I = h.shape
-    co, so = F.mxfp8_quantize(h)
-    vg = F.mxfp8_dequant(codes_g, scales_g)
-    vo = F.mxfp8_dequant(co, so)
+    _, dec, quant, dequant, _ = MX_FORMATS[fmt]
+    co, so = quant(h)
+    vg = dequant(codes_g, scales_g)
+    vo = dequant(co, so)
     diff = vg != vo
     if not diff.any():
         return np.zeros_like(h), 0
@@ -207,13 +230,13 @@ def check_h_block_codes(h, dh, codes_g, scales_g):
     db = dh.reshape(n, -1, 32)
     amax = np.abs(hb).max(axis=-1)
     dmax = db.max(axis=-1)
-    lo_e, hi_e = _block_exp(amax - dmax), _block_exp(amax + dmax)
+    lo_e, hi_e = _block_exp(amax - dmax, fmt), _block_exp(amax + dmax, fmt)
     bad_exp = (Eg != Eo) & ((Eg < lo_e) | (Eg > hi_e))
     assert not bad_exp.any(), (f"{bad_exp.sum()} block exponents no fp32 h reaches: "
                                f"kernel {Eg[bad_exp][:4]}, oracle {Eo[bad_exp][:4]}")
     sc = np.repeat(np.ldexp(1.0, Eg), 32, axis=-1)
-    qg = F.e4m3_decode(codes_g)
-    lo, hi = _e4m3_between((h - dh) / sc, (h + dh) / sc)
+    qg = dec(codes_g)
+    lo, hi = _between((h - dh) / sc, (h + dh) / sc, fmt)
     ok = (qg >= np.minimum(lo, hi)) & (qg <= np.maximum(lo, hi))
     bad = diff & ~ok
     assert not bad.any(), (f"{bad.sum()} h codes outside the fp32 bound: kernel "
@@ -226,10 +249,12 @@ MAX_FLIP_RATE = 1e-2  # far above the observed rate; a wrong rounding rule flips
 
 
 def check_mxfp8_workspace(b, lay, ws, T, x_bits, ids, w, orc, tokens=None, experts=None,
-                          x_rows=None):
-    """Checks of an MFMA-path call's intermediate values in its workspace:
+                          x_rows=None, fmt="e4m3"):
+    """Checks of an MFMA-path call's intermediate values in its workspace
+    (fmt "e4m3": the MXFP8 path; "e2m1": the MXFP4 path, whose code rows
+    hold two codes per byte):
       * x codes and block exponents of rows x_rows (default all) bit-exact
-        against the oracle's MXFP8 quantiser (x is exact bf16 on both sides),
+        against the oracle's quantiser (x is exact bf16 on both sides),
         zero codes and exponent 127 in the padding past H;
       * the plan: every pair at exactly one position, grouped by expert in
         ascending order;
@@ -245,9 +270,12 @@ def check_mxfp8_workspace(b, lay, ws, T, x_bits, ids, w, orc, tokens=None, exper
     ids = np.asarray(ids, np.int64)
     w = np.asarray(w, np.float64)
     rows = np.arange(T) if x_rows is None else np.asarray(x_rows)
-    xq = _region(b, lay, T, ws, b.WS_X_CODES, np.uint8).reshape(T, Kq)
+    quant = MX_FORMATS[fmt][2]
+    fp4 = fmt == "e2m1"
+    xq = _region(b, lay, T, ws, b.WS_X_CODES, np.uint8)
+    xq = unpack_nibbles(xq[:T * Kq // 2].reshape(T, Kq // 2)) if fp4 else xq.reshape(T, Kq)
     xs = _region(b, lay, T, ws, b.WS_X_SCALES, np.uint8).reshape(T, Kq // 32)
-    rc, rs = F.mxfp8_quantize(F.bf16_decode(x_bits[rows]))
+    rc, rs = quant(F.bf16_decode(x_bits[rows]))
     np.testing.assert_array_equal(xq[rows, :H], rc)
     np.testing.assert_array_equal(xs[rows][:, scale_pos(np.arange(H // 32))], rs)
     assert not xq[rows, H:].any()
@@ -258,7 +286,9 @@ def check_mxfp8_workspace(b, lay, ws, T, x_bits, ids, w, orc, tokens=None, exper
     assert (np.diff(pe) >= 0).all(), "plan positions not grouped by ascending expert"
     pos_of = np.empty(T * k, np.int64)
     pos_of[pairs] = np.arange(T * k)
-    hq = _region(b, lay, T, ws, b.WS_H_CODES, np.uint8).reshape(T * k, Iq)
+    hq = _region(b, lay, T, ws, b.WS_H_CODES, np.uint8)
+    hq = (unpack_nibbles(hq[:T * k * Iq // 2].reshape(T * k, Iq // 2)) if fp4
+          else hq.reshape(T * k, Iq))
     hsm = _region(b, lay, T, ws, b.WS_H_SCALES, np.uint8).reshape(T * k, Iq // 32)
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
     if experts is None:
@@ -274,9 +304,9 @@ def check_mxfp8_workspace(b, lay, ws, T, x_bits, ids, w, orc, tokens=None, exper
         pos = pos_of[t_idx * k + j_idx]
         assert not hq[pos, I:].any() and (hsm[pos][:, pad_pos] == 127).all()
         wg, wu, wd = dequant_expert(orc.expert_record(int(e)), H, I)
-        xin = F.mxfp8_roundtrip(F.bf16_decode(x_bits[t_idx]))
+        xin = (F.mxfp4_roundtrip if fp4 else F.mxfp8_roundtrip)(F.bf16_decode(x_bits[t_idx]))
         h, dh = h_error_bound(xin, wg, wu)
-        delta, nd = check_h_block_codes(h, dh, hq[pos, :I], hsm[pos][:, sg_pos])
+        delta, nd = check_h_block_codes(h, dh, hq[pos, :I], hsm[pos][:, sg_pos], fmt)
         return t_idx, j_idx, (delta @ wd.T if nd else None), nd, h.size
 
     results = threaded_map(one, [int(e) for e in experts], "h-code check")

@@ -176,6 +176,45 @@ def test_k3_prefill_4096_with_bias(b, k3):
           f"{per_expert[idlest]}; {few}: {per_expert[few]}): rel L2 max {err.max():.3e}")
 
 
+def test_k3_prefill_4096_mxfp4_activations(b, k3):
+    """K3 prefill (4096 tokens, logit bias) on the FP4 x FP4 path
+    (MOE_PATH_MFMA_FP4): routing for every token, MXFP4 x codes bit-exact on
+    256 tokens, h codes of every pair of every expert the sampled tokens use,
+    and the output of 32 tokens (the busiest expert's last tile first)
+    against the oracle in its MXFP4-activation mode."""
+    from synth import router_bias
+    bias_h = router_bias(0, 0, 896)
+    lay = b.Layer(7168, 1536, 896, 16, k3.lib.router_w, k3.lib.experts, k3.lib.shared_gate,
+                  k3.lib.shared_up, k3.lib.shared_down, router_bias=torch.from_numpy(bias_h).cuda())
+    orc = M.Layer(7168, 1536, 896, 16, k3.oracle.router_w, k3.oracle.expert_record,
+                  shared=k3.oracle.shared, router_bias=bias_h)
+    T = 4096
+    xh, xd = SD.upload_tokens(4000, T, 7168)
+    ids = torch.empty((T, 16), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, 16), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, 7168), dtype=torch.int16, device="cuda")
+    ws = lay.workspace(T)
+    b.moe_layer(lay, xd, y, ids, w, ws, path=b.PATH_MFMA_FP4)
+    torch.cuda.synchronize()
+    ids, w, y = ids.cpu().numpy(), w.cpu().numpy(), to_np_u16(y)
+    _, _, s = M.route(xh, orc)
+    check_routing(ids, w, s, 16)
+    per_expert = np.bincount(ids.ravel(), minlength=896)
+    busiest = int(per_expert.argmax())
+    pairs = b.workspace_region(lay, T, b.WS_PAIRS, ws).cpu().numpy().view(np.int32)
+    grp = pairs[ids.reshape(-1)[pairs] == busiest]
+    rng = np.random.default_rng(5)
+    sample = set((grp[(len(grp) - 1) // 64 * 64:] // 16)[:24].tolist()) | {0, T - 1}
+    while len(sample) < 32:
+        sample.add(int(rng.integers(T)))
+    sample = sorted(sample)
+    eff = check_mxfp8_workspace(b, lay, ws, T, xh, ids, w, orc, tokens=sample, fmt="e2m1",
+                                x_rows=np.sort(rng.choice(T, 256, replace=False)))
+    ref = oracle_rows(xh, orc, ids, oracle_weights(s, ids), sample, act_mxfp4=True)
+    err = check_parity(y[sample], ref, eff, strict=True)
+    print(f"K3 prefill MXFP4 activations, {len(sample)} sampled tokens: rel L2 max {err.max():.3e}")
+
+
 @pytest.mark.parametrize("T", [1, 64])
 def test_k3_router_bias_in_choice_only_with_routed_scale(b, k3, T):
     """K3 decode with the bias in the choice only (key sigmoid(l) + b, b of

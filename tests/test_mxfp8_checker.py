@@ -114,3 +114,29 @@ def test_scale_positions_permute_each_group_of_16():
     for g in range(4):
         assert sorted(p[16 * g:16 * g + 16].tolist()) == list(range(16 * g, 16 * g + 16))
     assert p[1] == 4 and p[4] == 1 and p[5] == 5
+
+
+def test_e2m1_codes_oracle_pass_and_one_step_off_fails():
+    """The same checks on MXFP4 (E2M1) codes."""
+    h = _h(6, n=8)
+    c, s = F.mxfp4_quantize(h)
+    delta, nd = check_h_block_codes(h, 1e-9 * np.abs(h), c, s, "e2m1")
+    assert nd == 0 and not delta.any()
+    q = F.e2m1_decode(c)
+    sc = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=-1)
+    on_code = np.isclose(h / sc, q, rtol=0, atol=1e-3) & (np.abs(q) >= 1) & (np.abs(q) < 6)
+    if not on_code.any():  # make one element sit exactly on a code
+        h[0, 3] = np.sign(h[0, 3] or 1.0) * 2.0 * sc[0, 3]
+        c, s = F.mxfp4_quantize(h)
+        on_code = np.zeros_like(h, bool)
+        on_code[0, 3] = True
+    i = np.argwhere(on_code)[0]
+    bad = c.copy()
+    bad[tuple(i)] = c[tuple(i)] + 1 if (c[tuple(i)] & 7) < 7 else c[tuple(i)] - 1
+    with pytest.raises(AssertionError, match="outside the fp32 bound"):
+        check_h_block_codes(h, 1e-9 * np.abs(h), bad, s, "e2m1")
+
+
+def test_unpack_nibbles_low_first():
+    from tests._gpu import unpack_nibbles
+    assert unpack_nibbles(np.array([[0x21, 0xF0]], np.uint8)).tolist() == [[1, 2, 0, 15]]
