@@ -15,8 +15,9 @@ the other layers run in between).
 
 b1_stream is the decode step with the experts NOT resident: their records sit
 in pinned host memory and an HBM pool of 256 slots is filled on demand
-(moe_pool_fetch) between the router and the expert kernels, so each step
-includes the host-to-device copies of the experts it misses.
+(moe_pool_fetch, on a copy stream) after the router; the shared experts run
+meanwhile and the routed experts wait for the copies (moe_forward_pooled), so
+each step includes the host-to-device copies of the experts it misses.
 
 Printed: one JSON line with tokens/s (value), ms per step, the expert-weight
 HBM rate, the dominant kernel's roofline (HIP events around each kernel of
@@ -544,8 +545,10 @@ def main():
     y = torch.empty((n_layers + 1, T, H), dtype=torch.int16, device=dev)
     normed = torch.empty((T, H), dtype=torch.int16, device=dev)
     ws = layers[0].workspace(T)
-    pool = pooled = None
+    pool = pooled = copy_stream = ready = None
     if cfgd.get("pool_slots"):
+        copy_stream = torch.cuda.Stream(device=dev)  # default priority
+        ready = torch.cuda.Event()
         L0 = layers[0]
         host = torch.empty(L0.experts.shape, dtype=torch.uint8, pin_memory=True)
         host.copy_(L0.experts)
@@ -558,11 +561,15 @@ def main():
 
     def step(i):
         if pooled is not None:
-            # the router picks the experts, the pool makes them resident
-            # (a host round trip for the ids), then the expert kernels run
+            # the router picks the experts (a host round trip for the ids);
+            # the pool copies their records on the copy stream while the
+            # shared experts run; the routed experts wait for the copies
             b.route(pooled, xs[i], ids[i, 0], wts[i, 0], ws)
-            pool.fetch(ids[i, 0].cpu().numpy())
-            b.forward(pooled, xs[i], ids[i, 0], wts[i, 0], y[0], ws, path=path)
+            ids_host = ids[i, 0].cpu().numpy()
+            copy_stream.wait_stream(torch.cuda.current_stream())
+            pool.fetch(ids_host, stream=copy_stream)
+            ready.record(copy_stream)
+            b.forward_pooled(pooled, xs[i], ids[i, 0], wts[i, 0], y[0], ws, ready, path=path)
         elif n_layers == 1:
             L = layers[i % len(layers)]
             b.moe_layer(L, xs[i], y[0], ids[i, 0], wts[i, 0], ws, path=path)
@@ -713,6 +720,7 @@ def main():
             "h2d_bytes_per_step": round(h2d),
             "h2d_gbs": round(h2d / (ms_per_step * 1e-3) / 1e9, 2),
             "pcie_peak_gbs": PCIE_PEAK_GBS,
+            "copies_at_pcie_peak_us": round(h2d / (PCIE_PEAK_GBS * 1e9) * 1e6, 1),
             "note": "value includes the host-to-device copies; kernel_us and roofline are the "
                     "same kernels timed on the resident layer"}
     if not args.no_cpu_baseline:

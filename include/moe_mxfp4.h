@@ -226,6 +226,23 @@ int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens
                 uint16_t* y, int32_t path, void* workspace, uint64_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * moe_forward for experts that arrive while the call runs (an expert pool
+ * filled on another stream; Deltafin README, I/O and streaming: the expert
+ * reads overlap the compute that does not need them).  On the GEMV path the
+ * shared experts (which need no routed record) are enqueued first, then
+ * `stream` waits for records_ready -- an event the caller records on the
+ * stream of moe_pool_fetch after the fetch -- then the routed experts and the
+ * combine run.  The MFMA paths, whose shared experts share the routed
+ * launches, wait before everything.  records_ready NULL: moe_forward.  The
+ * caller keeps earlier work that reads the pool ordered before the fetch
+ * (moe_pool_fetch overwrites slots on its own stream).
+ */
+int moe_forward_pooled(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                       const int32_t* topk_ids, const float* topk_w, const uint16_t* residual,
+                       uint16_t* y, int32_t path, void* workspace, uint64_t workspace_bytes,
+                       hipEvent_t records_ready, hipStream_t stream);
+
 /* moe_route followed by moe_forward, scheduled together (the shared experts
  * overlap the router).  topk_ids / topk_w receive the routing. */
 int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,

@@ -77,6 +77,8 @@ _SIGNATURES = {
     "moe_route": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _U64, _P]),
     "moe_forward": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P, _U64, _P]),
     "moe_layer": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P, _U64, _P]),
+    "moe_forward_pooled": (ctypes.c_int, [_DESC, _P, _I64, _P, _P, _P, _P, _I32, _P, _U64, _P,
+                                          _P]),
     "moe_mfma_min_tokens": (ctypes.c_int64, []),
     "moe_rmsnorm": (ctypes.c_int, [_P, _P, ctypes.c_float, _I64, _I32, _P, _P]),
     "moe_dequant_export": (ctypes.c_int, [_DESC, _I32, _I32, _P, _P]),
@@ -286,6 +288,17 @@ def forward(layer, x, topk_ids, topk_w, y, ws, residual=None, path=PATH_AUTO, st
     _check(_lib().moe_forward(layer.desc, _ptr(x), x.shape[0], _ptr(topk_ids), _ptr(topk_w),
                               _ptr(residual), _ptr(y), path, _ptr(ws), ws.numel(),
                               _stream(stream)), "moe_forward")
+
+
+def forward_pooled(layer, x, topk_ids, topk_w, y, ws, records_ready, residual=None,
+                   path=PATH_AUTO, stream=None):
+    """forward whose routed part waits for records_ready (a torch.cuda.Event
+    recorded after the pool's fetch on another stream); the shared experts
+    run before the wait."""
+    ev = None if records_ready is None else ctypes.c_void_p(records_ready.cuda_event)
+    _check(_lib().moe_forward_pooled(layer.desc, _ptr(x), x.shape[0], _ptr(topk_ids),
+                                     _ptr(topk_w), _ptr(residual), _ptr(y), path, _ptr(ws),
+                                     ws.numel(), ev, _stream(stream)), "moe_forward_pooled")
 
 
 def moe_layer(layer, x, y, topk_ids, topk_w, ws, residual=None, path=PATH_AUTO, stream=None):

@@ -299,6 +299,40 @@ int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const
   return stage(moe::StageKind::RoutedDownCombine, G, s3, stream);
 }
 
+// Given routing, with the routed experts' records arriving on another
+// stream (expert pool): the shared experts first -- plan + shared gate/up,
+// shared down -- then the stream waits for `ready` (recorded by the caller
+// after the records' copies), then routed gate/up and routed down + combine.
+// The shared experts' weight stream overlaps the copies.
+int do_forward_gemv_after(const moe_layer_desc* L, const uint16_t* x, int64_t T,
+                          const int32_t* ids, const float* w, const uint16_t* residual,
+                          uint16_t* y, void* ws, hipEvent_t ready, hipStream_t stream) {
+  moe::GemvLayer G = gemv_layer(L, x, T, ws);
+  G.ids_in = ids;
+  G.direct = T == 1;
+  G.w = w;
+  G.residual = residual;
+  G.y = y;
+  const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
+  moe::Stage s1;
+  s1.n_plan = 1;
+  s1.n_sgu = S * (L->inter / 16);
+  int st = stage(moe::StageKind::PlanSharedGateUp, G, s1, stream);
+  if (st) return st;
+  if (S > 0) {
+    moe::Stage s1b;  // the shared down alone (the routed gate/up launch without its routed part)
+    s1b.n_sdn = S * n_shared_tiles(L);
+    if ((st = stage(moe::StageKind::RoutedGateUp, G, s1b, stream))) return st;
+  }
+  if ((st = launched(hipStreamWaitEvent(stream, ready, 0), stream))) return st;
+  moe::Stage s2;
+  s2.n_rgu = ma * tiles_gu;
+  if ((st = stage(moe::StageKind::RoutedGateUp, G, s2, stream))) return st;
+  moe::Stage s3;
+  s3.n_rdn = ma * n_tiles(L);
+  return stage(moe::StageKind::RoutedDownCombine, G, s3, stream);
+}
+
 // Router and experts: logits + shared gate/up, top-k + plan + shared down,
 // routed gate/up, routed down + combine.
 int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
@@ -576,6 +610,37 @@ MOE_API int moe_forward(const moe_layer_desc* layer, const uint16_t* x, int64_t 
   if ((st = check_device())) return st;
   prof_begin(stream);
   const int p = resolve_path(path, n_tokens);
+  if (p != MOE_PATH_GEMV)
+    return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace,
+                           act_format(p), stream);
+  return do_forward_gemv(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace, stream);
+}
+
+MOE_API int moe_forward_pooled(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const uint16_t* residual, uint16_t* y, int32_t path,
+                               void* workspace, uint64_t workspace_bytes,
+                               hipEvent_t records_ready, hipStream_t stream) {
+  int st = check_layer(layer);
+  if (st) return st;
+  if ((st = check_tokens(n_tokens))) return st;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || y == nullptr) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(y))
+    return MOE_EALIGN;
+  if (residual != nullptr && !aligned16(residual)) return MOE_EALIGN;
+  if (!valid_path(path)) return MOE_EINVAL;
+  if ((st = check_ws(layer, n_tokens, workspace, workspace_bytes))) return st;
+  if ((st = check_device())) return st;
+  prof_begin(stream);
+  const int p = resolve_path(path, n_tokens);
+  if (p == MOE_PATH_GEMV && records_ready != nullptr)
+    return do_forward_gemv_after(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace,
+                                 records_ready, stream);
+  // MFMA paths (their shared experts share the routed launches) or no event:
+  // wait first, then the plain forward
+  if (records_ready != nullptr &&
+      (st = launched(hipStreamWaitEvent(stream, records_ready, 0), stream)))
+    return st;
   if (p != MOE_PATH_GEMV)
     return do_forward_mfma(layer, x, n_tokens, topk_ids, topk_w, residual, y, workspace,
                            act_format(p), stream);

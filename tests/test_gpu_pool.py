@@ -149,3 +149,49 @@ def test_pageable_host_records(b):
     pool.fetch(ids.cpu().numpy())
     np.testing.assert_array_equal(_forward(b, lay, xd, ids, w, b.PATH_GEMV),
                                   _forward(b, built.lib, xd, ids, w, b.PATH_GEMV))
+
+
+@pytest.mark.parametrize("path,T", [("gemv", 1), ("gemv", 3), ("mfma", 8)])
+def test_forward_pooled_waits_for_fetch_on_another_stream(b, path, T):
+    """The records are fetched on a second stream while the shared experts
+    run; the routed part waits for the event recorded after the fetch.  Each
+    call evicts records the previous one used (few slots), so a routed kernel
+    that ran before its copies landed would read another expert's record."""
+    cfg = RAGGED
+    built = Built(cfg, seed=36)
+    p = b.PATH_GEMV if path == "gemv" else b.PATH_MFMA
+    calls = []
+    for call in range(4):
+        xh, xd = SD.upload_tokens(3400 + 10 * T + call, T, cfg["hidden"])
+        calls.append((xh, xd, *_route(b, built, xd)))
+    n_slots = max(np.unique(ids.cpu().numpy()).size for _, _, ids, _ in calls)
+    pool, lay = _pooled(b, built, n_slots)
+    copy_stream = torch.cuda.Stream()  # default priority
+    main = torch.cuda.current_stream()
+    ws = lay.workspace(T)
+    copied_total = 0
+    for xh, xd, ids, w in calls:
+        ids_host = ids.cpu().numpy()
+        copy_stream.wait_stream(main)  # earlier reads of the slots come first
+        copied_total += pool.fetch(ids_host, stream=copy_stream)
+        ready = torch.cuda.Event()
+        ready.record(copy_stream)
+        y = torch.empty((T, cfg["hidden"]), dtype=torch.int16, device="cuda")
+        b.forward_pooled(lay, xd, ids, w, y, ws, ready, path=p)
+        torch.cuda.synchronize()
+        yn = to_np_u16(y)
+        np.testing.assert_array_equal(yn, _forward(b, built.lib, xd, ids, w, p))
+        _check_oracle(built, xh, ids, w, yn, mx=(b, lay, ws) if path == "mfma" else None)
+    assert copied_total > n_slots
+
+
+def test_forward_pooled_without_event_is_forward(b):
+    built = Built(synth.TINY, seed=37)
+    pool, lay = _pooled(b, built, 8)
+    xh, xd = SD.upload_tokens(3500, 2, 256)
+    ids, w = _route(b, built, xd)
+    pool.fetch(ids.cpu().numpy())
+    y = torch.empty((2, 256), dtype=torch.int16, device="cuda")
+    b.forward_pooled(lay, xd, ids, w, y, lay.workspace(2), None, path=b.PATH_GEMV)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np_u16(y), _forward(b, lay, xd, ids, w, b.PATH_GEMV))
