@@ -402,11 +402,17 @@ int n_quant_wgs(const moe::GemvLayer& G, int64_t T) { return int((T * (G.Kq / 32
 int n_token_tiles(int64_t T) { return int((T + 63) / 64); }
 // Grid of an XCD-ordered role over (pairs, token tiles): see xcd_split.
 int xcd_grid(int n_pairs, int64_t T) { return 8 * ((n_pairs + 7) / 8) * n_token_tiles(T); }
+// Grid of the prefill shared-expert role, two token tiles per workgroup
+// (see shared_mx_unit).
+int shared_mx_grid(int n_pairs, int64_t T) {
+  return 8 * ((n_pairs + 7) / 8) * ((n_token_tiles(T) + 1) / 2);
+}
 
 // Prefill experts once the plan and the MXFP8 x exist: routed gate/up
 // (scaled MFMA) + shared gate/up (bf16 MFMA); routed down -> per-pair
-// partials + shared down; combine.  Segments before an XCD-ordered role are
-// padded to multiples of 8 so its block index keeps the XCD of blockIdx.
+// partials + shared down; combine.  The GEMM launches run 8-wave
+// workgroups; the routed roles' blocks come first, so the shared tiles fill
+// the tail.
 // Blocks of a prefill GEMM launch over mt token tiles and tiles_r row tiles:
 // the XCD-grouped order of the launch (kMxGroup token tiles per XCD visit)
 // needs whole rounds of 8 groups.
@@ -418,13 +424,13 @@ int mx_blocks(int mt, int tiles_r) {
 int mfma_experts(const moe_layer_desc* L, const moe::GemvLayer& G, int64_t T, hipStream_t stream) {
   const int S = L->n_shared, mt = max_mtiles(L, T);
   moe::Stage s2;
-  s2.n_mgu = mx_blocks(mt, (L->inter + 127) / 128);
-  s2.n_sgmx = S > 0 ? xcd_grid(S * ((L->inter + 127) / 128), T) : 0;
+  s2.n_mgu = mx_blocks(mt, (L->inter + moe::kMxRowsGU - 1) / moe::kMxRowsGU);
+  s2.n_sgmx = S > 0 ? shared_mx_grid(S * ((L->inter + 127) / 128), T) : 0;
   int st = stage(moe::StageKind::MxGateUp, G, s2, stream);
   if (st) return st;
   moe::Stage s3;
-  s3.n_mdn = mx_blocks(mt, (L->hidden + 255) / 256);
-  s3.n_sdmx = S > 0 ? xcd_grid(S * ((L->hidden + 255) / 256), T) : 0;
+  s3.n_mdn = mx_blocks(mt, (L->hidden + moe::kMxRowsD - 1) / moe::kMxRowsD);
+  s3.n_sdmx = S > 0 ? shared_mx_grid(S * ((L->hidden + 255) / 256), T) : 0;
   if ((st = stage(moe::StageKind::MxDown, G, s3, stream))) return st;
   moe::Stage s4;
   s4.n_comb = int(T) * moe::combine_chunks(L->hidden);

@@ -55,13 +55,20 @@ __device__ __forceinline__ void load_to_lds16(const void* src, uint32_t lds_addr
                : "memory", "m0");
 }
 
+// The tile runs on a group of 4 waves: a 4-wave workgroup, or either half
+// of an 8-wave one (which then runs two tiles side by side; both halves go
+// through the same barriers).
+__device__ __forceinline__ int group_wave() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave % 4);
+}
+
 // Stages super-step kq of NB token sources (rows of K bf16) into NB LDS
 // buffers of kStageBytes: 17 wave-wide loads each, wave w issuing w, w + 4..
 // Chunks past K are loaded from the row's last chunk (valid memory) and
 // zeroed later by zero_tail.
 template <int NB, typename Row>
 __device__ __forceinline__ void stage_b(uint8_t* lds, int kq, int K, Row row) {
-  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const int wave = group_wave();
   const int lane = threadIdx.x % kWave;
   const int last = K / 8 - 1;  // last 16-byte chunk of a row
   const uint32_t l0 = uint32_t(reinterpret_cast<uintptr_t>((lvoid*)lds));
@@ -84,7 +91,7 @@ __device__ __forceinline__ void zero_tail(uint8_t* lds, int kq, int K) {
   if (valid >= kStepK) return;
   const int from = max(valid, 0) / 8;  // first 16-byte chunk to clear
   const int per_row = 16 - from;
-  for (int i = threadIdx.x; i < NB * kTok * per_row; i += kWave * 4) {
+  for (int i = threadIdx.x % (kWave * 4); i < NB * kTok * per_row; i += kWave * 4) {
     const int s = i / (kTok * per_row), r = i % (kTok * per_row);
     *reinterpret_cast<u32x4*>(lds + s * kStageBytes + (r / per_row) * kRowB +
                               16 * (from + r % per_row)) = u32x4{0, 0, 0, 0};

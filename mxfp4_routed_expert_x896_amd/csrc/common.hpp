@@ -143,7 +143,7 @@ struct Plan {
 };
 
 // Pairs per token tile of the prefill (MFMA) path.
-constexpr int kPlanTileTokens = 64;
+constexpr int kPlanTileTokens = 96;
 
 // floor(log2 |a|) of a non-zero finite fp32 (normal or subnormal).
 __device__ __forceinline__ int floor_log2_f32(float a) {

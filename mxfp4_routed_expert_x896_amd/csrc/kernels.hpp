@@ -45,6 +45,13 @@ constexpr int kRouterSplitMin = 5;
 __host__ __device__ inline int combine_chunks(int H) { return (H + 1023) / 1024; }
 // Consecutive prefill token tiles that one XCD runs side by side.
 constexpr int kMxGroup = 4;
+// Threads of a prefill routed-expert GEMM workgroup (8 waves; the other
+// launches use 4).
+constexpr int kMxThreads = 512;
+// Weight rows per prefill routed GEMM workgroup: gate/up takes 256 rows of
+// the intermediate dimension (of both matrices), down 512 rows of hidden.
+constexpr int kMxRowsGU = 256;
+constexpr int kMxRowsD = 512;
 
 // Everything the layer kernels need (layer.hip).
 struct GemvLayer {
@@ -149,8 +156,10 @@ enum class StageKind {
   RoutedDownCombine,   // roles: routed down + combine
   PlanQuantSharedGateUp,  // plan, x -> MXFP8 (prefill), shared gate/up (decode)
   RouterMxQuant,       // prefill: x -> MXFP8, router logits (MFMA)
-  MxGateUp,            // prefill: routed gate/up (scaled MFMA), shared gate/up (MFMA)
-  MxDown,              // prefill: routed down -> per-pair partials, shared down (MFMA)
+  MxGateUp,            // prefill (8-wave workgroups): routed gate/up (scaled MFMA), shared
+                       // gate/up (bf16 MFMA)
+  MxDown,              // prefill (8-wave workgroups): routed down -> per-pair partials,
+                       // shared down
   Combine,             // prefill: weighted combine of the partials
 };
 

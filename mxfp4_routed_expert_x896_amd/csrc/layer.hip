@@ -749,12 +749,12 @@ enum : unsigned {
   kRoleRoutedGU = 32u,    // routed gate/up, (active slot, 32 rows)
   kRoleRoutedDown = 64u,  // routed down, (active slot, kRowsD rows) + combine
   kRoleQuantX = 128u,     // prefill: x -> MXFP8 (256 blocks per workgroup)
-  kRoleMxGateUp = 256u,   // prefill: routed gate/up, (token tile, 128 rows)
-  kRoleMxDown = 512u,     // prefill: routed down, (token tile, 256 rows)
+  kRoleMxGateUp = 256u,   // prefill: routed gate/up, (token tile, 256 rows), 8 waves
+  kRoleMxDown = 512u,     // prefill: routed down, (token tile, 512 rows), 8 waves
   kRoleCombine = 1024u,   // prefill: combine, one token per workgroup
   kRoleRouterMx = 2048u,  // prefill: router logits, (256 experts, 64 tokens)
-  kRoleSharedGUMx = 4096u,    // prefill: shared gate/up, (expert, 128 rows, 64 tokens)
-  kRoleSharedDownMx = 8192u,  // prefill: shared down, (expert, 256 rows, 64 tokens)
+  kRoleSharedGUMx = 4096u,    // prefill: shared gate/up, 2 x (expert, 128 rows, 64 tokens)
+  kRoleSharedDownMx = 8192u,  // prefill: shared down, 2 x (expert, 256 rows, 64 tokens)
   kRoleSelectWait = 16384u,   // top-k of T <= 4 tokens once this launch's logits are flagged
 };
 
@@ -809,15 +809,34 @@ __device__ void router_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
   }
 }
 
-// Prefill shared gate/up: (shared expert, 128 rows of I, 64 tokens); wave w
-// takes row groups 2 w, 2 w + 1 of gate and up.  h = SiLU(g) * u leaves as
-// bf16 hi + lo, as on the decode path.
-__device__ void shared_gu_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
+// The shared-expert tiles of an 8-wave workgroup of the prefill GEMM
+// launches: each half (4 waves) takes one (weight slice, 64-token tile);
+// block b takes token tiles 2 i, 2 i + 1 of its slice (xcd_split over
+// half as many token tiles), so both halves read the same weights.  A half
+// without a tile repeats the other's and stores nothing (valid = false):
+// the halves share the workgroup's barriers.  lds: this half's buffers.
+__device__ __forceinline__ bool shared_mx_unit(int b, int n_pairs, int n_tt, int& pair, int& tt,
+                                               bool& valid) {
+  const int half = threadIdx.x / (kWave * 4);
+  int t2;
+  if (!xcd_split(b, n_pairs, (n_tt + 1) / 2, pair, t2)) return false;
+  tt = 2 * t2 + half;
+  valid = tt < n_tt;
+  tt = min(tt, n_tt - 1);
+  return true;
+}
+
+// Prefill shared gate/up: (shared expert, 128 rows of I, 64 tokens) per
+// half workgroup; wave w of the half takes row groups 2 w, 2 w + 1 of gate
+// and up.  h = SiLU(g) * u leaves as bf16 hi + lo, as on the decode path.
+__device__ __forceinline__ void shared_gu_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int n_rt = (L.I + 127) / 128, n_tt = (L.T + bf::kTok - 1) / bf::kTok;
   int pair, tt;
-  if (!xcd_split(b, L.S * n_rt, n_tt, pair, tt)) return;
+  bool valid;
+  if (!shared_mx_unit(b, L.S * n_rt, n_tt, pair, tt, valid)) return;
+  lds += (threadIdx.x / (kWave * 4)) * 2 * bf::kStageBytes;
   const int sx = pair / n_rt, rt = pair % n_rt;
-  const int wave = wave_id();
+  const int wave = bf::group_wave();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
   const int H = L.H, I = L.I;
@@ -833,7 +852,7 @@ __device__ void shared_gu_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
         return mats[s >> 1] + (size_t(rg) * nu + min(kt, nu - 1)) * 512 + 8 * lane;
       },
       H, lds, [&](int, int j) { return L.x + size_t(min(t0 + j, L.T - 1)) * H; });
-  if (rg0 >= ngroups) return;
+  if (rg0 >= ngroups || !valid) return;
   const size_t plane = size_t(L.S) * L.T * I;
 #pragma unroll
   for (int u = 0; u < bf::kSub; ++u) {
@@ -856,14 +875,16 @@ __device__ void shared_gu_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
   }
 }
 
-// Prefill shared down: (shared expert, 256 rows of H, 64 tokens); h enters
-// as its bf16 hi and lo parts (two token sources).
-__device__ void shared_down_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
+// Prefill shared down: (shared expert, 256 rows of H, 64 tokens) per half
+// workgroup; h enters as its bf16 hi and lo parts (two token sources).
+__device__ __forceinline__ void shared_down_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int n_rt = (L.H + 255) / 256, n_tt = (L.T + bf::kTok - 1) / bf::kTok;
   int pair, tt;
-  if (!xcd_split(b, L.S * n_rt, n_tt, pair, tt)) return;
+  bool valid;
+  if (!shared_mx_unit(b, L.S * n_rt, n_tt, pair, tt, valid)) return;
+  lds += (threadIdx.x / (kWave * 4)) * 4 * bf::kStageBytes;
   const int sx = pair / n_rt, rt = pair % n_rt;
-  const int wave = wave_id();
+  const int wave = bf::group_wave();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
   const int H = L.H, I = L.I;
@@ -882,6 +903,7 @@ __device__ void shared_down_mx_role(const GemvLayer& L, int b, uint8_t* lds) {
       I, lds, [&](int src, int j) {
         return L.hs + src * plane + (size_t(sx) * L.T + min(t0 + j, L.T - 1)) * I;
       });
+  if (!valid) return;
 #pragma unroll
   for (int u = 0; u < bf::kSub; ++u) {
     const int t = t0 + 16 * u + c;
@@ -989,12 +1011,12 @@ __device__ __forceinline__ bool mx_unit(const GemvLayer& L, int b, int tiles_r, 
   return mx_tile(L, kMxGroup * (b % 8 + 8 * (i / (kMxGroup * tiles_r))) + rem % kMxGroup, t);
 }
 
-// Prefill gate/up: workgroup = (token tile, 128 rows of I); wave w takes row
-// groups 2 w, 2 w + 1 of gate and up (4 A streams) against the tile's 64
-// tokens.  Epilogue: h = SiLU(g) * u in fp32, then MXFP8 along I -- the
-// wave's 32 rows are exactly one block per token.
-__device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
-  const int tiles_r = (L.I + 127) / 128;
+// Prefill gate/up: workgroup (8 waves) = (token tile, 256 rows of I); wave w
+// takes row groups 2 w, 2 w + 1 of gate and up (4 A streams) against the
+// tile's up to 128 tokens.  Epilogue: h = SiLU(g) * u in fp32, then MXFP8
+// (or MXFP4) along I -- the wave's 32 rows are exactly one block per token.
+__device__ __forceinline__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int tiles_r = (L.I + kMxRowsGU - 1) / kMxRowsGU;
   MxTile tt;
   int rt;
   if (!mx_unit(L, b, tiles_r, tt, rt)) return;
@@ -1005,18 +1027,21 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int e = L.plan.active[tt.a];
   const PackedMx pm(I, H);
   const int ngroups = I / 16;
-  const int rg0 = rt * 8 + 2 * wave;
+  const int rg0 = rt * (kMxRowsGU / 16) + 2 * wave;
   const uint8_t* rec = record_of(L, e);
   const uint8_t* base[2] = {rec, rec + pm.bytes};
   mx::AStreams st;
   st.nkb = pm.nkb;
+  st.nsup = pm.nkb4 / 4;
   st.lane_code = 16 * lane;
   st.lane_scl = lane * pm.nkb4;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
+    // the same in every lane: kept in SGPRs, so each weight load needs only
+    // the lane's 32-bit offset
     const int rg = min(rg0 + (s & 1), ngroups - 1);
-    st.codes[s] = base[s >> 1] + size_t(rg) * pm.nkb * 1024;
-    st.scl[s] = base[s >> 1] + pm.code_bytes + size_t(rg) * 64 * pm.nkb4;
+    st.codes[s] = mx::uniform_gptr(base[s >> 1] + size_t(rg) * pm.nkb * 1024);
+    st.scl[s] = mx::uniform_gptr(base[s >> 1] + pm.code_bytes + size_t(rg) * 64 * pm.nkb4);
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
@@ -1027,23 +1052,24 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   auto row = [&](int j) { return uint32_t(tok(j)) * uint32_t(xrow); };
   auto srow = [&](int j) { return uint32_t(tok(j)) * uint32_t(L.Kq / 32); };
   if (fp4)
-    mx::gemm_tile<mx::kFmtFp4>(acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs, row, srow);
+    mx::gemm_tile<mx::kFmtFp4>(acc, st, pm.nkb4 / 2, lds, tt.mt, L.xq, L.xs, row, srow);
   else
-    mx::gemm_tile<mx::kFmtFp8>(acc, st, pm.nkb4 / 4, lds, tt.mt, L.xq, L.xs, row, srow);
+    mx::gemm_tile<mx::kFmtFp8>(acc, st, pm.nkb4 / 2, lds, tt.mt, L.xq, L.xs, row, srow);
   if (rt == tiles_r - 1 && L.Iq > I) {
     // h columns I .. Iq are read by the down GEMM against clamped weight
     // tiles: zero codes with a finite exponent make them contribute 0
     const int pad_bytes = (fp4 ? (L.Iq - I) / 2 : L.Iq - I), hbase = fp4 ? I / 2 : I;
     const int pad16 = pad_bytes / 16, pad_blocks = (L.Iq - I) / 32;
-    for (int i = threadIdx.x; i < tt.mt * pad16; i += kThreads)
+    for (int i = threadIdx.x; i < tt.mt * pad16; i += kMxThreads)
       *reinterpret_cast<u32x4*>(L.hq + size_t(tt.p0 + i / pad16) * hrow_b + hbase +
                                 16 * (i % pad16)) = u32x4{0, 0, 0, 0};
-    for (int i = threadIdx.x; i < tt.mt * pad_blocks; i += kThreads)
+    for (int i = threadIdx.x; i < tt.mt * pad_blocks; i += kMxThreads)
       L.hs8[size_t(tt.p0 + i / pad_blocks) * (L.Iq / 32) +
             mx::scale_pos(I / 32 + i % pad_blocks)] = 127;
   }
   if (rg0 >= ngroups) return;  // no rows for this wave (I not a multiple of 128)
-  const int blk = (rt * 128 + 32 * wave) / 32;  // MX block of the wave's rows along I
+  const int r0 = rt * kMxRowsGU + 32 * wave;  // the wave's first row along I
+  const int blk = r0 / 32;                      // its MX block
 #pragma unroll
   for (int u = 0; u < mx::kSub; ++u) {
     float h[2][4];
@@ -1063,7 +1089,7 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
       const int pos = tt.p0 + j;  // h rows in plan order: a tile's rows are contiguous
       // lane (c, g) holds elements 16 r + 4 g .. + 3 of the wave's 32-row block
       if (fp4) {
-        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + (rt * 128 + 32 * wave) / 2;
+        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + r0 / 2;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           uint32_t half = 0;
@@ -1072,7 +1098,7 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
           *reinterpret_cast<uint16_t*>(hrow + 8 * r + 2 * g) = uint16_t(half);
         }
       } else {
-        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + rt * 128 + 32 * wave;
+        uint8_t* hrow = L.hq + size_t(pos) * hrow_b + r0;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           uint32_t word = 0;
@@ -1086,10 +1112,11 @@ __device__ void mx_gateup_role(const GemvLayer& L, int b, uint8_t* lds) {
   }
 }
 
-// Prefill down: workgroup = (token tile, 256 rows of H); wave w takes row
-// groups 4 w .. 4 w + 3.  Writes fp32 partials per pair (combined later).
-__device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
-  const int tiles_r = (L.H + 255) / 256;
+// Prefill down: workgroup (8 waves) = (token tile, 512 rows of H); wave w
+// takes row groups 4 w .. 4 w + 3.  Writes fp32 partials per pair (combined
+// later).
+__device__ __forceinline__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
+  const int tiles_r = (L.H + kMxRowsD - 1) / kMxRowsD;
   MxTile tt;
   int rt;
   if (!mx_unit(L, b, tiles_r, tt, rt)) return;
@@ -1100,17 +1127,18 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   const int e = L.plan.active[tt.a];
   const PackedMx pgu(I, H), pd(H, I);
   const int ngroups = H / 16;
-  const int rg0 = rt * 16 + 4 * wave;
+  const int rg0 = rt * (kMxRowsD / 16) + 4 * wave;
   const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
   mx::AStreams st;
   st.nkb = pd.nkb;
+  st.nsup = pd.nkb4 / 4;
   st.lane_code = 16 * lane;
   st.lane_scl = lane * pd.nkb4;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
     const int rg = min(rg0 + s, ngroups - 1);
-    st.codes[s] = base + size_t(rg) * pd.nkb * 1024;
-    st.scl[s] = base + pd.code_bytes + size_t(rg) * 64 * pd.nkb4;
+    st.codes[s] = mx::uniform_gptr(base + size_t(rg) * pd.nkb * 1024);
+    st.scl[s] = mx::uniform_gptr(base + pd.code_bytes + size_t(rg) * 64 * pd.nkb4);
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
@@ -1122,9 +1150,9 @@ __device__ void mx_down_role(const GemvLayer& L, int b, uint8_t* lds) {
   auto row = [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(hrow_b); };
   auto srow = [&](int j) { return uint32_t(min(j, tt.mt - 1)) * uint32_t(L.Iq / 32); };
   if (fp4)
-    mx::gemm_tile<mx::kFmtFp4>(acc, st, pd.nkb4 / 4, lds, tt.mt, hc, hs, row, srow);
+    mx::gemm_tile<mx::kFmtFp4>(acc, st, pd.nkb4 / 2, lds, tt.mt, hc, hs, row, srow);
   else
-    mx::gemm_tile<mx::kFmtFp8>(acc, st, pd.nkb4 / 4, lds, tt.mt, hc, hs, row, srow);
+    mx::gemm_tile<mx::kFmtFp8>(acc, st, pd.nkb4 / 2, lds, tt.mt, hc, hs, row, srow);
 #pragma unroll
   for (int u = 0; u < mx::kSub; ++u) {
     const int j = 16 * u + c;
@@ -1494,10 +1522,10 @@ __global__ __launch_bounds__(kThreads) void moe_plan_quant_shared_gateup(GemvLay
 __global__ __launch_bounds__(kThreads) void moe_router_mx_quant(GemvLayer L, Stage st) {
   stage_body<kRoleQuantX | kRoleRouterMx, 0>(L, st);
 }
-__global__ __launch_bounds__(kThreads) void moe_mx_gateup(GemvLayer L, Stage st) {
+__global__ __launch_bounds__(kMxThreads) void moe_mx_gateup(GemvLayer L, Stage st) {
   stage_body<kRoleMxGateUp | kRoleSharedGUMx, 0>(L, st);
 }
-__global__ __launch_bounds__(kThreads) void moe_mx_down(GemvLayer L, Stage st) {
+__global__ __launch_bounds__(kMxThreads) void moe_mx_down(GemvLayer L, Stage st) {
   stage_body<kRoleMxDown | kRoleSharedDownMx, 0>(L, st);
 }
 __global__ __launch_bounds__(kThreads) void moe_combine(GemvLayer L, Stage st) {
@@ -1523,14 +1551,18 @@ hipError_t launch_stage(StageKind kind, GemvLayer L, Stage st, hipStream_t strea
   if (st.n_logits > 0) lds = max(lds, size_t(kRouterTokens) * L.H * 2);
   if (st.n_rgu > 0) lds = max(lds, size_t(L.mtp_gu) * xrow * 2);
   if (st.n_rdn > 0) lds = max(lds, size_t(L.mtp_d) * hrow * 4);
-  if (st.n_mgu > 0 || st.n_mdn > 0) lds = max(lds, size_t(2 * mx::kStageBytes));
-  if (st.n_rmx > 0 || st.n_sgmx > 0) lds = max(lds, size_t(2 * bf::kStageBytes));
-  if (st.n_sdmx > 0) lds = max(lds, size_t(4 * bf::kStageBytes));
+  if (st.n_rmx > 0) lds = max(lds, size_t(2 * bf::kStageBytes));
+  if (st.n_sgmx > 0) lds = max(lds, size_t(2 * 2 * bf::kStageBytes));  // two halves
+  if (st.n_sdmx > 0) lds = max(lds, size_t(2 * 4 * bf::kStageBytes));
   const int wgs = st.n_logits + st.n_select + st.n_plan + st.n_sgu + st.n_sdn + st.n_rgu +
                   st.n_rdn + st.n_xq + st.n_mgu + st.n_mdn + st.n_comb + st.n_rmx + st.n_sgmx +
                   st.n_sdmx + st.n_selw;
   if (wgs <= 0) return hipSuccess;
-  const dim3 grid(wgs), block(kThreads);
+  if (st.n_mgu > 0 || st.n_mdn > 0)
+    lds = max(lds, size_t(L.afmt == mx::kFmtFp4 ? mx::lds_bytes<mx::kFmtFp4>()
+                                                 : mx::lds_bytes<mx::kFmtFp8>()));
+  const bool mx8 = kind == StageKind::MxGateUp || kind == StageKind::MxDown;
+  const dim3 grid(wgs), block(mx8 ? kMxThreads : kThreads);
   const LaunchEvents ev = next_launch_events();
   switch (kind) {
     case StageKind::RouterSharedGateUp: {

@@ -18,6 +18,8 @@ from tests._gpu import (Built, check_mxfp8_workspace, check_parity, check_routin
 
 pytestmark = pytest.mark.gpu
 
+PLAN_TILE = 96  # pairs of one expert per prefill token tile (the plan's tiles)
+
 
 @pytest.fixture(scope="module")
 def b():
@@ -123,7 +125,7 @@ def test_k3_prefill_4096_with_bias(b, k3):
     512 tokens; its h codes element by element for every pair of every
     expert the sampled tokens use; and the output of 32 or more
     tokens against the oracle in its MXFP8-activation mode -- every token of
-    the most loaded expert's last (ragged) 64-token tile, every token of
+    the most loaded expert's last (ragged) 96-token tile, every token of
     the least loaded expert and of one with about 3 pairs, the first and
     last token, and a spread."""
     from synth import router_bias
@@ -149,11 +151,11 @@ def test_k3_prefill_4096_with_bias(b, k3):
     assert per_expert.sum() == T * 16 and (per_expert > 0).all()
     busiest, idlest = int(per_expert.argmax()), int(per_expert.argmin())
     few = int(np.argmin(np.abs(per_expert - 3)))  # an expert with (about) 3 pairs
-    assert per_expert[busiest] % 64 != 0 and per_expert[few] <= 4
+    assert per_expert[busiest] % PLAN_TILE != 0 and per_expert[few] <= 4
     # the busiest expert's last tile: its last pairs in the plan's order
     pairs = b.workspace_region(lay, T, b.WS_PAIRS, ws).cpu().numpy().view(np.int32)
     grp = pairs[ids.reshape(-1)[pairs] == busiest]
-    last_tile = grp[(len(grp) - 1) // 64 * 64:] // 16
+    last_tile = grp[(len(grp) - 1) // PLAN_TILE * PLAN_TILE:] // 16
     small = np.nonzero(np.isin(ids, [idlest, few]).any(axis=1))[0]
     rng = np.random.default_rng(4)
     sample = set(last_tile.tolist()) | set(small.tolist()) | {0, T - 1}

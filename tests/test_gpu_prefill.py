@@ -65,7 +65,7 @@ def test_mfma_forward_matches_oracle_mxfp8(b, cfg, T):
 
 
 def test_mfma_skewed_routing_many_tiles_per_expert(b):
-    # every token picks experts 0..3: 300 pairs per expert, five 64-token tiles each
+    # every token picks experts 0..3: 300 pairs per expert, four 96-token tiles each (the last ragged)
     built = Built(MID, seed=22)
     T = 300
     xh, xd = SD.upload_tokens(1450, T, MID["hidden"])
@@ -100,7 +100,7 @@ def test_mfma_residual_and_layer_entry(b):
 
 @pytest.mark.parametrize("path", ["mfma", "gemv"])
 def test_layer_at_the_token_limit(b, path):
-    # 65,536 tokens, the most one call takes (about 128 64-token tiles per
+    # 65,536 tokens, the most one call takes (about 85 96-token tiles per
     # expert at the tiny shape), on either path; routing and output checked
     # on a sample of tokens spread over the batch, the first and last included
     cfg = synth.TINY

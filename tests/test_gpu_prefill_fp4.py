@@ -62,7 +62,7 @@ def test_fp4_forward_matches_oracle(b, cfg, T):
 
 
 def test_fp4_skewed_routing_many_tiles_per_expert(b):
-    # every token picks experts 0..3: 300 pairs per expert, five 64-token tiles each
+    # every token picks experts 0..3: 300 pairs per expert, four 96-token tiles each (the last ragged)
     built = Built(MID, seed=82)
     T = 300
     xh, xd = SD.upload_tokens(8200, T, MID["hidden"])
