@@ -40,11 +40,11 @@
  *           byte (rg nkb + kb) 1024; its bytes 16 l .. 16 l + 15 hold the
  *           codes of block 4 kb + l/16 of row 16 rg + l%16 (zero codes past
  *           block nb);
- *   scales: after the codes; byte (rg 64 + l) nkb4 + kb is that block's
- *           E8M0 exponent (127 past block nb).
+ *   scales: after the codes; byte ((rg nkb4/4 + kb/4) 64 + l) 4 + kb%4 is
+ *           that block's E8M0 exponent (127 past block nb).
  * A wave64 reads one tile as 1 KiB of contiguous codes in which lane l holds
- * exactly its MFMA operand, and a lane's exponents for four consecutive
- * tiles as one dword.  A record is gate, up, down matrices back to back;
+ * exactly its MFMA operand, and the exponents of four consecutive tiles (a
+ * super-step) as 256 contiguous bytes, one dword per lane.  A record is gate, up, down matrices back to back;
  * same size as the canonical record when K is a multiple of 512
  * (17,547,264 bytes at K3 shape).  bf16 shared matrices are packed into
  * 1 KiB tiles of 16 rows x 32 columns (lane l: row 16 rg + l%16, columns

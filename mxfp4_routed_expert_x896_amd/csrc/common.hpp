@@ -115,18 +115,25 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // ------------------------------------------------------------- layout -----
 // MFMA-tiled MXFP4 matrix (written by the pack kernels, see pack.hip): code
-// tiles of 16 rows x 128 columns (1 KiB, lane order), then the scales, lane
-// by lane, nkb4 bytes each.
+// tiles of 16 rows x 128 columns (1 KiB, lane order), then the scales: per
+// row group and super-step (4 tiles), 64 lane dwords (256 contiguous bytes),
+// lane l's dword holding its four tiles' exponents.
 struct PackedMx {
   int nb, nkb, nkb4;   // blocks per row, 128-column tiles per row group, nkb rounded to 4
+  int nsup;            // super-steps per row group (nkb4 / 4)
   size_t code_bytes;   // offset of the scales
   size_t bytes;        // whole matrix
   __host__ __device__ PackedMx(int R, int K) {
     nb = K / 32;
     nkb = (nb + 3) / 4;
     nkb4 = (nkb + 3) / 4 * 4;
+    nsup = nkb4 / 4;
     code_bytes = size_t(R / 16) * nkb * 1024;
     bytes = code_bytes + size_t(R / 16) * 64 * nkb4;
+  }
+  // byte offset of lane l's exponent dword of super-step q of row group rg
+  __host__ __device__ size_t scale_dword(int rg, int q, int l) const {
+    return code_bytes + ((size_t(rg) * nsup + q) * 64 + l) * 4;
   }
 };
 

@@ -262,8 +262,8 @@ __device__ __forceinline__ void load_gu(GuTiles& t, const uint8_t* gcodes, const
     t.g[j] = ld_nt(gcodes + size_t(kb) * 1024 + 16 * lane);
     t.u[j] = ld_nt(ucodes + size_t(kb) * 1024 + 16 * lane);
   }
-  t.sg = *reinterpret_cast<const uint32_t*>(gscl + 4 * kq);
-  t.su = *reinterpret_cast<const uint32_t*>(uscl + 4 * kq);
+  t.sg = *reinterpret_cast<const uint32_t*>(gscl + 256 * kq);
+  t.su = *reinterpret_cast<const uint32_t*>(uscl + 256 * kq);
 }
 
 __device__ __forceinline__ void mma_gu(const GuTiles& t, const uint16_t* xrow, int kq, int g,
@@ -379,8 +379,8 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
   const uint8_t* ubase = gbase + pm.bytes;
   const uint8_t* gcodes = gbase + size_t(rg) * pm.nkb * 1024;
   const uint8_t* ucodes = ubase + size_t(rg) * pm.nkb * 1024;
-  const uint8_t* gscl = gbase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
-  const uint8_t* uscl = ubase + pm.code_bytes + (size_t(rg) * 64 + lane) * pm.nkb4;
+  const uint8_t* gscl = gbase + pm.scale_dword(rg, 0, lane);
+  const uint8_t* uscl = ubase + pm.scale_dword(rg, 0, lane);
   const int xstride = pad_k(H) + 8;
 
   for (int t0 = p0; t0 < p1; t0 += L.mtp_gu) {
@@ -591,7 +591,7 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   const int nsteps = nrg * nkq;
   const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
   const uint8_t* codes = base + size_t(rg0) * pd.nkb * 1024 + 16 * lane;
-  const uint8_t* scl = base + pd.code_bytes + (size_t(rg0) * 64 + lane) * pd.nkb4;
+  const uint8_t* scl = base + pd.scale_dword(rg0, 0, lane);
   const int hstride = pad_k(I) + 8;
   auto load = [&](DnTiles& t, int s) {
     const int r = s / nkq, kq = s - r * nkq;
@@ -599,7 +599,7 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       t.w[j] = ld_nt(cr + size_t(min(4 * kq + j, pd.nkb - 1)) * 1024);
-    t.sc = *reinterpret_cast<const uint32_t*>(scl + size_t(r) * kWaves * 64 * pd.nkb4 + 4 * kq);
+    t.sc = *reinterpret_cast<const uint32_t*>(scl + size_t(r) * kWaves * pd.nsup * 256 + 256 * kq);
   };
 
   for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
@@ -1032,16 +1032,16 @@ __device__ __forceinline__ void mx_gateup_role(const GemvLayer& L, int b, uint8_
   const uint8_t* base[2] = {rec, rec + pm.bytes};
   mx::AStreams st;
   st.nkb = pm.nkb;
-  st.nsup = pm.nkb4 / 4;
+  st.nsup = pm.nsup;
   st.lane_code = 16 * lane;
-  st.lane_scl = lane * pm.nkb4;
+  st.lane_scl = 4 * lane;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
     // the same in every lane: kept in SGPRs, so each weight load needs only
     // the lane's 32-bit offset
     const int rg = min(rg0 + (s & 1), ngroups - 1);
     st.codes[s] = mx::uniform_gptr(base[s >> 1] + size_t(rg) * pm.nkb * 1024);
-    st.scl[s] = mx::uniform_gptr(base[s >> 1] + pm.code_bytes + size_t(rg) * 64 * pm.nkb4);
+    st.scl[s] = mx::uniform_gptr(base[s >> 1] + pm.scale_dword(rg, 0, 0));
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);
@@ -1131,14 +1131,14 @@ __device__ __forceinline__ void mx_down_role(const GemvLayer& L, int b, uint8_t*
   const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
   mx::AStreams st;
   st.nkb = pd.nkb;
-  st.nsup = pd.nkb4 / 4;
+  st.nsup = pd.nsup;
   st.lane_code = 16 * lane;
-  st.lane_scl = lane * pd.nkb4;
+  st.lane_scl = 4 * lane;
 #pragma unroll
   for (int s = 0; s < mx::kNS; ++s) {
     const int rg = min(rg0 + s, ngroups - 1);
     st.codes[s] = mx::uniform_gptr(base + size_t(rg) * pd.nkb * 1024);
-    st.scl[s] = mx::uniform_gptr(base + pd.code_bytes + size_t(rg) * 64 * pd.nkb4);
+    st.scl[s] = mx::uniform_gptr(base + pd.scale_dword(rg, 0, 0));
   }
   __shared__ int pairs[mx::kTok];
   load_tile_pairs(L, tt, pairs);

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void dequant_export_kernel(const uint8_t* __re
   if (bi >= pm.nb) return;
   const int row = rg * 16 + l % 16;
   const u32x4 codes = *reinterpret_cast<const u32x4*>(mat + tile * 1024 + 16 * l);
-  const float sc = e8m0_to_f32(mat[pm.code_bytes + (size_t(rg) * 64 + l) * pm.nkb4 + kb]);
+  const float sc = e8m0_to_f32(mat[pm.scale_dword(rg, kb / 4, l) + kb % 4]);
   float* o = out + size_t(row) * cols + size_t(bi) * 32;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {

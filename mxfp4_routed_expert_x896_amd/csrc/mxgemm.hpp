@@ -122,10 +122,10 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>((uint64_t(hi) << 32) | lo);
 }
 
-// Streams of a wave: code tiles of a 16-row group and the lane's exponent
-// bytes (nkb4 per lane, tile kb at byte kb).  The stream bases are uniform
+// Streams of a wave: code tiles of a 16-row group and its exponent dwords
+// (per super-step 64 lane dwords, 256 bytes).  The stream bases are uniform
 // across the wave; the lane's part is a 32-bit offset shared by all streams
-// (16 lane into a code tile, lane nkb4 into the exponents).
+// (16 lane into a code tile, 4 lane into a super-step's exponents).
 struct AStreams {
   const gbyte* codes[kNS];
   const gbyte* scl[kNS];
@@ -145,7 +145,7 @@ __device__ __forceinline__ u32x4 a_tile(const AStreams& st, int s, int kb) {
 }
 // Exponent dword of super-step q (tiles 4 q .. 4 q + 3) of stream s.
 __device__ __forceinline__ uint32_t a_exps(const AStreams& st, int s, int q) {
-  uint32_t off = 4 * uint32_t(min(q, st.nsup - 1)) + st.lane_scl;
+  uint32_t off = 256 * uint32_t(min(q, st.nsup - 1)) + st.lane_scl;
   asm volatile("" : "+v"(off));
   return *reinterpret_cast<gu32*>(st.scl[s] + off);
 }

@@ -6,11 +6,12 @@
 //   codes: tile (rg, kb), rg < R / 16, kb < nkb, is 1024 contiguous bytes at
 //     (rg * nkb + kb) * 1024; bytes [16 l, 16 l + 16), l = 16 g + c, are the
 //     codes of block 4 kb + g of row 16 rg + c (zeros past the last block);
-//   scales: after the codes, byte (rg * 64 + l) * nkb4 + kb is that block's
-//     E8M0 scale (127 past the last block).
+//   scales: after the codes, byte ((rg * nkb4 / 4 + kb / 4) * 64 + l) * 4 +
+//     kb % 4 is that block's E8M0 scale (127 past the last block).
 // One wave64 load of a tile is 1 KiB of contiguous codes whose lane l holds
 // exactly the 32 elements the MFMA A operand of lane l needs; a lane's
-// scales for four consecutive tiles are one aligned dword.
+// scales for four consecutive tiles (a super-step) are one aligned dword,
+// and the 64 lanes' dwords of a super-step are 256 contiguous bytes.
 //
 // bf16 matrix, R rows (multiple of 16) x K columns (multiple of 32):
 //   tile (rg, u) for u < K / 32 is 1024 contiguous bytes; lane l = 16 g + c
@@ -47,9 +48,10 @@ __global__ __launch_bounds__(256) void pack_mxfp4_kernel(const uint8_t* __restri
   }
   *reinterpret_cast<u32x4*>(dst + tile * 1024 + 16 * l) = v;
   uint8_t* sc = dst + size_t(R / 16) * nkb * 1024;
-  sc[(size_t(rg) * 64 + l) * nkb4 + kb] = s;
+  const size_t row_sc = size_t(rg) * (nkb4 / 4) * 256 + 4 * l;  // lane l's dwords, 256 apart
+  sc[row_sc + size_t(kb / 4) * 256 + kb % 4] = s;
   if (kb == nkb - 1)  // padding scales of the row group's last dword
-    for (int k2 = nkb; k2 < nkb4; ++k2) sc[(size_t(rg) * 64 + l) * nkb4 + k2] = 127;
+    for (int k2 = nkb; k2 < nkb4; ++k2) sc[row_sc + size_t(k2 / 4) * 256 + k2 % 4] = 127;
 }
 
 __global__ __launch_bounds__(256) void pack_bf16_kernel(const uint16_t* __restrict__ src, int R,
