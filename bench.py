@@ -114,6 +114,7 @@ def parse():
 
 # dominant launch per config: (HIP kernel name in traces, name in kernel_us)
 PMC_KERNELS = {"b1": ("moe_decode_front", "decode_front"),
+               "prefill": ("moe_mx_gateup", "mx_gateup"),
                "int8_dequant": ("int8_row_dequant_kernel", "int8_row_dequant")}
 
 
@@ -128,16 +129,20 @@ def pmc_summary(args, out_dir=None):
 
     def per_kernel(path, counter):
         d = collections.defaultdict(list)
+        copies = []  # (dispatch id, value) of the device copies
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] == counter:
                 d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return d
-    f = per_kernel(args.pmc_summary[0], "FETCH_SIZE")
-    w = per_kernel(args.pmc_summary[1], "WRITE_SIZE")
+                if "copyBuffer" in r["Kernel_Name"]:
+                    copies.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        # the calibration: the run's last three copies (1 GiB each; set-up
+        # copies of other sizes come earlier)
+        calib = float(np.median([v for _, v in sorted(copies)[-3:]]))
+        return d, calib
+    f, calib_f = per_kernel(args.pmc_summary[0], "FETCH_SIZE")
+    w, calib_w = per_kernel(args.pmc_summary[1], "WRITE_SIZE")
     kf = [k for k in f if ksub in k and "copyBuffer" not in k]
     assert len(kf) == 1, kf
-    calib_f = max(max(v) for k, v in f.items() if "copyBuffer" in k)
-    calib_w = max(max(v) for k, v in w.items() if "copyBuffer" in k)
     copy_kib = (1 << 30) / 1024
     fs, wsc = copy_kib / calib_f, copy_kib / calib_w
     fetch = float(np.mean(f[kf[0]]))
@@ -145,6 +150,8 @@ def pmc_summary(args, out_dir=None):
     if args.config == "int8_dequant":
         c = CONFIGS["int8_dequant"]
         alg = c["rows"] * c["cols"] * 5 + c["rows"] * 4
+    elif args.config == "prefill":  # 4096 tokens; every expert active at this routing
+        alg = kernel_bytes(name, CONFIGS["prefill"]["tokens"], 16, 896, 2)
     else:
         alg = kernel_bytes(name, 1, 16, 16, 2)
     out = {"kernel": ksub, "bench_name": name, "config": args.config,
