@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION ((2u << 16) | 3u)
+#define MOE_ABI_VERSION ((3u << 16) | 0u)
 
 /* status codes */
 #define MOE_OK 0

@@ -15,7 +15,7 @@ import torch  # noqa: F401  (loads the HIP runtime the library links against)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
 
-ABI_MAJOR = 2
+ABI_MAJOR = 3
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_ESHAPE",

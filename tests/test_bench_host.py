@@ -13,23 +13,28 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _csv(path, counter, rows):
+    """rows: (kernel name, value) in dispatch order."""
     with open(path, "w", newline="") as fh:
-        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(fh, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                           "Counter_Value"])
         w.writeheader()
-        for k, vals in rows.items():
-            for v in vals:
-                w.writerow({"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
+        for i, (k, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": k, "Counter_Name": counter,
+                        "Counter_Value": v})
 
 
 def test_pmc_summary_scales_by_the_copy_calibration(tmp_path):
-    # a 1 GiB copy reads 1 GiB and writes 1 GiB; here the fetch counter shows
-    # half of it (factor 2), the write counter all of it (factor 1)
+    # the run ends with three 1 GiB copies (1 GiB read and written each);
+    # here the fetch counter shows half of it (factor 2), the write counter
+    # all of it (factor 1).  A larger set-up copy earlier in the run is not
+    # the calibration.
     kib = (1 << 30) / 1024
+    kern, copy = "moe::int8_row_dequant_kernel(...)", "__amd_rocclr_copyBuffer"
     f, w = tmp_path / "f.csv", tmp_path / "w.csv"
-    _csv(f, "FETCH_SIZE", {"moe::int8_row_dequant_kernel(...)": [1000.0, 1200.0],
-                           "__amd_rocclr_copyBuffer": [kib / 2, 10.0]})
-    _csv(w, "WRITE_SIZE", {"moe::int8_row_dequant_kernel(...)": [4000.0, 4000.0],
-                           "__amd_rocclr_copyBuffer": [kib]})
+    _csv(f, "FETCH_SIZE", [(copy, 20 * kib), (kern, 1000.0), (kern, 1200.0),
+                           (copy, kib / 2), (copy, kib / 2), (copy, kib / 2 + 8)])
+    _csv(w, "WRITE_SIZE", [(copy, 40 * kib), (kern, 4000.0), (kern, 4000.0),
+                           (copy, kib), (copy, kib), (copy, kib)])
     args = argparse.Namespace(config="int8_dequant", pmc_summary=[str(f), str(w)])
     out = bench.pmc_summary(args, out_dir=str(tmp_path))
     assert out["calibration"]["fetch_scale"] == 2.0 and out["calibration"]["write_scale"] == 1.0
