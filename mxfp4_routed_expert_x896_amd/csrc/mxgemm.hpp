@@ -25,17 +25,17 @@
 // bytes ordered [g][j] (block 16 kq + 4 j + g at byte 4 g + j), so lane g's
 // dword holds its four tiles' exponents.
 //
-// Work split: a workgroup of 8 waves takes one token tile (up to 128 tokens
-// of one expert) and 8 x 4 row groups of 16 weight rows; each wave keeps 4
-// row groups x 8 token groups of fp32 accumulators (128 registers) and
-// streams its own weight tiles into registers, while the tile's activation
-// codes and exponents are staged in LDS for all waves.  Per 16x16x128 MFMA
-// that is 192 bytes brought into the CU (a 64-token, 4-wave tile needed
-// 384), which is what lets the matrix cores outrun the L2 and memory
-// traffic.  The contraction advances in steps of two MFMA tiles (256
-// columns): weight tiles are double-buffered in registers and requested two
-// steps ahead, activations are triple-buffered in LDS and staged two steps
-// ahead, so every load has about two steps (128 MFMAs per SIMD) to arrive.
+// Work split: a workgroup of 8 waves takes one token tile (up to kTok = 96
+// tokens of one expert) and 8 x 4 row groups of 16 weight rows; each wave
+// keeps 4 row groups x 6 token groups of fp32 accumulators (96 registers)
+// and streams its own weight tiles into registers, while the tile's
+// activation codes and exponents are staged in LDS for all waves.  Per
+// 16x16x128 MFMA that is 235 bytes brought into the CU (a 64-token, 4-wave
+// tile needed 384).  The contraction advances in steps of two MFMA tiles
+// (256 columns): weight tiles are double-buffered in registers and
+// requested two steps ahead, activations are triple-buffered in LDS and
+// staged two steps ahead, so every load has about two steps (96 MFMAs per
+// SIMD for a full tile) to arrive.
 #pragma once
 
 #include "common.hpp"
