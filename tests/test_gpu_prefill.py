@@ -65,7 +65,8 @@ def test_mfma_forward_matches_oracle_mxfp8(b, cfg, T):
 
 
 def test_mfma_skewed_routing_many_tiles_per_expert(b):
-    # every token picks experts 0..3: 300 pairs per expert, four 96-token tiles each (the last ragged)
+    # every token picks experts 0..3: 300 pairs per expert, four 96-token
+    # tiles each (the last ragged)
     built = Built(MID, seed=22)
     T = 300
     xh, xd = SD.upload_tokens(1450, T, MID["hidden"])
@@ -76,6 +77,43 @@ def test_mfma_skewed_routing_many_tiles_per_expert(b):
     y, ws = _forward(b, built, xd, ids, w)
     ref = M.moe_forward(xh, built.oracle, ids, w.astype(np.float64), act_mxfp8=True)
     check_parity(y, ref, check_mxfp8_workspace(b, built.lib, ws, T, xh, ids, w, built.oracle))
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["mxfp8", "mxfp4"])
+def test_mfma_token_tile_boundaries(b, fp4):
+    """Experts with 1, 15, 16, 17, 95, 96, 97, 192 and 193 pairs: tiles of
+    one to six 16-token groups, a tile exactly full, one pair past a full
+    tile, two full tiles and one past them (plan tiles of 96 pairs)."""
+    built = Built(MID, seed=26)
+    counts = [1, 15, 16, 17, 95, 96, 97, 192, 193]
+    k = MID["top_k"]
+    # 204 tokens x 4 slots = 816 pairs; expert e < 9 gets counts[e] of them,
+    # the rest go to experts 9..15, each token's slots distinct
+    T = 204
+    pool = np.concatenate([np.full(c, e) for e, c in enumerate(counts)])
+    rest = T * k - pool.size
+    pool = np.concatenate([pool, 9 + np.arange(rest) % 7])
+    # slot j of token t takes pair j T + t of the expert-sorted list: no
+    # expert has more than T pairs, so a token's slots are distinct
+    ids = np.ascontiguousarray(pool.reshape(k, T).T, dtype=np.int32)
+    rng = np.random.default_rng(8)
+    assert all(len(set(r)) == k for r in ids)
+    got = np.bincount(ids.ravel(), minlength=MID["n_experts"])
+    assert list(got[:9]) == counts
+    w = rng.random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    xh, xd = SD.upload_tokens(1470 + fp4, T, MID["hidden"])
+    idt = torch.from_numpy(ids).cuda()
+    wt = torch.from_numpy(w).cuda()
+    y = torch.empty((T, MID["hidden"]), dtype=torch.int16, device="cuda")
+    ws = built.lib.workspace(T)
+    b.forward(built.lib, xd, idt, wt, y, ws, path=b.PATH_MFMA_FP4 if fp4 else b.PATH_MFMA)
+    torch.cuda.synchronize()
+    ref = M.moe_forward(xh, built.oracle, ids, w.astype(np.float64), act_mxfp8=not fp4,
+                        act_mxfp4=fp4)
+    eff = check_mxfp8_workspace(b, built.lib, ws, T, xh, ids, w, built.oracle,
+                                fmt="e2m1" if fp4 else "e4m3")
+    check_parity(to_np_u16(y), ref, eff)
 
 
 def test_mfma_residual_and_layer_entry(b):
