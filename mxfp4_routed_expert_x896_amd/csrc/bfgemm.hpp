@@ -98,6 +98,17 @@ __device__ __forceinline__ void zero_tail(uint8_t* lds, int kq, int K) {
   }
 }
 
+// A weight tile load; the address passes through an empty asm statement so
+// that two requests of the same (clamped) tile stay two loads: the counted
+// wait at the end of a step depends on the number of loads issued after the
+// staging.
+template <typename AAddr>
+__device__ __forceinline__ u32x4 a_load(AAddr a, int s, int kt) {
+  const void* p = a(s, kt);
+  asm volatile("" : "+v"(p));
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // A super-step of weights: a(s, kt) is the lane's 16-byte address of
 // stream s, k-tile kt (already clamped to the valid tiles by the caller).
 template <typename AAddr>
@@ -106,7 +117,7 @@ __device__ __forceinline__ void load_a(ATiles& t, AAddr a, int kq) {
   for (int s = 0; s < kNS; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      t.w[s][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a(s, 4 * kq + j)));
+      t.w[s][j] = a_load(a, s, 4 * kq + j);
 }
 
 // s_waitcnt vmcnt(16) with expcnt and lgkmcnt left alone (gfx9 encoding:
@@ -167,8 +178,7 @@ __device__ __forceinline__ void gemm_tile(f32x4 (&acc)[kNS][kSub], AAddr a, int 
       if constexpr (kReload) {
 #pragma unroll
         for (int s = 0; s < kNS; ++s)
-          at.w[s][j] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(a(s, 4 * (kq + 1) + j)));
+          at.w[s][j] = a_load(a, s, 4 * (kq + 1) + j);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
