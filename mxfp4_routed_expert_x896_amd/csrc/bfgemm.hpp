@@ -98,15 +98,14 @@ __device__ __forceinline__ void zero_tail(uint8_t* lds, int kq, int K) {
   }
 }
 
-// A weight tile load; the address passes through an empty asm statement so
-// that two requests of the same (clamped) tile stay two loads: the counted
-// wait at the end of a step depends on the number of loads issued after the
-// staging.
+// A weight tile load; the k-tile index passes through an empty asm
+// statement so that two requests of the same (clamped) tile stay two loads:
+// the counted wait at the end of a step depends on the number of loads
+// issued after the staging.  (kt is the same in every lane: a scalar.)
 template <typename AAddr>
 __device__ __forceinline__ u32x4 a_load(AAddr a, int s, int kt) {
-  const void* p = a(s, kt);
-  asm volatile("" : "+v"(p));
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  asm volatile("" : "+s"(kt));
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a(s, kt)));
 }
 
 // A super-step of weights: a(s, kt) is the lane's 16-byte address of
