@@ -43,8 +43,8 @@ REC_BYTES = 3 * MAT_BYTES                          # one expert: 17,547,264 B
 SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 # kernels of one moe_layer call, in launch order (see moe_profile_events)
 KERNELS_GEMV = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
-# one token: router, top-k, shared experts and routed gate/up in one launch
-KERNELS_GEMV_ONE = ["decode_front", "routed_down_combine"]
+# one token: the whole layer in one launch
+KERNELS_GEMV_ONE = ["decode_front"]
 # 2 to 4 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
 KERNELS_GEMV_SMALL = ["router_shared_gateup_topk", "shared_down_routed_gateup", "routed_down_combine"]
 KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
@@ -263,10 +263,11 @@ def kernel_bytes(name, T, k, D, S, H=7168, I=1536, E=896):
                 + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
     if name == "routed_down_combine":
         return D * MAT_BYTES + T * k * I * 4 + T * k * 4 + S * T * H * 4 + x
-    if name == "decode_front":  # router + top-k + shared experts + routed gate/up
+    if name == "decode_front":  # the whole one-token layer: the three-launch sum
         return (kernel_bytes("router_shared_gateup_topk", T, k, D, S, H, I, E)
                 + D * 2 * MAT_BYTES + T * k * 4 + T * k * I * 4
-                + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4)
+                + S * SHARED_MAT_BYTES + S * T * I * 4 + S * T * H * 4
+                + kernel_bytes("routed_down_combine", T, k, D, S, H, I, E))
     # prefill (MFMA) path; MXFP8 rows are padded to multiples of 512 (exact at K3)
     xq = T * H * (1 + 1 / 32)
     hq = T * k * I * (1 + 1 / 32)

@@ -137,7 +137,7 @@ unsigned long long next_epoch() {
 
 // Workspace layout for T tokens.
 struct Carve {
-  uint64_t status, lflags, idsflag, sgflags, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
+  uint64_t status, lflags, idsflag, sgflags, guflags, idtag, logits, n_active, active, act_off, pairs, h, hs, part, ysh, tile_cnt, sel_cnt;
   uint64_t n_mtiles, mtiles, xq, xs, hq, hs8, total;
 };
 
@@ -155,6 +155,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
   c.lflags = take(uint64_t(n_logit_wgs(L)) * 8);
   c.idsflag = take(8);
   c.sgflags = take(S * (I / 16) * 8);
+  c.guflags = take((T == 1 ? k * (I / 32) : 1) * 8);  // one token: routed gate/up flags
+  c.idtag = take(k * 8);
   c.logits = take(t * E * 4 * (T >= moe::kRouterSplitMin ? moe::kRouterSplit : 1));
   c.n_active = take(4);
   c.active = take(E * 4);
@@ -214,6 +216,8 @@ moe::GemvLayer gemv_layer(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   G.status = at<unsigned long long>(ws, c.status);
   G.idsflag = at<unsigned long long>(ws, c.idsflag);
   G.sgflags = at<unsigned long long>(ws, c.sgflags);
+  G.guflags = at<unsigned long long>(ws, c.guflags);
+  G.idtag = at<unsigned long long>(ws, c.idtag);
   G.epoch = next_epoch();
   G.spin_limit = g_wait_limit;
   G.lsplit = 1;
@@ -351,22 +355,16 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   s1.n_logits = n_router_wgs(L, T);
   s1.n_sgu = S * (L->inter / 16);
   if (T == 1) {
-    // one token: router, top-k, shared experts and routed gate/up in one
-    // launch whose workgroups wait on flags of earlier blocks
-    // (moe_decode_front); no plan (direct mode); then the routed down and the
-    // combine
+    // one token: the whole layer in one launch whose workgroups wait on
+    // flags of earlier blocks (moe_decode_front); no plan (direct mode)
     G.direct = 1;
     G.front = 1;
     s1.n_selw = 1;
     s1.plan_after_select = 1;
     s1.n_rgu = ma * tiles_gu;
     s1.n_sdn = S * n_shared_tiles(L);
-    int st = stage(moe::StageKind::DecodeFront, G, s1, stream);
-    if (st) return st;
-    G.front = 0;
-    moe::Stage s4;
-    s4.n_rdn = ma * n_tiles(L);
-    return stage(moe::StageKind::RoutedDownCombine, G, s4, stream);
+    s1.n_rdn = ma * ((L->hidden + moe::kFrontDownRows - 1) / moe::kFrontDownRows);
+    return stage(moe::StageKind::DecodeFront, G, s1, stream);
   }
   if (n_select_wgs(T) == 1) {
     // 2 to 4 tokens: the top-k and the plan run in the router launch, on one

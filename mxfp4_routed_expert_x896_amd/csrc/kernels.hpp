@@ -36,6 +36,10 @@ constexpr long kDefaultSpinLimit = 1l << 20;
 // Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
+// Routed down rows per workgroup when the down runs in the one-token front
+// launch (half as many workgroups, each wave streams twice as long).
+constexpr int kFrontDownRows = 256;
+static_assert(kFrontDownRows % kDownRows == 0, "front tiles count on the same counters");
 // Router logits of kRouterSplitMin or more tokens (GEMV path: the batches
 // whose top-k has a launch of its own): bf16 MFMA over kRouterSplit quarters
 // of the contraction, one workgroup per (16 experts, quarter).
@@ -101,16 +105,24 @@ struct GemvLayer {
   float* part;              // fp32 [T*k][H]   routed expert outputs per pair
   float* ysh;               // fp32 [S][T][H]  shared expert outputs
   int* tile_cnt;            // [n_tiles] routed down arrivals per output tile (zeroed by
-                            // the plan builder of the same call)
-  // One-token decode front (moe_decode_front: router, top-k, shared experts
-  // and routed gate/up in one launch): the top-k stores `epoch` into
-  // *idsflag once its ids and weights are stored, which the routed gate/up
-  // workgroups wait for; each shared gate/up workgroup stores it into
-  // sgflags[sx * I/16 + rg] once its h rows are stored, which the shared
-  // down workgroups of expert sx wait for.
+                            // the plan builder, for one token the top-k, of the call)
+  // One-token decode (moe_decode_front: the whole layer in one launch).
+  // The top-k, once its ids, weights and cleared arrival counters are
+  // stored, stores idtag[a] = (epoch mod 2^48) << 16 | expert of slot a
+  // (E <= 1024), which a routed workgroup of slot a polls for both its
+  // go-ahead and its expert, and `epoch` into *idsflag, which the shared down
+  // workgroups wait for before they count arrivals.  Each shared gate/up
+  // workgroup stores `epoch` into sgflags[sx * I/16 + rg] once its h rows are
+  // stored (the shared down of expert sx waits for them); each routed gate/up
+  // workgroup into guflags[a * I/32 + tile] (the routed down of slot a waits
+  // for them).  The routed down runs on kFrontDownRows-row tiles; the shared
+  // down workgroups count on the tiles' arrival counters beside the routed
+  // down ones, and whichever arrives last combines the tile.
   int front;
   unsigned long long* idsflag;
   unsigned long long* sgflags;
+  unsigned long long* guflags;
+  unsigned long long* idtag;
   // prefill (MFMA) path: MX activations, rows padded to Kq / Iq columns
   // (multiples of 512, zero codes past H / I); scale rows in MFMA order.
   // afmt 0: MXFP8 (E4M3, one byte per element); afmt 4: MXFP4 (E2M1, two per

@@ -68,6 +68,13 @@ __device__ __forceinline__ u32x4 ld_nt(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// 16 bytes stored by another workgroup of the same launch: two device-scope
+// 8-byte loads (past this XCD's L2, see store_coherent).
+__device__ __forceinline__ u32x4 ld16_coherent(const void* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = load_coherent(q), b = load_coherent(q + 1);
+  return u32x4{uint32_t(a), uint32_t(a >> 32), uint32_t(b), uint32_t(b >> 32)};
+}
 template <bool kReuse>
 __device__ __forceinline__ u32x4 ld_w(const void* p) {
   if constexpr (kReuse) return ld16(p);
@@ -125,13 +132,15 @@ __device__ __forceinline__ void stage_rows(uint16_t* dst, int stride, int mt, in
 // 2 j + 1 = lo of token j (zero-filled from K to Kp).  As B columns of one
 // MFMA, hi and lo of a token are then multiplied by the same weights in one
 // instruction; hi_sum() adds the two columns afterwards.
-template <typename Src>
+// kCoherent: the rows were stored by other workgroups of the same launch.
+template <bool kCoherent = false, typename Src>
 __device__ __forceinline__ void stage_h(uint16_t* dst, int stride, int mt, int K, int Kp,
                                         Src src) {
   const int nch = Kp / 4;
   for (int i = threadIdx.x; i < mt * nch; i += kThreads) {
     const int j = i / nch, q = i % nch;
-    const u32x4 v = q * 4 < K ? ld16(src(j) + q * 4) : u32x4{0, 0, 0, 0};
+    u32x4 v = {0, 0, 0, 0};
+    if (q * 4 < K) v = kCoherent ? ld16_coherent(src(j) + q * 4) : ld16(src(j) + q * 4);
     const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
     *reinterpret_cast<u32x2*>(dst + (2 * j) * stride + q * 4) =
         u32x2{(w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16)};
@@ -329,6 +338,23 @@ __device__ __forceinline__ void join_halves(f32x4_t& a, f32x4_t& b, float* red) 
   }
 }
 
+// One-token front: the expert of slot a, once the top-k of this launch has
+// stored its tagged word (bounded like wait_flags; a give-up sets the status
+// marker and returns what is there, clamped by the caller).  Every thread of
+// the workgroup calls it.
+__device__ int front_expert(const GemvLayer& L, int a) {
+  const unsigned long long tag = L.epoch & 0xFFFFFFFFFFFFull;
+  unsigned long long v = 0;
+  bool done = false;
+  for (long it = 0; it < L.spin_limit && !done; ++it) {
+    v = load_coherent(&L.idtag[a]);
+    done = __syncthreads_and((v >> 16) == tag) != 0;
+    if (!done) __builtin_amdgcn_s_sleep(8);
+  }
+  if (threadIdx.x == 0 && !done) store_coherent(L.status, kWaitGaveUp);
+  return __builtin_amdgcn_readfirstlane(int(v & 0xFFFFu));
+}
+
 // Expert slot a of the routed launches: the number of live slots, its
 // expert and its plan positions [p0, p1).  The plan reads are issued
 // together (all in bounds for any a < E) and the slot is checked after they
@@ -337,9 +363,9 @@ __device__ __forceinline__ void slot_of(const GemvLayer& L, int a, int& n, int& 
                                         int& p1) {
   if (L.direct) {
     n = L.T * L.k;
-    const int32_t* p = L.ids_in + min(a, n - 1);
-    // in the front launch the top-k wrote them in this launch: coherent load
-    e = min(max(L.front ? load_coherent(p) : *p, 0), L.E - 1);  // clamped like the plan's ids
+    // in the front launch the top-k of this launch stores it (tagged word)
+    const int id = L.front ? front_expert(L, min(a, n - 1)) : L.ids_in[min(a, n - 1)];
+    e = min(max(id, 0), L.E - 1);  // clamped like the plan's ids
     p0 = a;
     p1 = a + 1;
     return;
@@ -362,6 +388,10 @@ __device__ __forceinline__ const uint8_t* record_of(const GemvLayer& L, int e) {
   return L.experts + size_t(r) * L.stride;
 }
 
+// kFront: in the one-token front launch; the h rows are stored through the
+// coherent level and flagged for the routed down of the same launch
+// (guflags[a * I/32 + tile]).
+template <bool kFront = false>
 __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs, float* red) {
   int na, e, p0, p1;
   slot_of(L, a, na, e, p0, p1);
@@ -406,17 +436,26 @@ __device__ void routed_gateup(const GemvLayer& L, int a, int tile, uint16_t* xs,
         split_bf16(silu(ag[i]) * au[i], hi, lo);
         hv[i] = uint32_t(hi) | (uint32_t(lo) << 16);
       }
-      *reinterpret_cast<u32x4*>(L.h + size_t(t0 + c) * I + rg * 16 + 4 * g) =
-          u32x4{hv[0], hv[1], hv[2], hv[3]};
+      uint32_t* hrow = L.h + size_t(t0 + c) * I + rg * 16 + 4 * g;
+      if (kFront) {  // read by the routed down of this launch
+        store_coherent(reinterpret_cast<uint64_t*>(hrow), uint64_t(hv[0]) | uint64_t(hv[1]) << 32);
+        store_coherent(reinterpret_cast<uint64_t*>(hrow) + 1,
+                       uint64_t(hv[2]) | uint64_t(hv[3]) << 32);
+      } else {
+        *reinterpret_cast<u32x4*>(hrow) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+      }
     }
+  }
+  if (kFront) {  // h rows stored: flag them for the routed down of slot a
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) store_coherent(&L.guflags[a * (I / 32) + tile], L.epoch);
   }
 }
 
-// Shared gate/up and down waves keep this many super-steps of weights in
-// flight (the shared launches have few workgroups per CU); the shared down
-// shares its launch with the routed gate/up, whose occupancy (three waves
-// per SIMD) its registers must not lower.
-constexpr int kSharedStages = 4;
+// Shared down waves keep this many super-steps of weights in flight; the
+// shared down shares its launch with the routed gate/up, whose occupancy
+// (three waves per SIMD) its registers must not lower.
 constexpr int kSharedDownStages = 3;
 
 // Shared gate/up (bf16): 1 KiB tiles of 16 rows x 32 columns are the A
@@ -429,8 +468,8 @@ constexpr int kSharedDownStages = 3;
 // cap on tokens per pass from the LDS size) is needed.
 // kReuse: more than one pass of tokens, so the weights are loaded with the
 // default cache policy and later passes find them in the caches; a single
-// pass streams them past the caches.
-template <bool kReuse>
+// pass streams them past the caches.  D: super-steps in flight.
+template <bool kReuse, int D = 3>
 __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -460,9 +499,9 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
         t.x[j] = ld16(xrow + u * 32);
       }
     };
-    Tiles bufs[3];
+    Tiles bufs[D];
     f32x4_t ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = {0.0f, 0.0f, 0.0f, 0.0f};
-    pipelineN<3>(q0, q1, bufs, load, [&]() {}, [&](const Tiles& t, int q) {
+    pipelineN<D>(q0, q1, bufs, load, [&]() {}, [&](const Tiles& t, int q) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (4 * q + j >= nu) break;  // uniform
@@ -570,12 +609,23 @@ struct DnTiles {
 // a wave streams 2 row groups x 3 super-steps of 4 KiB, and more waves in
 // flight per SIMD beat deeper pipelines per wave (measured).
 constexpr int kDownStages = 3;
+// In the one-token front launch (two waves per SIMD, the front's register
+// budget) a wave keeps six steps in flight, the first five issued before the
+// wait for the slot's h.
+constexpr int kDownStagesFront = 6;
+// Shared gate/up super-steps in flight in the front launch.
+constexpr int kSharedStagesFront = 3;
+// Waves per SIMD the front launch's registers are fitted to.
+constexpr int kFrontWaves = 2;
 
 // Routed down: workgroup = (expert, tile of kRowsD rows); wave w takes the
 // tile's row groups w, w + 4, w + 8, ... one after the other as one continuous
 // pipeline of (row group, super-step) steps, so its loads never drain
 // between row groups; a row group's partials are stored after its last
-// super-step.
+// super-step.  kFront: in the front launch, h is waited for (the slot's
+// gate/up flags) and read through the coherent level once the prologue's
+// weight loads are in flight.
+template <int D, bool kFront>
 __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, int tile,
                             uint16_t* hsm) {
   const int wave = wave_id();
@@ -585,8 +635,9 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   const PackedMx pgu(I, H), pd(H, I);
   const int nkq = pd.nkb4 / 4;
   // the tile's row groups rg0 + wave + kWaves r, r = 0 .. nrg - 1
-  const int tile_rg = min(kRowsD / 16, H / 16 - tile * (kRowsD / 16));  // ragged last tile
-  const int rg0 = tile * (kRowsD / 16) + wave;
+  constexpr int R = kFront ? kFrontDownRows : kRowsD;  // rows per tile
+  const int tile_rg = min(R / 16, H / 16 - tile * (R / 16));  // ragged last tile
+  const int rg0 = tile * (R / 16) + wave;
   const int nrg = max(0, (tile_rg - wave + kWaves - 1) / kWaves);
   const int nsteps = nrg * nkq;
   const uint8_t* base = record_of(L, e) + 2 * pgu.bytes;
@@ -604,17 +655,18 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
 
   for (int t0 = p0; t0 < p1; t0 += L.mtp_d) {
     const int mt = min(L.mtp_d, p1 - t0);
-    DnTiles bufs[kDownStages];
+    DnTiles bufs[D];
     const uint16_t* bh = hsm + (c < 2 * mt ? c : 0) * hstride;  // column c: token c / 2, hi / lo
     const int tok = c / 2;
     const int pair = pair_at(L, t0 + (tok < mt ? tok : 0));
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
     auto stage = [&]() {
       __syncthreads();
-      stage_h(hsm, hstride, mt, I, pad_k(I), [&](int j) { return L.h + size_t(t0 + j) * I; });
+      if constexpr (kFront) wait_flags(L, L.guflags + a * (I / 32), I / 32);
+      stage_h<kFront>(hsm, hstride, mt, I, pad_k(I), [&](int j) { return L.h + size_t(t0 + j) * I; });
       __syncthreads();
     };
-    pipelineN<kDownStages>(0, nsteps, bufs, load, stage, [&](const DnTiles& t, int s) {
+    pipelineN<D>(0, nsteps, bufs, load, stage, [&](const DnTiles& t, int s) {
       const int r = s / nkq, kq = s - r * nkq;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -639,7 +691,18 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
   }
 }
 
-template <bool kReuse>  // as for shared_gateup
+// Arrivals that complete front tile ft (kFrontDownRows rows) of one token:
+// the k routed down workgroups and the shared down workgroups of its rows.
+__device__ __forceinline__ int front_arrivals(const GemvLayer& L, int ft) {
+  constexpr int per = kFrontDownRows / kRowsSD;
+  return L.T * L.k + L.S * min(per, L.n_stiles - per * ft);
+}
+template <int R, bool kFront>
+__device__ void combine_tile(const GemvLayer& L, int tile);
+
+// kReuse as for shared_gateup; kFront: in the one-token front launch (the
+// rows count towards the front tiles' combine).
+template <bool kReuse, bool kFront = false>
 __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -681,19 +744,33 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
     if (live && (c & 1) == 0 && c / 2 < mt) {
+      float* yrow = L.ysh + (size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        L.ysh[(size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g + i] = y[i];
+      for (int i = 0; i < 4; ++i) {
+        if (kFront)  // read by the combine of this launch
+          store_coherent(yrow + i, y[i]);
+        else
+          yrow[i] = y[i];
+      }
     }
+  }
+  if (kFront) {  // rows stored: count them; the last arriver of the tile combines it
+    wait_flags(L, L.idsflag, 1);  // the counters were cleared before the ids flag
+    const int ft = tile / (kFrontDownRows / kRowsSD);
+    if (arrive_last(&L.tile_cnt[ft], front_arrivals(L, ft)))
+      combine_tile<kFrontDownRows, true>(L, ft);
   }
 }
 
 // The last routed workgroup of a tile sums the partials into the bf16 output.
 // All of a token's partial loads are issued before the first add, so the
 // tail costs one memory round trip, not k of them.
+// R: rows per tile; kFront: the shared outputs were stored in the same
+// launch (read through the coherent level).
+template <int R, bool kFront>
 __device__ void combine_tile(const GemvLayer& L, int tile) {
   const int H = L.H, k = L.k;
-  const int n_out = L.T * kRowsD;
+  const int n_out = L.T * R;
   // Every load of a token's sum is issued unconditionally, with clamped
   // indices and stand-in rows for absent operands, and their values are taken
   // at one point: a load under a condition would be waited for on its own,
@@ -701,8 +778,8 @@ __device__ void combine_tile(const GemvLayer& L, int tile) {
   const float* ysh = L.S > 0 ? L.ysh : L.part;
   const uint16_t* res = L.residual != nullptr ? L.residual : L.x;
   for (int idx = threadIdx.x; idx < n_out; idx += kThreads) {
-    const int t = idx / kRowsD;
-    const int n = tile * kRowsD + idx % kRowsD;
+    const int t = idx / R;
+    const int n = tile * R + idx % R;
     if (n >= H) continue;
     float acc = 0.0f;
     float sv[4];
@@ -717,8 +794,10 @@ __device__ void combine_tile(const GemvLayer& L, int tile) {
       }
       if (j0 == 0) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          sv[s] = ysh[(size_t(max(min(s, L.S - 1), 0)) * L.T + t) * H + n];
+        for (int s = 0; s < 4; ++s) {
+          const float* q = ysh + (size_t(max(min(s, L.S - 1), 0)) * L.T + t) * H + n;
+          sv[s] = kFront ? load_coherent(q) : *q;
+        }
         rv = res[size_t(t) * H + n];
       }
 #pragma unroll
@@ -1255,8 +1334,8 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const bool single = st.n_select + st.n_selw == 1;
   __shared__ int own_ids[4 * 32];
   __shared__ SelectScratch sc[kWaves];
+  int id = 0;  // this lane's selected expert (lanes < k of a token's wave)
   if (t < L.T) {
-    int id;
     float w;
     const float* lrow = L.logits + size_t(t) * L.E;
     const size_t ps = size_t(L.T) * L.E;
@@ -1283,16 +1362,19 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
       }
     }
   }
-  if (L.front) {  // ids and weights stored (above): flag them for the routed gate/up
+  // Direct mode (no plan): only the combine's arrival counters need clearing,
+  // before the ids flag: a routed down of the same launch may count once it
+  // sees the flag.
+  if (st.plan_after_select && L.direct)
+    for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) store_coherent(&L.tile_cnt[i], 0);
+  if (L.front) {  // ids, weights and counters stored (above): publish the slots' experts
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (wave == 0 && lane < L.k && L.T == 1)
+      store_coherent(&L.idtag[lane], (L.epoch & 0xFFFFFFFFFFFFull) << 16 | uint32_t(id));
     if (threadIdx.x == 0) store_coherent(L.idsflag, L.epoch);
   }
-  if (!st.plan_after_select) return;
-  if (L.direct) {  // no plan: only the combine's arrival counters need clearing
-    for (int i = threadIdx.x; i < L.n_tiles; i += kThreads) L.tile_cnt[i] = 0;
-    return;
-  }
+  if (!st.plan_after_select || L.direct) return;
   if (single) {
     __syncthreads();
     build_plan([&](int p) { return own_ids[p]; }, L.T * L.k, L.E, L.plan, L.tile_cnt, L.n_tiles);
@@ -1304,12 +1386,19 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
              L.n_tiles);
 }
 
+template <bool kFront>
 __device__ void routed_down_role(const GemvLayer& L, int a, int tile, uint16_t* hsm) {
   int n_active, e, p0, p1;
   slot_of(L, a, n_active, e, p0, p1);
   if (a >= n_active) return;  // slot beyond this routing's experts
-  routed_down(L, a, e, p0, p1, tile, hsm);
-  if (arrive_last(&L.tile_cnt[tile], n_active)) combine_tile(L, tile);
+  if constexpr (kFront) {
+    routed_down<kDownStagesFront, true>(L, a, e, p0, p1, tile, hsm);
+    if (arrive_last(&L.tile_cnt[tile], front_arrivals(L, tile)))
+      combine_tile<kFrontDownRows, true>(L, tile);
+  } else {
+    routed_down<kDownStages, false>(L, a, e, p0, p1, tile, hsm);
+    if (arrive_last(&L.tile_cnt[tile], n_active)) combine_tile<kRowsD, false>(L, tile);
+  }
 }
 
 template <unsigned R, int NCH>
@@ -1430,7 +1519,7 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   }
   if constexpr ((R & kRoleRoutedDown) != 0) {
     if (b < st.n_rdn) {
-      routed_down_role(L, b / L.n_tiles, b % L.n_tiles, lds16p);
+      routed_down_role<false>(L, b / L.n_tiles, b % L.n_tiles, lds16p);
       return;
     }
     b -= st.n_rdn;
@@ -1443,17 +1532,22 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   }
 }
 
-// One-token decode front: every workgroup role of the layer up to the
-// routed down, in one launch, in this block order: router logits (each flags
-// its logits), shared gate/up (each flags its h rows), the top-k (waits for
-// the logits flags, flags its ids and weights), routed gate/up (waits for the
-// ids flag), shared down (waits for its shared expert's gate/up flags).  A
-// workgroup only waits for blocks with lower indices, which the dispatcher
-// hands out first (in order on every XCD), so the lowest-indexed unfinished
-// block can always run to its end: every wait ends; each is bounded besides
-// (wait_flags).  The routed gate/up stream starts as soon as the top-k is
-// done, while the shared experts still stream, instead of after a launch
-// boundary.
+// One-token decode: every workgroup role of the layer in one launch, in
+// this block order: router logits (each flags its logits), shared gate/up
+// (each flags its h rows), the top-k (waits for the logits flags, publishes
+// each slot's expert), routed gate/up (waits for its slot's expert, flags its
+// h rows), routed down (waits for its slot's expert and gate/up flags,
+// counts its tile's arrival), shared down (waits for its shared expert's
+// gate/up flags, counts its tile's arrival); the last arriver of a tile
+// combines it.  A workgroup only waits for blocks with lower indices, which
+// the dispatcher hands out first (in order on every XCD), so the
+// lowest-indexed unfinished block can always run to its end: every wait
+// ends; each is bounded besides (wait_flags).  The routed streams start as
+// soon as the top-k is done, while the shared experts still stream, and the
+// routed down starts while the gate/up of later slots still streams: no
+// launch boundary drains the machine between them.  Measured against other
+// block orders and tile sizes (routed gate/up first, shared down before the
+// routed down, 64-row gate/up or 128/512-row down tiles): all slower.
 template <int NCH>
 __device__ __forceinline__ void front_body(const GemvLayer& L, const Stage& st) {
   extern __shared__ u32x4 lds_raw[];
@@ -1461,6 +1555,7 @@ __device__ __forceinline__ void front_body(const GemvLayer& L, const Stage& st) 
   __shared__ float red[kWaves * kWave * 8];
   const int sgu_rows = L.I / 16, gu_tiles = L.I / 32;
   int b = blockIdx.x;
+  // router logits
   if (b < st.n_logits) {
     if (b == 0 && threadIdx.x == 0 && L.sel_cnt != nullptr) L.sel_cnt[0] = 0;
     router_logits_rows<NCH>(L.x, L.wr, L.rbias, L.logits, L.T, L.H, L.E, b, lds_raw);
@@ -1470,33 +1565,44 @@ __device__ __forceinline__ void front_body(const GemvLayer& L, const Stage& st) 
     return;
   }
   b -= st.n_logits;
+  // shared gate/up
   if (b < st.n_sgu) {
-    shared_gateup<false>(L, b / sgu_rows, b % sgu_rows, red);
+    shared_gateup<false, kSharedStagesFront>(L, b / sgu_rows, b % sgu_rows, red);
     return;
   }
   b -= st.n_sgu;
+  // top-k
   if (b < st.n_selw) {
     select_waits(L, st.n_logits);
     select_role<true>(L, st, 0);
     return;
   }
   b -= st.n_selw;
-  if (b < st.n_rgu) {
-    wait_flags(L, L.idsflag, 1);
-    routed_gateup(L, b / gu_tiles, b % gu_tiles, lds16p, red);
+  // routed gate/up
+  if (b < st.n_rgu) {  // waits for its slot's expert (slot_of)
+    routed_gateup<true>(L, b / gu_tiles, b % gu_tiles, lds16p, red);
     return;
   }
   b -= st.n_rgu;
+  // routed down
+  if (b < st.n_rdn) {  // waits for its slot's gate/up flags
+    const int nft = (L.H + kFrontDownRows - 1) / kFrontDownRows;
+    routed_down_role<true>(L, b / nft, b % nft, lds16p);
+    return;
+  }
+  b -= st.n_rdn;
+  // shared down
   if (b < st.n_sdn) {
     const int sx = b / L.n_stiles;
     wait_flags(L, L.sgflags + sx * sgu_rows, sgu_rows);
-    shared_down<false>(L, sx, b % L.n_stiles);
+    shared_down<false, true>(L, sx, b % L.n_stiles);
   }
 }
 
 // The launches, named for what they run.
 template <int NCH>
-__global__ __launch_bounds__(kThreads) void moe_decode_front(GemvLayer L, Stage st) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFrontWaves))) void
+moe_decode_front(GemvLayer L, Stage st) {
   front_body<NCH>(L, st);
 }
 template <int NCH>
