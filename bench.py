@@ -19,6 +19,9 @@ in pinned host memory and an HBM pool of 256 slots is filled on demand
 meanwhile and the routed experts wait for the copies (moe_forward_pooled), so
 each step includes the host-to-device copies of the experts it misses.
 
+Untimed warmup: the W warmup steps, repeated until they have run for at
+least 0.2 s (the GPU's clocks reach their steady state under load).
+
 Printed: one JSON line with tokens/s (value), ms per step, the expert-weight
 HBM rate, the dominant kernel's roofline (HIP events around each kernel of
 the library's own launches) and the float64 oracle timed on the host cores
@@ -52,6 +55,7 @@ FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 PCIE_PEAK_GBS = 64.0            # PCIe 5.0 x16, one direction
+WARMUP_S = 0.2                  # least wall time of untimed warmup steps
 
 CONFIGS = {
     "b1": dict(tokens=1, layers=1, replicas=8,
@@ -589,9 +593,19 @@ def main():
                             residual=cur, path=path)
                 cur = y[l + 1]
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    # warmup: the W warmup steps, repeated until the GPU has run at least
+    # WARMUP_S of them (after the idle setup the clocks need tens of
+    # milliseconds of load to reach their steady state: the first 25 ms of
+    # one-token steps ran 6% slower than the next)
+    t_w = time.perf_counter()
+    warmup_run = 0
+    while True:
+        for i in range(args.warmup):
+            step(i)
+        warmup_run += args.warmup
+        torch.cuda.synchronize()
+        if args.warmup == 0 or time.perf_counter() - t_w >= WARMUP_S:
+            break
     pool_before = pool.stats() if pool is not None else None
     t0 = time.perf_counter()
     for i in range(args.warmup, n_steps):
@@ -686,6 +700,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warmup_run,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

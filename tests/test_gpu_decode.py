@@ -323,6 +323,41 @@ def test_consecutive_calls_with_changing_inputs(b):
         check_parity(to_np_u16(y), ref)
 
 
+@pytest.mark.parametrize("fill", ["zeros", "ones", "random"])
+def test_one_token_on_an_uninitialised_workspace(b, fill):
+    """One token runs the whole layer in one launch whose workgroups hand
+    over through the workspace: epoch-tagged expert words and flags, and
+    arrival counters the top-k clears.  None of it needs initialising: calls
+    on a workspace refilled before each call with zero bytes, all-one bytes
+    or random bytes match the oracle and report no give-up.  The ragged
+    shape leaves a short last output tile (288 = 256 + 32 rows)."""
+    built = Built(RAGGED, seed=17)
+    H, k = RAGGED["hidden"], RAGGED["top_k"]
+    ws = built.lib.workspace(1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((1, H), dtype=torch.int16, device="cuda")
+    for i in range(3):
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ones":
+            ws.fill_(255)
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda",
+                                   generator=gen))
+        xh, xd = SD.upload_tokens(7100 + i, 1, H)
+        b.moe_layer(built.lib, xd, y, ids, w, ws, path=b.PATH_GEMV)
+        torch.cuda.synchronize()
+        assert b.workspace_status(ws) == b.MOE_OK
+        _, _, s = M.route(xh, built.oracle)
+        ids_np = ids.cpu().numpy()
+        check_routing(ids_np, w.cpu().numpy(), s, k)
+        check_parity(to_np_u16(y), M.moe_forward(xh, built.oracle, ids_np,
+                                                 oracle_weights(s, ids_np)))
+
+
 def test_alternating_batch_sizes_share_a_workspace(b):
     """One workspace, token counts alternating over the three launch
     structures (one token: no plan; 2-4 tokens: top-k and plan inside the
