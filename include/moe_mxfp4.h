@@ -252,14 +252,17 @@ int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
 /*
  * Status of the calls that used a workspace.  For up to 4 tokens on the GEMV
  * path, moe_layer runs the top-k inside the router launch, in a workgroup
- * that waits for the other workgroups' logits (a bounded wait: see
- * moe_set_wait_limit).  If that wait ever gives up, the call's routing (and
- * output) is wrong, and the first 8 bytes of its workspace are set to a
- * marker that no call clears.  moe_workspace_status synchronises `stream`
- * (the stream of those calls), reads the marker and returns MOE_ETIMEOUT if
- * it is set -- clearing it, so a later query reports only later calls --
- * else MOE_OK.  A workspace whose first bytes were never written by a call
- * reads as MOE_OK.  Host-synchronous (unlike every other call).
+ * that waits for the other workgroups' logits; for one token the whole
+ * layer is that launch, whose routed and shared workgroups also wait for
+ * the top-k's expert ids and for the gate/up results they consume.  Every
+ * such wait is bounded (see moe_set_wait_limit).  If one ever gives up, the
+ * call's routing (and output) is wrong, and the first 8 bytes of its
+ * workspace are set to a marker that no call clears.  moe_workspace_status
+ * synchronises `stream` (the stream of those calls), reads the marker and
+ * returns MOE_ETIMEOUT if it is set -- clearing it, so a later query reports
+ * only later calls -- else MOE_OK.  A workspace whose first bytes were never
+ * written by a call reads as MOE_OK.  Host-synchronous (unlike every other
+ * call).
  */
 int moe_workspace_status(const void* workspace, uint64_t workspace_bytes, hipStream_t stream);
 
@@ -387,8 +390,8 @@ int moe_pool_destroy(moe_expert_pool* pool);
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
  * + combine -- for 2 to 4 tokens: router logits + shared gate/up + top-k
  * and plan, shared down + routed gate/up, routed down + combine; for one
- * token: router logits + shared gate/up + top-k + routed gate/up + shared
- * down (one launch), routed down + combine;
+ * token: the whole layer (router logits, shared gate/up, top-k, routed
+ * gate/up and down, shared down, combine) in one launch;
  * moe_layer (MFMA path): x to MXFP8 + router logits, top-k + plan, routed +
  * shared gate/up, routed + shared down, combine; moe_forward (MFMA path):
  * plan + x to MXFP8, then the same last three.  The caller creates and owns the hipEvent_t
