@@ -231,15 +231,18 @@ __device__ __forceinline__ void pipelineN(int s0, int s1, Buf (&b)[D], Load load
 }
 
 // ------------------------------------------------------------------------
-// Waits until flags[0 .. n) all hold this call's epoch, or gives up after
-// L.spin_limit polls and sets the workspace status marker (the caller reads
-// it with moe_workspace_status; the work then runs on what is there: wrong
-// results, no hang).  Every thread of the workgroup calls it.
-__device__ void wait_flags(const GemvLayer& L, const unsigned long long* flags, int n) {
+// Waits until flags[0 .. n) and flags2[0 .. n2) all hold this call's epoch
+// (both polled in one round trip), or gives up after L.spin_limit polls and
+// sets the workspace status marker (the caller reads it with
+// moe_workspace_status; the work then runs on what is there: wrong results,
+// no hang).  Every thread of the workgroup calls it.
+__device__ void wait_flags(const GemvLayer& L, const unsigned long long* flags, int n,
+                           const unsigned long long* flags2 = nullptr, int n2 = 0) {
   bool done = false;
   for (long it = 0; it < L.spin_limit && !done; ++it) {
     int ok = 1;
-    for (int i = threadIdx.x; i < n; i += kThreads) ok &= load_coherent(&flags[i]) == L.epoch;
+    for (int i = threadIdx.x; i < n + n2; i += kThreads)
+      ok &= load_coherent(i < n ? &flags[i] : &flags2[i - n]) == L.epoch;
     done = __syncthreads_and(ok) != 0;
     if (!done) __builtin_amdgcn_s_sleep(8);
   }
@@ -700,9 +703,7 @@ __device__ __forceinline__ int front_arrivals(const GemvLayer& L, int ft) {
 template <int R, bool kFront>
 __device__ void combine_tile(const GemvLayer& L, int tile);
 
-// kReuse as for shared_gateup; kFront: in the one-token front launch (the
-// rows count towards the front tiles' combine).
-template <bool kReuse, bool kFront = false>
+template <bool kReuse>  // as for shared_gateup
 __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -744,22 +745,71 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
     if (live && (c & 1) == 0 && c / 2 < mt) {
-      float* yrow = L.ysh + (size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kFront)  // read by the combine of this launch
-          store_coherent(yrow + i, y[i]);
-        else
-          yrow[i] = y[i];
-      }
+      for (int i = 0; i < 4; ++i)
+        L.ysh[(size_t(sx) * L.T + t0 + c / 2) * H + rg * 16 + 4 * g + i] = y[i];
     }
   }
-  if (kFront) {  // rows stored: count them; the last arriver of the tile combines it
-    wait_flags(L, L.idsflag, 1);  // the counters were cleared before the ids flag
-    const int ft = tile / (kFrontDownRows / kRowsSD);
-    if (arrive_last(&L.tile_cnt[ft], front_arrivals(L, ft)))
-      combine_tile<kFrontDownRows, true>(L, ft);
+}
+
+// Shared down in the one-token front launch: workgroup = (shared expert sx,
+// 64 rows), wave w takes row group 4 tile + w.  The weight loads of the
+// pipeline's first steps are issued before the wait for the shared
+// expert's gate/up flags (and the top-k's, which clears the arrival
+// counters), both polled in one round trip; the token's h (hi and lo rows)
+// is then staged in LDS from the coherent level.  The rows are stored
+// through the coherent level and counted on their front tile, whose last
+// arriver combines it.
+__device__ void shared_down_front(const GemvLayer& L, int sx, int tile, uint16_t* hsm) {
+  const int wave = wave_id();
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int rg = tile * (kRowsSD / 16) + wave;
+  const bool live = rg < L.H / 16;
+  const int H = L.H, I = L.I;
+  const int nu = I / 32;
+  const int nq = (nu + 3) / 4;
+  const int hp = pad_k(I);  // staged row length (zeros past I)
+  const uint16_t* dt = L.sdown + sx * (size_t(H) * I) + size_t(live ? rg : 0) * nu * 512;
+  const size_t plane = size_t(L.S) * L.T * I;
+  struct Tiles {
+    u32x4 w[4];
+  };
+  auto load = [&](Tiles& t, int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.w[j] = ld_nt(dt + size_t(min(4 * q + j, nu - 1)) * 512 + 8 * lane);
+  };
+  auto stage = [&]() {
+    wait_flags(L, L.sgflags + sx * (I / 16), I / 16, L.idsflag, 1);
+    for (int i = threadIdx.x; i < 2 * (hp / 8); i += kThreads) {
+      const int r = i / (hp / 8), q = i % (hp / 8);
+      u32x4 v = {0, 0, 0, 0};
+      if (q * 8 < I) v = ld16_coherent(L.hs + r * plane + size_t(sx) * L.T * I + q * 8);
+      *reinterpret_cast<u32x4*>(hsm + r * hp + q * 8) = v;
+    }
+    __syncthreads();
+  };
+  // B column c: the token's hi (c even) or lo (c odd) row
+  const uint16_t* bh = hsm + (c & 1) * hp + 8 * g;
+  Tiles bufs[kSharedDownStages];
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  pipelineN<kSharedDownStages>(0, live ? nq : 0, bufs, load, stage, [&](const Tiles& t, int q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (4 * q + j >= nu) break;  // uniform
+      acc = mfma(t.w[j], lds16(bh + (4 * q + j) * 32), acc);
+    }
+  });
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = hi_lo_sum(acc[i]);
+  if (live && c == 0) {
+    float* yrow = L.ysh + size_t(sx) * L.T * H + rg * 16 + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_coherent(yrow + i, y[i]);
   }
+  const int ft = tile / (kFrontDownRows / kRowsSD);
+  if (arrive_last(&L.tile_cnt[ft], front_arrivals(L, ft))) combine_tile<kFrontDownRows, true>(L, ft);
 }
 
 // The last routed workgroup of a tile sums the partials into the bf16 output.
@@ -1593,9 +1643,7 @@ __device__ __forceinline__ void front_body(const GemvLayer& L, const Stage& st) 
   b -= st.n_rdn;
   // shared down
   if (b < st.n_sdn) {
-    const int sx = b / L.n_stiles;
-    wait_flags(L, L.sgflags + sx * sgu_rows, sgu_rows);
-    shared_down<false, true>(L, sx, b % L.n_stiles);
+    shared_down_front(L, b / L.n_stiles, b % L.n_stiles, lds16p);
   }
 }
 
