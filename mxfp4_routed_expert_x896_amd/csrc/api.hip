@@ -118,6 +118,18 @@ int max_mtiles(const moe_layer_desc* L, int64_t T) {
   return int((pairs + (moe::kPlanTileTokens - 1) * active) / moe::kPlanTileTokens + 1);
 }
 int n_shared_tiles(const moe_layer_desc* L) { return (L->hidden + 63) / 64; }
+// Workgroups of the GEMV launches' shared roles for T tokens: (expert, row
+// group or 64-row tile, pass of tokens), grouped by XCD (layer.hip
+// xcd_split: 8 units per group of blocks, the passes of a unit on one XCD).
+int xcd_units(int units, int passes) { return 8 * ((units + 7) / 8) * passes; }
+int n_sgu_wgs(const moe_layer_desc* L, int64_t T) {
+  const int pass = moe::kGemvPassTokens;
+  return xcd_units(L->n_shared * (L->inter / 16), int((T + pass - 1) / pass));
+}
+int n_sdn_wgs(const moe_layer_desc* L, int64_t T) {
+  const int pass = moe::kGemvPassTokens / 2;
+  return xcd_units(L->n_shared * n_shared_tiles(L), int((T + pass - 1) / pass));
+}
 
 int n_logit_wgs(const moe_layer_desc* L) { return (L->n_experts + 3) / 4; }
 // Router workgroups of the GEMV path for T tokens (see lsplit).
@@ -291,11 +303,11 @@ int do_forward_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T, const
   const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
   moe::Stage s1;
   s1.n_plan = 1;
-  s1.n_sgu = S * (L->inter / 16);
+  s1.n_sgu = n_sgu_wgs(L, T);
   int st = stage(moe::StageKind::PlanSharedGateUp, G, s1, stream);
   if (st) return st;
   moe::Stage s2;
-  s2.n_sdn = S * n_shared_tiles(L);
+  s2.n_sdn = n_sdn_wgs(L, T);
   s2.n_rgu = ma * tiles_gu;
   if ((st = stage(moe::StageKind::RoutedGateUp, G, s2, stream))) return st;
   moe::Stage s3;
@@ -320,12 +332,12 @@ int do_forward_gemv_after(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
   moe::Stage s1;
   s1.n_plan = 1;
-  s1.n_sgu = S * (L->inter / 16);
+  s1.n_sgu = n_sgu_wgs(L, T);
   int st = stage(moe::StageKind::PlanSharedGateUp, G, s1, stream);
   if (st) return st;
   if (S > 0) {
     moe::Stage s1b;  // the shared down alone (the routed gate/up launch without its routed part)
-    s1b.n_sdn = S * n_shared_tiles(L);
+    s1b.n_sdn = n_sdn_wgs(L, T);
     if ((st = stage(moe::StageKind::RoutedGateUp, G, s1b, stream))) return st;
   }
   if ((st = launched(hipStreamWaitEvent(stream, ready, 0), stream))) return st;
@@ -353,7 +365,7 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   const int S = L->n_shared, tiles_gu = L->inter / 32, ma = max_active(L, T);
   moe::Stage s1;
   s1.n_logits = n_router_wgs(L, T);
-  s1.n_sgu = S * (L->inter / 16);
+  s1.n_sgu = n_sgu_wgs(L, T);
   if (T == 1) {
     // one token: the whole layer in one launch whose workgroups wait on
     // flags of earlier blocks (moe_decode_front); no plan (direct mode)
@@ -361,6 +373,8 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
     G.front = 1;
     s1.n_selw = 1;
     s1.plan_after_select = 1;
+    // the front's own decomposition: one workgroup per shared row group / tile
+    s1.n_sgu = S * (L->inter / 16);
     s1.n_rgu = ma * tiles_gu;
     s1.n_sdn = S * n_shared_tiles(L);
     s1.n_rdn = ma * ((L->hidden + moe::kFrontDownRows - 1) / moe::kFrontDownRows);
@@ -375,7 +389,7 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
     if (st) return st;
     moe::Stage s3;
     s3.n_rgu = ma * tiles_gu;
-    s3.n_sdn = S * n_shared_tiles(L);
+    s3.n_sdn = n_sdn_wgs(L, T);
     if ((st = stage(moe::StageKind::RoutedGateUp, G, s3, stream))) return st;
     moe::Stage s4;
     s4.n_rdn = ma * n_tiles(L);
@@ -386,7 +400,7 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
   moe::Stage s2;
   s2.n_select = n_select_wgs(T);
   s2.plan_after_select = 1;
-  s2.n_sdn = S * n_shared_tiles(L);
+  s2.n_sdn = n_sdn_wgs(L, T);
   if ((st = stage(moe::StageKind::SelectSharedDown, G, s2, stream))) return st;
   moe::Stage s3;
   s3.n_rgu = ma * tiles_gu;

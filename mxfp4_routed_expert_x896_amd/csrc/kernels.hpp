@@ -34,6 +34,10 @@ constexpr unsigned long long kWaitGaveUp = 0x5449'4D45'4F55'5400ull;
 constexpr long kDefaultSpinLimit = 1l << 20;
 
 // Output rows per routed down workgroup (and per combine tile).
+// Tokens per pass of the GEMV path's shared-expert roles: the 16 B columns
+// of one MFMA (the shared down's pass takes 8, each token's h as two
+// columns, hi and lo).
+constexpr int kGemvPassTokens = 16;
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
 // Routed down rows per workgroup when the down runs in the one-token front

@@ -52,6 +52,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kRowsD = kDownRows;  // routed down rows per workgroup (a multiple of 16)
 constexpr int kRowsSD = 64;        // shared down rows per workgroup (one row group per wave)
 constexpr int kCols = 16;         // B columns of one MFMA: at most 16 tokens per pass
+static_assert(kCols == kGemvPassTokens, "the launcher sizes the shared roles' passes");
 constexpr int kLdsBudget = 32768;  // bytes of staged activations per workgroup
 // Routed gate/up: its token rows are H bf16 each (14 KiB at K3); three
 // workgroups per CU (its register limit) leave 53 KiB of LDS each, three K3
@@ -472,8 +473,11 @@ constexpr int kSharedDownStages = 3;
 // kReuse: more than one pass of tokens, so the weights are loaded with the
 // default cache policy and later passes find them in the caches; a single
 // pass streams them past the caches.  D: super-steps in flight.
+// Tokens p0 .. p1 - 1 (p1 < 0: all), kCols per pass.
 template <bool kReuse, int D = 3>
-__device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
+__device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red, int p0 = 0,
+                              int p1 = -1) {
+  if (p1 < 0) p1 = L.T;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -488,8 +492,8 @@ __device__ void shared_gateup(const GemvLayer& L, int sx, int rg, float* red) {
   struct Tiles {
     u32x4 g[4], u[4], x[4];
   };
-  for (int t0 = 0; t0 < L.T; t0 += kCols) {
-    const int mt = min(kCols, L.T - t0);
+  for (int t0 = p0; t0 < p1; t0 += kCols) {
+    const int mt = min(kCols, p1 - t0);
     // B straight from the token rows (L2-resident): lane (c, g) reads token
     // c's 8 columns of each 32-column tile (a clamped token past mt)
     const uint16_t* xrow = L.x + size_t(t0 + min(c, mt - 1)) * H + 8 * g;
@@ -703,8 +707,9 @@ __device__ __forceinline__ int front_arrivals(const GemvLayer& L, int ft) {
 template <int R, bool kFront>
 __device__ void combine_tile(const GemvLayer& L, int tile);
 
-template <bool kReuse>  // as for shared_gateup
-__device__ void shared_down(const GemvLayer& L, int sx, int tile) {
+template <bool kReuse>  // as for shared_gateup; tokens p0 .. p1 - 1, kCols / 2 per pass
+__device__ void shared_down(const GemvLayer& L, int sx, int tile, int p0 = 0, int p1 = -1) {
+  if (p1 < 0) p1 = L.T;
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
@@ -718,8 +723,8 @@ __device__ void shared_down(const GemvLayer& L, int sx, int tile) {
   struct Tiles {
     u32x4 w[4], h[4];
   };
-  for (int t0 = 0; t0 < L.T; t0 += kCols / 2) {
-    const int mt = min(kCols / 2, L.T - t0);
+  for (int t0 = p0; t0 < p1; t0 += kCols / 2) {
+    const int mt = min(kCols / 2, p1 - t0);
     // B straight from h (L2-resident): column c is token c / 2's hi (c even)
     // or lo (c odd) part; lane (c, g) reads 8 columns of each 32-column tile
     const int tok = t0 + min(c / 2, mt - 1);
@@ -1544,18 +1549,29 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
     b -= st.n_sdmx;
   }
   const int gu_tiles = L.I / 32;
+  // The shared roles: one workgroup per (expert, row group or tile, pass of
+  // tokens), the passes of one row range on one XCD (xcd_split), where the
+  // first to load the weights leaves them in L2 for the others.
   if constexpr ((R & kRoleSharedGU) != 0) {
     if (b < st.n_sgu) {
-      if (L.T > kCols) shared_gateup<true>(L, b / (L.I / 16), b % (L.I / 16), red);
-      else shared_gateup<false>(L, b / (L.I / 16), b % (L.I / 16), red);
+      const int rows = L.I / 16, n_pass = (L.T + kCols - 1) / kCols;
+      int unit, pass;
+      if (!xcd_split(b, L.S * rows, n_pass, unit, pass)) return;
+      const int p0 = pass * kCols, p1 = min(L.T, p0 + kCols);
+      if (n_pass > 1) shared_gateup<true>(L, unit / rows, unit % rows, red, p0, p1);
+      else shared_gateup<false>(L, unit / rows, unit % rows, red, p0, p1);
       return;
     }
     b -= st.n_sgu;
   }
   if constexpr ((R & kRoleSharedDown) != 0) {
     if (b < st.n_sdn) {
-      if (L.T > kCols / 2) shared_down<true>(L, b / L.n_stiles, b % L.n_stiles);
-      else shared_down<false>(L, b / L.n_stiles, b % L.n_stiles);
+      const int n_pass = (L.T + kCols / 2 - 1) / (kCols / 2);
+      int unit, pass;
+      if (!xcd_split(b, L.S * L.n_stiles, n_pass, unit, pass)) return;
+      const int p0 = pass * (kCols / 2), p1 = min(L.T, p0 + kCols / 2);
+      if (n_pass > 1) shared_down<true>(L, unit / L.n_stiles, unit % L.n_stiles, p0, p1);
+      else shared_down<false>(L, unit / L.n_stiles, unit % L.n_stiles, p0, p1);
       return;
     }
     b -= st.n_sdn;
