@@ -48,7 +48,7 @@ SHARED_MAT_BYTES = 7168 * 1536 * 2                 # one bf16 shared matrix
 KERNELS_GEMV = ["router_shared_gateup", "select_shared_down", "routed_gateup", "routed_down_combine"]
 # one token: the whole layer in one launch
 KERNELS_GEMV_ONE = ["decode_front"]
-# 2 to 4 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
+# 2 to 8 tokens: the top-k runs in the router launch; the shared down beside the routed gate/up
 KERNELS_GEMV_SMALL = ["router_shared_gateup_topk", "shared_down_routed_gateup", "routed_down_combine"]
 KERNELS_MFMA = ["router_quant", "select_plan", "mx_gateup", "mx_down", "combine"]
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense MXFP8 (the FP4 x FP8 block-scaled MFMA rate)
@@ -192,7 +192,7 @@ def config_kernels(config):
         return ["int8_row_dequant"]
     T = cfgd["tokens"]
     return (KERNELS_MFMA if cfgd.get("path") in ("mfma", "mfma_fp4") else KERNELS_GEMV_ONE
-            if T == 1 else KERNELS_GEMV_SMALL if T <= 4 else KERNELS_GEMV)
+            if T == 1 else KERNELS_GEMV_SMALL if T <= 8 else KERNELS_GEMV)
 
 
 def stats_summary(args):

@@ -250,7 +250,7 @@ int moe_layer(const moe_layer_desc* layer, const uint16_t* x, int64_t n_tokens,
               int32_t path, void* workspace, uint64_t workspace_bytes, hipStream_t stream);
 
 /*
- * Status of the calls that used a workspace.  For up to 4 tokens on the GEMV
+ * Status of the calls that used a workspace.  For up to 8 tokens on the GEMV
  * path, moe_layer runs the top-k inside the router launch, in a workgroup
  * that waits for the other workgroups' logits; for one token the whole
  * layer is that launch, whose routed and shared workgroups also wait for
@@ -388,7 +388,7 @@ int moe_pool_destroy(moe_expert_pool* pool);
  * moe_forward (GEMV path): plan + shared gate/up, shared down + routed
  * gate/up, routed down + combine; moe_layer (GEMV path): router logits +
  * shared gate/up, top-k + plan + shared down, routed gate/up, routed down
- * + combine -- for 2 to 4 tokens: router logits + shared gate/up + top-k
+ * + combine -- for 2 to 8 tokens: router logits + shared gate/up + top-k
  * and plan, shared down + routed gate/up, routed down + combine; for one
  * token: the whole layer (router logits, shared gate/up, top-k, routed
  * gate/up and down, shared down, combine) in one launch;

@@ -164,7 +164,8 @@ Carve carve(const moe_layer_desc* L, int64_t T) {
     return at;
   };
   c.status = take(8);  // first: the same place for every layer and T
-  c.lflags = take(uint64_t(n_logit_wgs(L)) * 8);
+  // flags of the logits workgroups (either router decomposition)
+  c.lflags = take(uint64_t(std::max(n_logit_wgs(L), (L->n_experts + 15) / 16 * moe::kRouterSplit)) * 8);
   c.idsflag = take(8);
   c.sgflags = take(S * (I / 16) * 8);
   c.guflags = take((T == 1 ? k * (I / 32) : 1) * 8);  // one token: routed gate/up flags
@@ -380,9 +381,9 @@ int do_layer_gemv(const moe_layer_desc* L, const uint16_t* x, int64_t T,
     s1.n_rdn = ma * ((L->hidden + moe::kFrontDownRows - 1) / moe::kFrontDownRows);
     return stage(moe::StageKind::DecodeFront, G, s1, stream);
   }
-  if (n_select_wgs(T) == 1) {
-    // 2 to 4 tokens: the top-k and the plan run in the router launch, on one
-    // workgroup that waits for the logits
+  if (T <= moe::kSelwMaxTokens) {
+    // 2 to kSelwMaxTokens tokens: the top-k and the plan run in the router
+    // launch, on one workgroup that waits for the logits
     s1.n_selw = 1;
     s1.plan_after_select = 1;
     int st = stage(moe::StageKind::RouterSharedGateUp, G, s1, stream);

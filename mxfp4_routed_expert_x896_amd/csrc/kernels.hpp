@@ -47,6 +47,9 @@ static_assert(kFrontDownRows % kDownRows == 0, "front tiles count on the same co
 // Router logits of kRouterSplitMin or more tokens (GEMV path: the batches
 // whose top-k has a launch of its own): bf16 MFMA over kRouterSplit quarters
 // of the contraction, one workgroup per (16 experts, quarter).
+// Tokens whose top-k and plan run in the router launch, on one workgroup
+// (its waves take the tokens in turn) that waits for the logits.
+constexpr int kSelwMaxTokens = 8;
 constexpr int kRouterSplit = 4;
 constexpr int kRouterSplitMin = 5;
 // Prefill combine workgroups per token: 1024-column chunks of the output row.

@@ -587,7 +587,9 @@ __device__ void router_split_role(const GemvLayer& L, int b, float* red) {
 #pragma unroll
         for (int ww = 1; ww < kWaves; ++ww) v += red[(ww * kWave + lane) * 4 + r];
         if (q == 0 && L.rbias != nullptr && e < E) v += L.rbias[e];
-        if (e < E) part[size_t(t0 + c) * E + e] = v;
+        // through the coherent level: the top-k of up to kSelwMaxTokens
+        // tokens reads it in the same launch
+        if (e < E) store_coherent(&part[size_t(t0 + c) * E + e], v);
       }
     }
   }
@@ -889,7 +891,7 @@ enum : unsigned {
   kRoleRouterMx = 2048u,  // prefill: router logits, (256 experts, 64 tokens)
   kRoleSharedGUMx = 4096u,    // prefill: shared gate/up, 2 x (expert, 128 rows, 64 tokens)
   kRoleSharedDownMx = 8192u,  // prefill: shared down, 2 x (expert, 256 rows, 64 tokens)
-  kRoleSelectWait = 16384u,   // top-k of T <= 4 tokens once this launch's logits are flagged
+  kRoleSelectWait = 16384u,   // top-k of T <= 8 tokens once this launch's logits are flagged
 };
 
 // XCD-aware order for a grid over (pair, token tile): block b runs on XCD
@@ -1364,14 +1366,12 @@ __device__ void combine_role(const GemvLayer& L, int b) {
   }
 }
 
-// The top-k workgroup of the router launch (T <= 4, the launch's last
-// block) waits until every logits workgroup has flagged its logits with this
-// call's epoch, then clears the flags for the next call.  Only this one
-// workgroup waits, on workgroups that wait on nothing, so the others always
-// get to run.  The wait is bounded (L.spin_limit polls): if it gives up, the
-// workspace status word is set to kWaitGaveUp, which the caller reads with
-// moe_workspace_status, and the selection runs on what is there (wrong
-// results, no hang).
+// The top-k workgroup of the router launch (T <= kSelwMaxTokens, the launch's last block) waits
+// until every logits workgroup has flagged its logits with this call's epoch, then clears the
+// flags for the next call. Only this one workgroup waits, on workgroups that wait on nothing, so
+// the others always get to run. The wait is bounded (L.spin_limit polls): if it gives up, the
+// workspace status word is set to kWaitGaveUp, which the caller reads with moe_workspace_status,
+// and the selection runs on what is there (wrong results, no hang).
 __device__ void select_waits(const GemvLayer& L, int n) {
   wait_flags(L, L.lflags, n);
   __syncthreads();
@@ -1382,14 +1382,17 @@ template <bool kCoherent = false>
 __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
-  const int t = b * 4 + wave;
-  // With one top-k workgroup (T <= 4) it builds the plan straight from its
-  // own selections in LDS: no arrival count, and no round trips through the
-  // coherent level for the ids it has just computed.
+  // With one top-k workgroup (T <= kSelwMaxTokens; its waves take the
+  // tokens in turn) it builds the plan straight from its own selections in
+  // LDS: no arrival count, and no round trips through the coherent level for
+  // the ids it has just computed.
   const bool single = st.n_select + st.n_selw == 1;
-  __shared__ int own_ids[4 * 32];
+  __shared__ int own_ids[kSelwMaxTokens * 32];
   __shared__ SelectScratch sc[kWaves];
   int id = 0;  // this lane's selected expert (lanes < k of a token's wave)
+  const int rounds = single ? (L.T + kWaves - 1) / kWaves : 1;
+  for (int r = 0; r < rounds; ++r) {
+  const int t = (single ? r : b) * kWaves + wave;
   if (t < L.T) {
     float w;
     const float* lrow = L.logits + size_t(t) * L.E;
@@ -1416,6 +1419,7 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
         store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
       }
     }
+  }
   }
   // Direct mode (no plan): only the combine's arrival counters need clearing,
   // before the ids flag: a routed down of the same launch may count once it

@@ -131,7 +131,7 @@ def test_select_mode_saturated_scores_tie_in_fp32(b, T):
     check_parity(y, M.moe_forward(xh, built.oracle, ids, M.combine_weights(s, ids)))
 
 
-@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("T", [1, 3, 8])
 def test_wait_give_up_is_reported(b, T):
     """With a wait limit of 0 the top-k workgroup of the router launch gives
     up at once (every kernel still runs to its end); the call's workspace
@@ -151,14 +151,15 @@ def test_wait_give_up_is_reported(b, T):
         torch.cuda.synchronize()
         assert b.workspace_status(ws) == b.MOE_ETIMEOUT
         assert b.workspace_status(ws) == b.MOE_OK       # reported once
-        # a call structure without the in-launch wait is unaffected
-        x8h, x8d = SD.upload_tokens(6310, 8, 256)
-        ws8 = built.lib.workspace(8)
-        i8 = torch.empty((8, 4), dtype=torch.int32, device="cuda")
-        w8 = torch.empty((8, 4), dtype=torch.float32, device="cuda")
-        y8 = torch.empty((8, 256), dtype=torch.int16, device="cuda")
-        b.moe_layer(built.lib, x8d, y8, i8, w8, ws8, path=b.PATH_GEMV)
-        assert b.workspace_status(ws8) == b.MOE_OK
+        # a call structure without the in-launch wait (more than 8 tokens:
+        # the top-k has a launch of its own) is unaffected
+        x9h, x9d = SD.upload_tokens(6310, 9, 256)
+        ws9 = built.lib.workspace(9)
+        i9 = torch.empty((9, 4), dtype=torch.int32, device="cuda")
+        w9 = torch.empty((9, 4), dtype=torch.float32, device="cuda")
+        y9 = torch.empty((9, 256), dtype=torch.int16, device="cuda")
+        b.moe_layer(built.lib, x9d, y9, i9, w9, ws9, path=b.PATH_GEMV)
+        assert b.workspace_status(ws9) == b.MOE_OK
     finally:
         b.set_wait_limit(-1)
     b.moe_layer(built.lib, xd, y, ids, w, ws, path=b.PATH_GEMV)
