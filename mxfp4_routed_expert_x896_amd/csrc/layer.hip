@@ -847,7 +847,7 @@ __device__ void combine_tile(const GemvLayer& L, int tile) {
       for (int j = 0; j < 16; ++j) {
         const size_t p = size_t(t) * k + min(j0 + j, k - 1);
         pv[j] = load_coherent(&L.part[p * H + n]);
-        wv[j] = L.w[p];
+        wv[j] = kFront ? load_coherent(&L.w[p]) : L.w[p];  // front: the top-k's, same launch
       }
       if (j0 == 0) {
 #pragma unroll
