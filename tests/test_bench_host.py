@@ -1,5 +1,5 @@
-"""Host-side logic of bench.py (CPU only): the HBM counter summary and the
-one-GPU refusal."""
+"""Host-side logic of bench.py (CPU only): the HBM counter summary, the
+algorithmic byte accounting of the launches and the one-GPU refusal."""
 
 import argparse
 import csv
@@ -52,3 +52,33 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_one_token_launch_bytes_are_the_layer_s_bytes():
+    """The one-token launch runs the whole layer: its algorithmic bytes are
+    the three-launch structure's sum less one read of the token (the router
+    and the routed gate/up read x in one launch, counted once), and the
+    weights in it are exactly the router, 2 shared experts and 16 routed
+    experts of the K3 shape."""
+    import bench
+    one = bench.kernel_bytes("decode_front", 1, 16, 16, 2)
+    three = (bench.kernel_bytes("router_shared_gateup_topk", 1, 16, 16, 2)
+             + bench.kernel_bytes("shared_down_routed_gateup", 1, 16, 16, 2)
+             + bench.kernel_bytes("routed_down_combine", 1, 16, 16, 2))
+    assert one == three - 7168 * 2 == 426_093_824
+    weights = 896 * 7168 * 2 + 2 * 3 * 7168 * 1536 * 2 + 16 * 17_547_264
+    assert weights == 425_721_856
+    # activations and intermediates: x twice, logits written and read, ids and
+    # weights written and read, h (routed and shared, hi + lo) written and
+    # read, the shared outputs written and read, y
+    assert one - weights == 371_968
+
+
+def test_kernel_lists_follow_the_launch_structure():
+    """One token: one launch; 2 to 8 tokens: three; more: four; MFMA: five."""
+    import bench
+    assert bench.config_kernels("b1") == ["decode_front"]
+    assert bench.config_kernels("b2") == bench.KERNELS_GEMV_SMALL
+    assert bench.config_kernels("b8") == bench.KERNELS_GEMV_SMALL
+    assert bench.config_kernels("b64") == bench.KERNELS_GEMV
+    assert bench.config_kernels("prefill") == bench.KERNELS_MFMA
