@@ -149,11 +149,11 @@ struct GemvLayer {
 struct Stage {
   int n_logits = 0;           // ceil(E / 4)
   int n_select = 0;           // ceil(T / 4)
-  int n_selw = 0;             // 0 or 1: top-k (T <= 4) after waiting for this launch's logits
+  int n_selw = 0;             // 0 or 1: top-k (T <= 8) after waiting for this launch's logits
   int plan_after_select = 0;  // the last top-k workgroup builds the plan
   int n_plan = 0;             // 0 or 1
-  int n_sgu = 0;              // S * I / 16
-  int n_sdn = 0;              // S * ceil(H / 64)
+  int n_sgu = 0;              // S * I / 16 (x passes of 16 tokens, XCD-grouped; the front: one)
+  int n_sdn = 0;              // S * ceil(H / 64) (x passes of 8 tokens, XCD-grouped; the front: one)
   int n_rgu = 0;              // max_active * I / 32
   int n_rdn = 0;              // max_active * ceil(H / kDownRows)
   int n_xq = 0;               // x quantisation, 256 blocks of 32 per workgroup
@@ -167,8 +167,9 @@ struct Stage {
 
 enum class StageKind {
   RouterSharedGateUp,  // roles: logits, shared gate/up, top-k waiting for the logits
-  DecodeFront,         // one token: logits, shared gate/up, top-k, routed gate/up, shared
-                       // down, each waiting on flags of blocks before it
+  DecodeFront,         // one token, the whole layer: logits, shared gate/up, top-k, routed
+                       // gate/up and down, shared down, combine; roles wait on flags of
+                       // blocks before them
   SelectSharedDown,    // roles: top-k (+ plan), shared down
   PlanSharedGateUp,    // roles: plan, shared gate/up
   RoutedGateUp,        // roles: shared down, routed gate/up

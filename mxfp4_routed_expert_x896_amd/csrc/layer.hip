@@ -1,11 +1,14 @@
 // The layer's kernels.  Every launch is one role-dispatch kernel whose
 // workgroups take different roles by block index, so that independent work
-// shares a launch: moe_layer runs
+// shares a launch.  moe_layer on the GEMV path runs, for more than 8 tokens,
 //   1. router logits            + shared experts' gate/up
 //   2. top-k and plan           + shared experts' down
 //   3. routed gate/up
-//   4. routed down and the weighted combine
-// and moe_forward (routing given) runs plan + shared gate/up, routed gate/up
+//   4. routed down and the weighted combine;
+// for 2 to 8 tokens the top-k and plan end launch 1 (on one workgroup that
+// waits for the logits) and the shared down joins launch 3; one token runs
+// the whole layer in one launch whose roles wait on flags (moe_decode_front).
+// moe_forward (routing given) runs plan + shared gate/up, routed gate/up
 // + shared down, routed down + combine.  The shared experts do not depend on
 // the routing, so their weights stream while the router and the top-k run.
 //
