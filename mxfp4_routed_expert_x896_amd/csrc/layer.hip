@@ -675,7 +675,8 @@ __device__ void routed_down(const GemvLayer& L, int a, int e, int p0, int p1, in
     auto stage = [&]() {
       __syncthreads();
       if constexpr (kFront) wait_flags(L, L.guflags + a * (I / 32), I / 32);
-      stage_h<kFront>(hsm, hstride, mt, I, pad_k(I), [&](int j) { return L.h + size_t(t0 + j) * I; });
+      stage_h<kFront>(hsm, hstride, mt, I, pad_k(I),
+                      [&](int j) { return L.h + size_t(t0 + j) * I; });
       __syncthreads();
     };
     pipelineN<D>(0, nsteps, bufs, load, stage, [&](const DnTiles& t, int s) {
@@ -787,7 +788,8 @@ __device__ void shared_down_front(const GemvLayer& L, int sx, int tile, uint16_t
   };
   auto load = [&](Tiles& t, int q) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) t.w[j] = ld_nt(dt + size_t(min(4 * q + j, nu - 1)) * 512 + 8 * lane);
+    for (int j = 0; j < 4; ++j)
+      t.w[j] = ld_nt(dt + size_t(min(4 * q + j, nu - 1)) * 512 + 8 * lane);
   };
   auto stage = [&]() {
     wait_flags(L, L.sgflags + sx * (I / 16), I / 16, L.idsflag, 1);
@@ -819,7 +821,8 @@ __device__ void shared_down_front(const GemvLayer& L, int sx, int tile, uint16_t
     for (int i = 0; i < 4; ++i) store_coherent(yrow + i, y[i]);
   }
   const int ft = tile / (kFrontDownRows / kRowsSD);
-  if (arrive_last(&L.tile_cnt[ft], front_arrivals(L, ft))) combine_tile<kFrontDownRows, true>(L, ft);
+  if (arrive_last(&L.tile_cnt[ft], front_arrivals(L, ft)))
+    combine_tile<kFrontDownRows, true>(L, ft);
 }
 
 // The last routed workgroup of a tile sums the partials into the bf16 output.
@@ -1395,34 +1398,34 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   int id = 0;  // this lane's selected expert (lanes < k of a token's wave)
   const int rounds = single ? (L.T + kWaves - 1) / kWaves : 1;
   for (int r = 0; r < rounds; ++r) {
-  const int t = (single ? r : b) * kWaves + wave;
-  if (t < L.T) {
-    float w;
-    const float* lrow = L.logits + size_t(t) * L.E;
-    const size_t ps = size_t(L.T) * L.E;
-    if (L.sbias != nullptr) {
-      if (L.lsplit == kRouterSplit)
-        select_token<kCoherent, kRouterSplit, true>(lrow, ps, L.E, L.k, id, w, sc[wave], L.sbias,
-                                                    L.rscale);
-      else
-        select_token<kCoherent, 1, true>(lrow, 0, L.E, L.k, id, w, sc[wave], L.sbias, L.rscale);
-    } else if (L.lsplit == kRouterSplit) {
-      select_token<kCoherent, kRouterSplit>(lrow, ps, L.E, L.k, id, w, sc[wave], nullptr,
-                                            L.rscale);
-    } else {
-      select_token<kCoherent>(lrow, 0, L.E, L.k, id, w, sc[wave], nullptr, L.rscale);
-    }
-    if (lane < L.k) {
-      if (single && !L.front) {
-        L.ids_out[size_t(t) * L.k + lane] = id;
-        L.w_out[size_t(t) * L.k + lane] = w;
-        own_ids[t * L.k + lane] = id;
-      } else {  // read by other workgroups of this launch (or the next top-k's plan)
-        store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
-        store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
+    const int t = (single ? r : b) * kWaves + wave;
+    if (t < L.T) {
+      float w;
+      const float* lrow = L.logits + size_t(t) * L.E;
+      const size_t ps = size_t(L.T) * L.E;
+      if (L.sbias != nullptr) {
+        if (L.lsplit == kRouterSplit)
+          select_token<kCoherent, kRouterSplit, true>(lrow, ps, L.E, L.k, id, w, sc[wave], L.sbias,
+                                                      L.rscale);
+        else
+          select_token<kCoherent, 1, true>(lrow, 0, L.E, L.k, id, w, sc[wave], L.sbias, L.rscale);
+      } else if (L.lsplit == kRouterSplit) {
+        select_token<kCoherent, kRouterSplit>(lrow, ps, L.E, L.k, id, w, sc[wave], nullptr,
+                                              L.rscale);
+      } else {
+        select_token<kCoherent>(lrow, 0, L.E, L.k, id, w, sc[wave], nullptr, L.rscale);
+      }
+      if (lane < L.k) {
+        if (single && !L.front) {
+          L.ids_out[size_t(t) * L.k + lane] = id;
+          L.w_out[size_t(t) * L.k + lane] = w;
+          own_ids[t * L.k + lane] = id;
+        } else {  // read by other workgroups of this launch (or the next top-k's plan)
+          store_coherent(&L.ids_out[size_t(t) * L.k + lane], id);
+          store_coherent(&L.w_out[size_t(t) * L.k + lane], w);
+        }
       }
     }
-  }
   }
   // Direct mode (no plan): only the combine's arrival counters need clearing,
   // before the ids flag: a routed down of the same launch may count once it
