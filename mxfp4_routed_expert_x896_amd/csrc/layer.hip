@@ -1384,7 +1384,10 @@ __device__ void select_waits(const GemvLayer& L, int n) {
   for (int i = threadIdx.x; i < n; i += kThreads) L.lflags[i] = 0;
 }
 
-template <bool kCoherent = false>
+// kRounds: the most tokens per wave (kSelwMaxTokens / kWaves where the
+// router launch's top-k can take up to kSelwMaxTokens tokens, else 1), a
+// compile-time bound so that the other launches' top-k code is unchanged.
+template <bool kCoherent = false, int kRounds = 1>
 __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   const int wave = wave_id();
   const int lane = threadIdx.x % kWave;
@@ -1396,8 +1399,10 @@ __device__ void select_role(const GemvLayer& L, const Stage& st, int b) {
   __shared__ int own_ids[kSelwMaxTokens * 32];
   __shared__ SelectScratch sc[kWaves];
   int id = 0;  // this lane's selected expert (lanes < k of a token's wave)
-  const int rounds = single ? (L.T + kWaves - 1) / kWaves : 1;
-  for (int r = 0; r < rounds; ++r) {
+  const int rounds = single ? min(kRounds, (L.T + kWaves - 1) / kWaves) : 1;
+#pragma nounroll
+  for (int r = 0; r < kRounds; ++r) {  // one copy of the selection code, not kRounds
+    if (r >= rounds) break;  // uniform
     const int t = (single ? r : b) * kWaves + wave;
     if (t < L.T) {
       float w;
@@ -1603,7 +1608,7 @@ __device__ __forceinline__ void stage_body(const GemvLayer& L, const Stage& st) 
   if constexpr ((R & kRoleSelectWait) != 0) {  // last: it waits on the blocks before it
     if (b < st.n_selw) {
       select_waits(L, st.n_logits);
-      select_role<true>(L, st, 0);
+      select_role<true, kSelwMaxTokens / kWaves>(L, st, 0);
     }
   }
 }
