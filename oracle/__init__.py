@@ -27,8 +27,9 @@ listed in the repository's design notes; each function names its reading.
 
 Parity pins: every public function is pinned by tests under tests/ marked
 "not gpu" (closed forms, library routines, brute force, invariants).  The
-layer output itself has no worked example on the pages: "parity unpinned by
-the pages"; its parts are pinned individually.
+pages print no worked example of a layer output; the whole layer is pinned
+against a result assembled by hand from exactly rounded router sums and
+closed-form experts, and its parts individually.
 
 Modules:
   formats -- E2M1, E8M0, E4M3, bf16 encodings and the MXFP4/MXFP8 codecs.

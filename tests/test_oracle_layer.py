@@ -4,7 +4,9 @@ Closed forms on hand-built sparse experts (which fail on a swapped gate/up,
 a transposed matrix, a wrong nibble or block index), the invariants the
 layer must satisfy (all experts equal -> one dense FFN independent of
 routing; zero routed experts -> shared experts only; one more scale
-exponent -> exactly twice the expert output), and torch's RMSNorm.
+exponent -> exactly twice the expert output), torch's RMSNorm, and the
+whole layer against a result assembled by hand from per-token routing and
+closed-form experts.
 """
 
 import math
@@ -218,3 +220,51 @@ def test_mxfp4_mode_all_experts_equal_is_dense_ffn_of_rounded_activations():
     xq = F.mxfp4_roundtrip(F.bf16_decode(x))
     hq = F.mxfp4_roundtrip(M.silu(xq @ wg.T) * (xq @ wu.T))
     np.testing.assert_allclose(y, hq @ wd.T, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+
+
+def _bf16_value(bits):
+    """bf16 bit pattern -> float, through the float32 pattern (bits << 16)."""
+    import struct
+    return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+
+def test_layer_end_to_end_from_per_token_routing_and_closed_forms():
+    """The whole layer on 3 tokens and 5 distinct experts against a result
+    assembled here by hand: logits as exactly rounded sums (math.fsum) of the
+    bf16 products, scores sorted as (score desc, index asc) tuples, weights
+    renormalised, and each expert's output from its closed form (expert e is
+    closed form a or b, by parity, times 2^e through its down matrix's block
+    exponents), plus the residual.  Catches a token's routing applied to
+    another token, a weight paired with the wrong expert, or an expert id
+    read from the wrong slot -- which the all-experts-equal and zero-expert
+    invariants cannot see."""
+    E, k, T = 5, 2, 3
+    cg, sg = I * H // 2, I * H // 32
+    recs = []
+    for e in range(E):
+        rec = (_expert_a() if e % 2 == 0 else _expert_b()).copy()
+        down_scales = 2 * (cg + sg) + H * I // 2
+        rec[down_scales: down_scales + H * I // 32] = 127 + e
+        recs.append(rec)
+    closed = [_closed_a if e % 2 == 0 else _closed_b for e in range(E)]
+    layer = _layer(recs, k=k, router_seed=3)
+    x_bits = _x(1010, T)
+    res_bits = synth.activations(1011, T, H)
+    y, ids, w = M.moe_layer(x_bits, layer, residual_bits=res_bits)
+    wr = layer.router_w
+    for t in range(T):
+        xt = [_bf16_value(b) for b in x_bits[t]]
+        logit = [math.fsum(xt[h] * _bf16_value(wr[e, h]) for h in range(H)) for e in range(E)]
+        score = [1.0 / (1.0 + math.exp(-v)) for v in logit]
+        order = sorted(range(E), key=lambda e: (-score[e], e))
+        assert score[order[k - 1]] - score[order[k]] > 1e-9  # no near-tie at the cut
+        chosen = order[:k]
+        total = sum(score[e] for e in chosen)
+        assert list(ids[t]) == chosen
+        np.testing.assert_allclose(w[t], [score[e] / total for e in chosen], rtol=1e-13)
+        want = [_bf16_value(b) for b in res_bits[t]]
+        for e in chosen:
+            want = np.asarray(want) + (score[e] / total) * 2.0 ** e * closed[e](np.asarray(xt))
+        np.testing.assert_allclose(y[t], want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # the tokens do not all take the same experts (else a token mix-up would pass)
+    assert len({tuple(r) for r in ids.tolist()}) > 1
