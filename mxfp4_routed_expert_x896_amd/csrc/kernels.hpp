@@ -33,23 +33,23 @@ constexpr unsigned long long kWaitGaveUp = 0x5449'4D45'4F55'5400ull;
 // Default number of polls before a top-k wait gives up (~0.3 us each).
 constexpr long kDefaultSpinLimit = 1l << 20;
 
-// Output rows per routed down workgroup (and per combine tile).
 // Tokens per pass of the GEMV path's shared-expert roles: the 16 B columns
 // of one MFMA (the shared down's pass takes 8, each token's h as two
 // columns, hi and lo).
 constexpr int kGemvPassTokens = 16;
+// Output rows per routed down workgroup (and per combine tile).
 constexpr int kDownRows = 128;
 static_assert(kDownRows % 16 == 0, "whole row groups");
 // Routed down rows per workgroup when the down runs in the one-token front
 // launch (half as many workgroups, each wave streams twice as long).
 constexpr int kFrontDownRows = 256;
 static_assert(kFrontDownRows % kDownRows == 0, "front tiles count on the same counters");
-// Router logits of kRouterSplitMin or more tokens (GEMV path: the batches
-// whose top-k has a launch of its own): bf16 MFMA over kRouterSplit quarters
-// of the contraction, one workgroup per (16 experts, quarter).
 // Tokens whose top-k and plan run in the router launch, on one workgroup
 // (its waves take the tokens in turn) that waits for the logits.
 constexpr int kSelwMaxTokens = 8;
+// Router logits of kRouterSplitMin or more tokens on the GEMV path: bf16
+// MFMA over kRouterSplit quarters of the contraction, one workgroup per
+// (16 experts, quarter), partial sums added in order by the top-k.
 constexpr int kRouterSplit = 4;
 constexpr int kRouterSplitMin = 5;
 // Prefill combine workgroups per token: 1024-column chunks of the output row.
