@@ -118,6 +118,7 @@ def parse():
 
 # dominant launch per config: (HIP kernel name in traces, name in kernel_us)
 PMC_KERNELS = {"b1": ("moe_decode_front", "decode_front"),
+               "b64": ("moe_routed_gateup", "routed_gateup"),
                "prefill": ("moe_mx_gateup", "mx_gateup"),
                "int8_dequant": ("int8_row_dequant_kernel", "int8_row_dequant")}
 
@@ -156,6 +157,11 @@ def pmc_summary(args, out_dir=None):
         alg = c["rows"] * c["cols"] * 5 + c["rows"] * 4
     elif args.config == "prefill":  # 4096 tokens; every expert active at this routing
         alg = kernel_bytes(name, CONFIGS["prefill"]["tokens"], 16, 896, 2)
+    elif args.config == "b64":
+        # the counters average over every dispatch of the run, warmup included:
+        # distinct experts at their expectation for 64 tokens routed uniformly
+        T, k, E = CONFIGS["b64"]["tokens"], 16, 896
+        alg = kernel_bytes(name, T, k, E * (1 - (1 - k / E) ** T), 2)
     else:
         alg = kernel_bytes(name, 1, 16, 16, 2)
     out = {"kernel": ksub, "bench_name": name, "config": args.config,
@@ -166,8 +172,17 @@ def pmc_summary(args, out_dir=None):
            "fetch_bytes_per_launch": round(fetch * 1024 * fs),
            "write_bytes_per_launch": round(write * 1024 * wsc)}
     out["bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
-    out["algorithmic_bytes"] = alg
+    out["algorithmic_bytes"] = round(alg)
     out["traffic_over_algorithmic"] = round(out["bytes_per_launch"] / alg, 4)
+    # the config's other launches, same runs and scaling
+    others = {}
+    for n in config_kernels(args.config):
+        hit = [kn for kn in f if HIP_KERNEL[n] in kn and "copyBuffer" not in kn]
+        if len(hit) == 1 and hit[0] != kf[0] and hit[0] in w:
+            others[n] = {"fetch_bytes_per_launch": round(float(np.mean(f[hit[0]])) * 1024 * fs),
+                         "write_bytes_per_launch": round(float(np.mean(w[hit[0]])) * 1024 * wsc)}
+    if others:
+        out["other_launches"] = others
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"pmc_{name}_{args.config}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
