@@ -53,11 +53,13 @@
  * Conventions for every call:
  *   - pointers are DEVICE pointers unless stated; bf16 is passed as uint16_t
  *     bit patterns; every device pointer must be 16-byte aligned.
- *   - the caller owns every buffer.  The library allocates nothing, keeps no
- *     mutable global state (beyond two per-host-thread settings: the timing
- *     hook and the wait limit), never synchronises the host (except
- *     moe_workspace_status, a query), and enqueues all work on the given
- *     stream (NULL = the default stream).
+ *   - the caller owns every buffer.  The library allocates no device memory
+ *     at run time (moe_layer_scratch uses a static device array, present
+ *     from load; an expert pool keeps its bookkeeping in host memory),
+ *     keeps no other mutable global state (beyond two per-host-thread
+ *     settings: the timing hook and the wait limit), never synchronises the
+ *     host (except moe_workspace_status, a query), and enqueues all work on
+ *     the given stream (NULL = the default stream).
  *   - arguments are validated on the host before anything is launched; on
  *     error nothing is launched and a negative MOE_E* code is returned.
  *     Device-side faults surface at the caller's next synchronisation.
