@@ -736,6 +736,12 @@ def main():
         "layer_span_us_median": round(float(np.median(span)), 2),
         "layer_span_us_iqr": [round(float(np.percentile(span, 25)), 2),
                               round(float(np.percentile(span, 75)), 2)],
+        # median span per resident copy of the layer (step i runs copy i mod copies):
+        # identical bytes at different addresses
+        "layer_span_us_by_copy": ([round(float(np.median(span[(c - args.warmup) % len(layers)::len(layers)])), 2)
+                                   for c in range(len(layers))]
+                                  if n_layers == 1 and len(layers) > 1 and len(span) >= 2 * len(layers)
+                                  else None),
         "hbm_copy_gbs": copy_gbs,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
